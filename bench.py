@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of POEM-style output-relative block-sparse prefill on one MI355X.
+
+One step = the whole hot path on resident inputs: poem_select (selector sweeps,
+ranking/threshold, CSR) followed by poem_sparse_prefill over the retained blocks.
+poem_dense_prefill (same kernel, full causal lists) is timed beside it for the
+speedup. Prints one JSON line.
+
+value  = 4 d P_R / (t_select + t_sparse): retained-block attention FLOPs per second
+         of the whole step (P_R = causal (query, key) pairs inside retained blocks,
+         summed over query heads).
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_FP32_TFLOPS = 157.3   # MI355X fp32 (MFMA and vector)
+PEAK_HBM_GBS = 8000.0
+METRIC = "sparse prefill attn latency + eff. TFLOP/s at 128K; speedup vs own dense kernel"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def tile_table(gp):
+    """Per global tile: (n_rows, diag) from the problem geometry."""
+    rows, diags = [], []
+    B = gp.block_size
+    for nq, nk in zip(gp.seqlens_q, gp.seqlens_k):
+        d0 = (nk - nq) // B
+        for t in range(-(-nq // B)):
+            rows.append(min(B, nq - t * B))
+            diags.append(d0 + t)
+    return np.array(rows, np.int64), np.array(diags, np.int64)
+
+
+def pair_counts(gp, rp, bi):
+    """(retained pairs, dense pairs) over all (head, tile) rows of the CSR."""
+    B = gp.block_size
+    n_rows, diags = tile_table(gp)
+    T = len(n_rows)
+    H = gp.num_heads_q
+    counts = np.diff(rp).reshape(H, T)
+    # does each row hold its diagonal block? rows are ascending, so the diagonal is last
+    last = np.where(counts.ravel() > 0, bi[np.maximum(rp[1:] - 1, 0)], -1).reshape(H, T)
+    has_diag = (last == diags[None, :]).astype(np.int64)
+    full = counts - has_diag
+    tri = n_rows * (n_rows + 1) // 2
+    retained = int((full * (n_rows[None, :] * B) + has_diag * tri[None, :]).sum())
+    dense = int(H * (diags * n_rows * B + tri).sum())
+    return retained, dense
+
+
+def cpu_baseline(w, inp, gp, rp, bi, seconds):
+    """The fp64 oracle, as it stands, on a bounded sample of the same workload: per
+    sampled (head, tile), the selector and the sparse attention over its oracle-kept
+    blocks. Reported in the step's unit (retained-block TFLOP/s)."""
+    from block_sparse_attention_poem_amd import synth
+    from oracle import poem_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    op = O.Problem(tuple(w.seqlens_q), tuple(w.seqlens_k), w.num_heads_q, w.num_heads_kv, w.head_dim, w.block_size)
+    tl = O.tiles(op)
+    rng = np.random.default_rng(0)
+    order = rng.permutation([(h, t.gtile) for h in range(w.num_heads_q) for t in tl] if len(tl) * w.num_heads_q < 4096
+                            else [(int(h), int(g)) for h, g in zip(rng.integers(0, w.num_heads_q, 4096),
+                                                                     rng.integers(0, len(tl), 4096))])
+    q = inp.q
+    k64 = synth.to_f64(inp.k)
+    v64 = synth.to_f64(inp.v)
+    B = w.block_size
+    flops = 0.0
+    done = 0
+    t0 = time.perf_counter()
+    for h, gt in order:
+        h, gt = int(h), int(gt)
+        t = tl[gt]
+        # widen only this tile's queries (the oracle reads exact bf16 -> fp64 values)
+        qt = np.zeros((t.q_row0 + t.n_rows, w.num_heads_q, w.head_dim))
+        qt[t.q_row0:t.q_row0 + t.n_rows, h] = synth.to_f64(q[t.q_row0:t.q_row0 + t.n_rows, h])
+        sel = O.select_tile(op, qt, k64, v64, h, t, float(inp.tau[h]), w.n_sink_blocks, w.n_local_blocks,
+                            w.rows_per_tile)
+        O.tile_attention(op, qt, k64, v64, h, t, sel.retained)
+        kept = sel.retained
+        full = len(kept) - (1 if t.diag in kept else 0)
+        pairs = full * t.n_rows * B + (t.n_rows * (t.n_rows + 1) // 2 if t.diag in kept else 0)
+        flops += 4.0 * w.head_dim * pairs
+        done += 1
+        if time.perf_counter() - t0 > seconds:
+            break
+    el = time.perf_counter() - t0
+    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} (head, tile) pairs drawn uniformly from the workload; per pair the fp64 selector "
+                      f"(8 sampled rows) and the sparse attention over its kept blocks; {el:.1f} s",
+            "seconds": el, "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (1..5); 3 is the 128K layer")
+    ap.add_argument("--sink-offset", type=float, default=None, help="L_s - ln N (default 6)")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this build runs on one GPU: the path shards by KV head with no intra-op "
+                                   "communication, but only the single-GPU kernel is built; run with --gpus 1"}))
+        sys.exit(2)
+
+    import torch
+    from block_sparse_attention_poem_amd import _lib as L
+    from block_sparse_attention_poem_amd import synth
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    L.load()
+    w = synth.WORKLOADS[args.workload]
+    if args.sink_offset is not None:
+        w = w.with_(sink_offset=args.sink_offset)
+    log(f"[bench] generating workload {args.workload}: {w.name}")
+    inp = synth.make(w)
+    if inp.is_bf16:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    else:
+        conv = lambda a: torch.from_numpy(np.ascontiguousarray(a)).cuda()
+    q, k, v = conv(inp.q), conv(inp.k), conv(inp.v)
+    gp = L.Problem(list(w.seqlens_q), list(w.seqlens_k), w.num_heads_q, w.num_heads_kv, w.head_dim, w.block_size,
+                   0.0, w.dtype)
+    ws = L.SelectWorkspace(gp, w.rows_per_tile)
+    T = L.num_tiles(gp)
+    cap = L.csr_capacity(gp)
+    row_ptr = torch.empty(w.num_heads_q * T + 1, dtype=torch.int32, device="cuda")
+    block_idx = torch.empty(cap, dtype=torch.int32, device="cuda")
+    out_dtype = "bf16" if w.dtype == "bf16" else "fp32"
+    out, lse = L._alloc_out(gp, out_dtype, True, q.device)
+    stream = torch.cuda.current_stream()
+
+    import ctypes
+    lib = L.load()
+    cp = gp.c()
+    tau_arr = (ctypes.c_float * w.num_heads_q)(*[float(x) for x in inp.tau])
+    odt = L.POEM_FP32 if out_dtype == "fp32" else L.POEM_BF16
+
+    def select():
+        L._check(lib.poem_select(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), tau_arr, w.n_sink_blocks,
+                                 w.n_local_blocks, w.rows_per_tile, L._ptr(row_ptr), L._ptr(block_idx), cap,
+                                 None, None, None, ctypes.c_void_p(ws.ptr), ws.nbytes,
+                                 ctypes.c_void_p(stream.cuda_stream)))
+
+    def sparse():
+        L._check(lib.poem_sparse_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(row_ptr),
+                                         L._ptr(block_idx), L._ptr(out), odt, L._ptr(lse),
+                                         ctypes.c_void_p(stream.cuda_stream)))
+
+    def dense():
+        L._check(lib.poem_dense_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(out), odt,
+                                        L._ptr(lse), ctypes.c_void_p(stream.cuda_stream)))
+
+    log(f"[bench] warmup {args.warmup}")
+    for _ in range(args.warmup):
+        select()
+        sparse()
+    torch.cuda.synchronize()
+
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    log(f"[bench] timing {args.steps} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        ev[i][0].record(stream)
+        select()
+        ev[i][1].record(stream)
+        sparse()
+        ev[i][2].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    t_sel = np.array([ev[i][0].elapsed_time(ev[i][1]) for i in range(args.steps)])
+    t_sp = np.array([ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)])
+
+    rp = row_ptr.cpu().numpy().astype(np.int64)
+    bi = block_idx.cpu().numpy()
+    p_ret, p_dense = pair_counts(gp, rp, bi)
+    kept_blocks = int(rp[-1])
+    flop_ret = 4.0 * w.head_dim * p_ret
+    flop_dense = 4.0 * w.head_dim * p_dense
+
+    t_dense = None
+    if not args.no_dense:
+        log("[bench] dense baseline")
+        for _ in range(max(1, args.warmup // 2)):
+            dense()
+        evd = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
+        for i in range(args.steps):
+            evd[i][0].record(stream)
+            dense()
+            evd[i][1].record(stream)
+        torch.cuda.synchronize()
+        t_dense = np.array([evd[i][0].elapsed_time(evd[i][1]) for i in range(args.steps)])
+
+    ms_step = wall * 1e3 / args.steps
+    sel_ms, sp_ms = float(np.median(t_sel)), float(np.median(t_sp))
+    value = flop_ret / ((sel_ms + sp_ms) * 1e-3) / 1e12
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
+    # dominant kernel of the step: the sparse attention kernel (one launch) or the selector
+    attn_tflops = flop_ret / (sp_ms * 1e-3) / 1e12
+    roofline = {"kernel": "attn_fwd_kernel (sparse)", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+                "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None,
+                "algorithmic": f"4 d P_R = {flop_ret:.4e} FLOP per launch"}
+    res = {
+        "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic",
+        "config": {"workload": w.name, "heads_q": w.num_heads_q, "heads_kv": w.num_heads_kv,
+                   "head_dim": w.head_dim, "seqlens_k": list(w.seqlens_k), "seqlens_q": list(w.seqlens_q),
+                   "block": w.block_size, "rows_per_tile": w.rows_per_tile, "sink_offset": w.sink_offset,
+                   "tau": list(w.tau), "mandatory": {"sink_blocks": w.n_sink_blocks,
+                                                     "local_blocks": w.n_local_blocks}},
+        "latency_ms": {"select": sel_ms, "sparse_attn": sp_ms, "select_plus_sparse": sel_ms + sp_ms,
+                       "dense_attn": float(np.median(t_dense)) if t_dense is not None else None,
+                       "select_min": float(t_sel.min()), "sparse_min": float(t_sp.min())},
+        "speedup_vs_dense": (float(np.median(t_dense)) / (sel_ms + sp_ms)) if t_dense is not None else None,
+        "speedup_attn_only": (float(np.median(t_dense)) / sp_ms) if t_dense is not None else None,
+        "eff_tflops_sparse_kernel": attn_tflops,
+        "dense_tflops": (flop_dense / (float(np.median(t_dense)) * 1e-3) / 1e12) if t_dense is not None else None,
+        "keep_fraction_blocks": kept_blocks / cap,
+        "keep_fraction_pairs": p_ret / p_dense,
+        "roofline": roofline,
+    }
+    if not args.no_cpu_baseline:
+        log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
+        res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

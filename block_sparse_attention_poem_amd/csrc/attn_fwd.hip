@@ -1,0 +1,200 @@
+// Block-sparse (and dense) causal prefill attention for gfx950.
+//
+// One workgroup computes one (query head, query tile): B rows, 32 per wave, over
+// the key blocks the tile retains (sparse: its CSR row; dense: 0 .. diagonal), the
+// retained-block attention of the POEM note (Section 4.1). K/V of each 64-key
+// stage are staged in LDS once and shared by the tile's waves; the loop visits
+// only listed blocks, as BFLA's support-restricted kernel does (Section 3.4).
+// Online softmax runs in the log2 domain in fp32; QK^T and PV run on bf16 (or
+// fp32) MFMAs with fp32 accumulation. Only the diagonal block is masked.
+//
+// Work order: workgroups are ranked by the tile's diagonal block, longest first.
+// The KV head is the fastest-varying index of the workgroup id, so with 8 KV heads
+// and the round-robin dispatch over the 8 XCDs every XCD streams one KV head's
+// K/V through its own L2, and the query heads sharing a KV head run back to back.
+#include "poem_internal.hpp"
+
+namespace poem {
+
+// Two waves per SIMD (two workgroups per CU) when the LDS stages allow it: the MFMA
+// work of one wave overlaps the softmax of the other.
+template <typename T, int D>
+constexpr int attn_waves_per_eu() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
+
+template <typename T, int D, int BLK, bool SPARSE>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
+void attn_fwd_kernel(AttnParams p) {
+  constexpr int WAVES = BLK / 32;
+  constexpr int NT = WAVES * 64;
+  using St = Stage<T, D, NT>;
+  constexpr int SUBS = BLK / kStageKeys;
+  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jcol = lane & 31, g2 = lane >> 5;
+
+  const int bid = blockIdx.x;
+  const int gk = bid % p.hkv;
+  const int rest = bid / p.hkv;
+  const int hg = rest % p.group;
+  const int rank = rest / p.group;
+  int seq, t;
+  rank_to_item(p.seqs, 1, rank, seq, t);
+  if (seq < 0) return;
+  const int h = gk * p.group + hg;
+  const int n_q = p.seqs.n_q[seq], n_k = p.seqs.n_k[seq];
+  const int diag = p.seqs.diag0[seq] + t;
+  const int row0 = t * BLK;
+  const int n_rows = min(BLK, n_q - row0);
+  const int pos0 = (n_k - n_q) + row0;  // absolute position of the tile's first row
+  const int wrow = 32 * wave + jcol;
+  const bool row_ok = wrow < n_rows;
+  const int my_pos = pos0 + wrow;
+  const int wave_pos_min = pos0 + 32 * wave, wave_pos_max = wave_pos_min + 31;
+
+  const int64_t qrow = (int64_t)p.seqs.q_start[seq] + row0 + wrow;
+  QFrag<T, D> qf;
+  qf.load(reinterpret_cast<const T*>(p.q) + (qrow * p.hq + h) * D, row_ok, g2);
+
+  const int64_t row_stride = (int64_t)p.hkv * D;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+
+  // block list
+  const int32_t* ids = nullptr;
+  int nblk;
+  if constexpr (SPARSE) {
+    const int64_t r = (int64_t)h * p.seqs.total_tiles + p.seqs.tile_start[seq] + t;
+    const int a = p.row_ptr[r], b = p.row_ptr[r + 1];
+    ids = p.block_idx + a;
+    int n = b - a;
+    // rows are ascending: keep the ids in [0, diag]
+    int lo = 0, hi = n;  // first index with id >= 0
+    while (lo < hi) { int mid = (lo + hi) >> 1; if (ids[mid] < 0) lo = mid + 1; else hi = mid; }
+    int first = lo;
+    hi = n;  // first index with id > diag
+    while (lo < hi) { int mid = (lo + hi) >> 1; if (ids[mid] <= diag) lo = mid + 1; else hi = mid; }
+    ids += first;
+    nblk = lo - first;
+  } else {
+    nblk = diag + 1;
+  }
+  auto stage_key0 = [&](int it) {
+    const int blk = SPARSE ? ids[it / SUBS] : it / SUBS;
+    return blk * BLK + (it % SUBS) * kStageKeys;
+  };
+
+  const int total = nblk * SUBS;
+  f32x16 O[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float c = p.scale_log2;
+
+  typename St::Regs regs;
+  if (total > 0) {
+    St::load(regs, kbase, vbase, row_stride, stage_key0(0), n_k, tid);
+    St::store(regs, smem, tid);
+  }
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    char* cur = smem + (it & 1) * St::BYTES;
+    if (it + 1 < total) St::load(regs, kbase, vbase, row_stride, stage_key0(it + 1), n_k, tid);
+    const int key0 = stage_key0(it);
+    if (key0 <= wave_pos_max) {
+      f32x16 S[2];
+      S[0] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 0, lane);
+      S[1] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 1, lane);
+      float mx = -INFINITY;
+      if (key0 + kStageKeys - 1 > wave_pos_min) {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float s = (key0 + acc_key(kt, r, g2) > my_pos) ? -INFINITY : S[kt][r];
+            S[kt][r] = s;
+            mx = fmaxf(mx, s);
+          }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+      }
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
+          S[kt][r] = e;
+          rs += e;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
+      }
+      pv_stage<T, D, St::V_STRIDE, false>(cur + St::K_BYTES, S, O, lane);
+    }
+    if (it + 1 < total) St::store(regs, smem + ((it + 1) & 1) * St::BYTES, tid);
+    __syncthreads();
+  }
+
+  const float l_tot = l_run + wave_xor32(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_ok) {
+    char* orow = reinterpret_cast<char*>(p.out) + (qrow * p.hq + h) * D * (p.out_f32 ? 4 : 2);
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        const int d = 32 * dt + 8 * a + 4 * g2;
+        f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv};
+        if (p.out_f32) {
+          *reinterpret_cast<f32x4*>(orow + d * 4) = o;
+        } else {
+          u32x2 w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
+          *reinterpret_cast<u32x2*>(orow + d * 2) = w;
+        }
+      }
+    if (p.lse != nullptr && g2 == 0)
+      p.lse[(int64_t)h * p.total_q + qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+  }
+}
+
+template <typename T, int D, int BLK, bool SPARSE>
+static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
+  const int64_t grid = (int64_t)p.seqs.total_tiles * p.hq;
+  if (grid == 0) return hipSuccess;
+  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, SPARSE>), dim3((unsigned)grid), dim3(BLK * 2), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D, int BLK>
+static hipError_t launch_mode(const AttnParams& p, bool sparse, hipStream_t s) {
+  return sparse ? launch_one<T, D, BLK, true>(p, s) : launch_one<T, D, BLK, false>(p, s);
+}
+
+template <typename T, int D>
+static hipError_t launch_block(const AttnParams& p, int block, bool sparse, hipStream_t s) {
+  return block == 64 ? launch_mode<T, D, 64>(p, sparse, s) : launch_mode<T, D, 128>(p, sparse, s);
+}
+
+template <typename T>
+static hipError_t launch_dim(const AttnParams& p, int d, int block, bool sparse, hipStream_t s) {
+  return d == 64 ? launch_block<T, 64>(p, block, sparse, s) : launch_block<T, 128>(p, block, sparse, s);
+}
+
+hipError_t launch_attention(const AttnParams& p, int in_dtype, int head_dim, int block, bool sparse,
+                            hipStream_t stream) {
+  return in_dtype == 0 ? launch_dim<uint16_t>(p, head_dim, block, sparse, stream)
+                       : launch_dim<float>(p, head_dim, block, sparse, stream);
+}
+
+}  // namespace poem

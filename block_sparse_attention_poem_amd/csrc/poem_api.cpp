@@ -1,0 +1,301 @@
+// libpoem C ABI: argument validation, geometry, workspace layout and launches.
+// Every check runs on the host before anything is enqueued; nothing here allocates
+// device memory, copies host data to the device or synchronises the host.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <string>
+
+#include "poem.h"
+#include "poem_internal.hpp"
+
+namespace {
+
+thread_local std::string g_error;
+
+poem_status fail(poem_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return s;
+}
+
+poem_status ok() {
+  g_error.clear();
+  return POEM_OK;
+}
+
+struct Geometry {
+  poem::SeqTable st;
+  int64_t total_q = 0, total_k = 0;
+  int64_t num_tiles = 0;
+  int64_t vis_per_head = 0;
+  int64_t max_vis = 0;
+  int64_t capacity = 0;
+  float scale = 0.f;
+};
+
+poem_status build_geometry(const poem_problem* p, Geometry& g) {
+  if (p == nullptr) return fail(POEM_ERR_INVALID_ARG, "problem is NULL");
+  if (p->num_seqs < 1) return fail(POEM_ERR_INVALID_ARG, "num_seqs must be >= 1 (got %d)", p->num_seqs);
+  if (p->num_seqs > POEM_MAX_SEQS)
+    return fail(POEM_ERR_UNSUPPORTED, "num_seqs %d exceeds POEM_MAX_SEQS (%d)", p->num_seqs, POEM_MAX_SEQS);
+  if (p->seqlens_q_host == nullptr || p->seqlens_k_host == nullptr)
+    return fail(POEM_ERR_INVALID_ARG, "seqlens_q_host / seqlens_k_host is NULL");
+  if (p->num_heads_q < 1 || p->num_heads_kv < 1)
+    return fail(POEM_ERR_INVALID_ARG, "num_heads_q and num_heads_kv must be >= 1 (got %d, %d)", p->num_heads_q,
+                p->num_heads_kv);
+  if (p->num_heads_q % p->num_heads_kv != 0)
+    return fail(POEM_ERR_INVALID_ARG, "num_heads_q (%d) is not a multiple of num_heads_kv (%d)", p->num_heads_q,
+                p->num_heads_kv);
+  if (p->head_dim <= 0) return fail(POEM_ERR_INVALID_ARG, "head_dim must be positive (got %d)", p->head_dim);
+  if (p->head_dim != 64 && p->head_dim != 128)
+    return fail(POEM_ERR_UNSUPPORTED, "head_dim %d is not built (64 or 128)", p->head_dim);
+  if (p->block_size <= 0) return fail(POEM_ERR_INVALID_ARG, "block_size must be positive (got %d)", p->block_size);
+  if (p->block_size != 64 && p->block_size != 128)
+    return fail(POEM_ERR_UNSUPPORTED, "block_size %d is not built (64 or 128)", p->block_size);
+  if (!isfinite(p->softmax_scale)) return fail(POEM_ERR_INVALID_ARG, "softmax_scale is not finite");
+  if (p->in_dtype != POEM_BF16 && p->in_dtype != POEM_FP32)
+    return fail(POEM_ERR_INVALID_ARG, "in_dtype %d is not a poem_dtype", p->in_dtype);
+
+  const int B = p->block_size;
+  memset(&g.st, 0, sizeof g.st);
+  g.st.num_seqs = p->num_seqs;
+  g.st.block = B;
+  int64_t qs = 0, ks = 0, tiles = 0, vis = 0, maxv = 0;
+  for (int s = 0; s < p->num_seqs; ++s) {
+    const int64_t nq = p->seqlens_q_host[s], nk = p->seqlens_k_host[s];
+    if (nq < 0 || nk < 0) return fail(POEM_ERR_INVALID_ARG, "sequence %d: negative length (N_q=%lld, N_k=%lld)", s,
+                                      (long long)nq, (long long)nk);
+    if (nk < nq)
+      return fail(POEM_ERR_INVALID_ARG, "sequence %d: N_k (%lld) < N_q (%lld)", s, (long long)nk, (long long)nq);
+    if ((nk - nq) % B != 0)
+      return fail(POEM_ERR_INVALID_ARG, "sequence %d: N_k - N_q (%lld) is not a multiple of block_size %d", s,
+                  (long long)(nk - nq), B);
+    const int64_t nt = (nq + B - 1) / B;
+    const int64_t d0 = (nk - nq) / B;
+    g.st.q_start[s] = (int32_t)qs;
+    g.st.k_start[s] = (int32_t)ks;
+    g.st.n_q[s] = (int32_t)nq;
+    g.st.n_k[s] = (int32_t)nk;
+    g.st.n_tiles[s] = (int32_t)nt;
+    g.st.tile_start[s] = (int32_t)tiles;
+    g.st.diag0[s] = (int32_t)d0;
+    g.st.vis_start[s] = vis;
+    vis += nt * (d0 + 1) + nt * (nt - 1) / 2;
+    if (nt > 0) maxv = maxv > d0 + nt ? maxv : d0 + nt;
+    qs += nq;
+    ks += nk;
+    tiles += nt;
+    if (qs > INT32_MAX || ks > INT32_MAX) return fail(POEM_ERR_UNSUPPORTED, "total tokens exceed 2^31 - 1");
+  }
+  g.st.total_tiles = (int32_t)tiles;
+  g.st.vis_per_head = vis;
+  g.total_q = qs;
+  g.total_k = ks;
+  g.num_tiles = tiles;
+  g.vis_per_head = vis;
+  g.max_vis = maxv;
+  g.capacity = vis * p->num_heads_q;
+  if (g.capacity > INT32_MAX)
+    return fail(POEM_ERR_UNSUPPORTED, "CSR capacity %lld exceeds int32 offsets", (long long)g.capacity);
+  if (tiles * (int64_t)p->num_heads_q > INT32_MAX) return fail(POEM_ERR_UNSUPPORTED, "too many (head, tile) rows");
+  g.scale = p->softmax_scale > 0.f ? p->softmax_scale : 1.0f / sqrtf((float)p->head_dim);
+  return POEM_OK;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+struct SelLayout {
+  size_t row_stats = 0, blk_stats = 0, counts = 0, slots = 0, total = 0;
+};
+
+SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S) {
+  const int G = p->num_heads_q / p->num_heads_kv;
+  const int CT = (G * S + 31) / 32;
+  SelLayout L;
+  size_t off = 0;
+  L.row_stats = off;
+  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * CT * 32 * (p->head_dim + 4));
+  L.blk_stats = off;
+  off += align256(sizeof(float) * (size_t)p->num_heads_q * g.vis_per_head * S * 2);
+  L.counts = off;
+  off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.num_tiles);
+  L.slots = off;
+  off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.vis_per_head);
+  L.total = off;
+  return L;
+}
+
+poem_status check_rows(const poem_problem* p, int32_t S) {
+  if (S < 1) return fail(POEM_ERR_INVALID_ARG, "rows_per_tile must be >= 1 (got %d)", S);
+  if (S > POEM_MAX_ROWS_PER_TILE)
+    return fail(POEM_ERR_UNSUPPORTED, "rows_per_tile %d exceeds POEM_MAX_ROWS_PER_TILE (%d)", S, POEM_MAX_ROWS_PER_TILE);
+  const int G = p->num_heads_q / p->num_heads_kv;
+  if ((int64_t)G * S > 128)
+    return fail(POEM_ERR_UNSUPPORTED, "group size x rows_per_tile = %d exceeds 128 selector columns", G * S);
+  return POEM_OK;
+}
+
+poem_status hip_status(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(POEM_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+int64_t poem_num_tiles(const poem_problem* problem) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  ok();
+  return g.num_tiles;
+}
+
+int64_t poem_csr_capacity(const poem_problem* problem) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  ok();
+  return g.capacity;
+}
+
+int64_t poem_max_visible_blocks(const poem_problem* problem) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  ok();
+  return g.max_vis;
+}
+
+int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  s = check_rows(problem, rows_per_tile);
+  if (s != POEM_OK) return s;
+  ok();
+  return (int64_t)sel_layout(problem, g, rows_per_tile).total;
+}
+
+poem_status poem_select(const poem_problem* problem, const void* q, const void* k, const void* v,
+                        const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks, int32_t rows_per_tile,
+                        int32_t* row_ptr, int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
+                        float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes, void* stream) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  s = check_rows(problem, rows_per_tile);
+  if (s != POEM_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
+  if (row_ptr == nullptr || block_idx == nullptr) return fail(POEM_ERR_INVALID_ARG, "row_ptr or block_idx is NULL");
+  if (tau_host == nullptr) return fail(POEM_ERR_INVALID_ARG, "tau_host is NULL");
+  if (problem->num_heads_q > poem::kMaxHeadsQ)
+    return fail(POEM_ERR_UNSUPPORTED, "num_heads_q %d exceeds %d for the selector", problem->num_heads_q,
+                poem::kMaxHeadsQ);
+  for (int h = 0; h < problem->num_heads_q; ++h)
+    if (!(tau_host[h] >= 0.f) || !isfinite(tau_host[h]))
+      return fail(POEM_ERR_INVALID_ARG, "tau_host[%d] must be finite and >= 0", h);
+  if (n_sink_blocks < 0) return fail(POEM_ERR_INVALID_ARG, "n_sink_blocks must be >= 0 (got %d)", n_sink_blocks);
+  if (n_local_blocks < 1)
+    return fail(POEM_ERR_INVALID_ARG, "n_local_blocks must be >= 1 (it counts the diagonal block; got %d)",
+                n_local_blocks);
+  if (g.max_vis > POEM_MAX_VISIBLE_BLOCKS)
+    return fail(POEM_ERR_UNSUPPORTED, "a tile sees %lld blocks, above POEM_MAX_VISIBLE_BLOCKS (%d)",
+                (long long)g.max_vis, POEM_MAX_VISIBLE_BLOCKS);
+  if (block_idx_capacity < g.capacity)
+    return fail(POEM_ERR_CAPACITY, "block_idx capacity %lld < required %lld", (long long)block_idx_capacity,
+                (long long)g.capacity);
+  const SelLayout L = sel_layout(problem, g, rows_per_tile);
+  if (workspace == nullptr) return fail(POEM_ERR_WORKSPACE, "workspace is NULL");
+  if (workspace_bytes < L.total)
+    return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
+  if (((uintptr_t)workspace & 255) != 0) return fail(POEM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+
+  poem::SelectParams sp;
+  memset(&sp, 0, sizeof sp);
+  sp.q = q;
+  sp.k = k;
+  sp.v = v;
+  sp.hq = problem->num_heads_q;
+  sp.hkv = problem->num_heads_kv;
+  sp.group = problem->num_heads_q / problem->num_heads_kv;
+  sp.S = rows_per_tile;
+  sp.col_tiles = (sp.group * rows_per_tile + 31) / 32;
+  sp.n_sink = n_sink_blocks;
+  sp.n_local = n_local_blocks;
+  sp.max_vis = (int32_t)g.max_vis;
+  sp.scale_log2 = g.scale * poem::kLog2e;
+  for (int h = 0; h < problem->num_heads_q; ++h) sp.tau[h] = tau_host[h];
+  char* ws = static_cast<char*>(workspace);
+  sp.row_stats = reinterpret_cast<float*>(ws + L.row_stats);
+  sp.blk_stats = reinterpret_cast<float*>(ws + L.blk_stats);
+  sp.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+  sp.slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  sp.row_ptr = row_ptr;
+  sp.block_idx = block_idx;
+  sp.tile_scores = tile_scores;
+  sp.tile_mass = tile_mass;
+  sp.row_bound = row_bound;
+  sp.seqs = g.st;
+  return hip_status(poem::launch_select(sp, problem->in_dtype, problem->head_dim, problem->block_size,
+                                        static_cast<hipStream_t>(stream)),
+                    "poem_select launch");
+}
+
+static poem_status attention(const poem_problem* problem, const void* q, const void* k, const void* v,
+                             const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
+                             float* lse, void* stream, bool sparse) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
+  if (out == nullptr) return fail(POEM_ERR_INVALID_ARG, "out is NULL");
+  if (sparse && (row_ptr == nullptr || block_idx == nullptr))
+    return fail(POEM_ERR_INVALID_ARG, "row_ptr or block_idx is NULL");
+  if (out_dtype != POEM_BF16 && out_dtype != POEM_FP32)
+    return fail(POEM_ERR_INVALID_ARG, "out_dtype %d is not a poem_dtype", out_dtype);
+  poem::AttnParams ap;
+  memset(&ap, 0, sizeof ap);
+  ap.q = q;
+  ap.k = k;
+  ap.v = v;
+  ap.row_ptr = row_ptr;
+  ap.block_idx = block_idx;
+  ap.out = out;
+  ap.lse = lse;
+  ap.hq = problem->num_heads_q;
+  ap.hkv = problem->num_heads_kv;
+  ap.group = problem->num_heads_q / problem->num_heads_kv;
+  ap.out_f32 = out_dtype == POEM_FP32 ? 1 : 0;
+  ap.total_q = (int32_t)g.total_q;
+  ap.scale_log2 = g.scale * poem::kLog2e;
+  ap.seqs = g.st;
+  return hip_status(poem::launch_attention(ap, problem->in_dtype, problem->head_dim, problem->block_size, sparse,
+                                           static_cast<hipStream_t>(stream)),
+                    sparse ? "poem_sparse_prefill launch" : "poem_dense_prefill launch");
+}
+
+poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, const void* k, const void* v,
+                                const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
+                                float* lse, void* stream) {
+  return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, stream, true);
+}
+
+poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k, const void* v, void* out,
+                               int32_t out_dtype, float* lse, void* stream) {
+  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, stream, false);
+}
+
+const char* poem_last_error(void) { return g_error.c_str(); }
+
+const char* poem_version(void) { return "libpoem 0.1.0 (gfx950)"; }
+
+}  // extern "C"

@@ -1,0 +1,59 @@
+// Host-side interface between the C ABI layer and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "poem_device.hpp"
+
+namespace poem {
+
+constexpr int kMaxHeadsQ = 128;  // query heads the selector accepts (tau travels in kernel arguments)
+
+struct AttnParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  const int32_t* row_ptr;    // sparse only
+  const int32_t* block_idx;  // sparse only
+  void* out;
+  float* lse;                // nullable
+  int32_t hq, hkv, group;
+  int32_t out_f32;
+  int32_t total_q;
+  float scale_log2;          // softmax scale * log2(e)
+  SeqTable seqs;
+};
+
+// in_dtype: 0 bf16, 1 fp32.
+hipError_t launch_attention(const AttnParams& p, int in_dtype, int head_dim, int block, bool sparse,
+                            hipStream_t stream);
+
+struct SelectParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  int32_t hq, hkv, group;
+  int32_t S;                 // sampled rows per tile
+  int32_t col_tiles;         // 32-column tiles per (KV head, tile)
+  int32_t n_sink, n_local;
+  int32_t max_vis;
+  float scale_log2;
+  float tau[kMaxHeadsQ];     // per query head, passed by value
+  // workspace regions
+  float* row_stats;          // [hkv][total_tiles][col_tiles*32][D + 4]: M2, l, pad, pad, normalised o
+  float* blk_stats;          // per (h, gtile): [S][n_vis] I then [S][n_vis] m, at slot offsets
+  int32_t* counts;           // [hq * total_tiles]
+  int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets
+  // outputs
+  int32_t* row_ptr;
+  int32_t* block_idx;
+  float* tile_scores;        // nullable
+  float* tile_mass;          // nullable
+  float* row_bound;          // nullable
+  SeqTable seqs;
+};
+
+hipError_t launch_select(const SelectParams& p, int in_dtype, int head_dim, int block, hipStream_t stream);
+
+}  // namespace poem

@@ -1,0 +1,509 @@
+// Output-relative block selector for gfx950 (POEM note, Section 4.1 and Equation (4)).
+//
+// Columns. For a KV head g and query tile t, the selector's query columns are the
+// sampled rows of the G query heads that share g (BFLA Section 3.3): column
+// f = hg * S + j is row r_j of head g*G + hg. They are packed 32 to a wave, so one
+// K/V fetch serves every head of the group and the MFMA is fully used when
+// G * S = 32 (Llama-3-8B shapes: G = 4, S = 8).
+//
+// Pass 1 (sel_sweep_kernel<..., false>): per column, the dense softmax statistics
+//   over all visible keys (c = scale * log2 e): the final running max M2 of c s_j,
+//   l = sum_j 2^(c s_j - M2) and o = sum_j 2^(c s_j - M2) v_j / l.
+// Pass 2 (sel_sweep_kernel<..., true>): per column and visible block b, with the
+//   same weights w_j = 2^(c s_j - M2): L_b = sum_{j in b} w_j, U_b = sum_{j in b} w_j v_j,
+//   then m_b = L_b / l and I_b = ||U_b - L_b o|| / l (= ||u_b - m_b o||; a cross-lane
+//   sum of squares). Normalising only at the end keeps the weight of the row's
+//   maximum key exactly 1, so the block that dominates o (typically the sink) sees
+//   the same rounding in U_b as in o and u_b - m_b o does not lose its digits.
+// Both passes stream the visible K/V blocks through the same LDS stages as the
+// attention kernel; a workgroup holds several tiles of one KV head so each fetch is
+// shared by up to 128 columns. P V runs as two bf16 MFMAs (P = hi + lo) so the
+// block sums keep about 16 bits of P: u_b - m_b o cancels when v_b is close to o.
+//
+// Threshold (sel_threshold_kernel): per (query head, tile), the tile score is the
+// mean of I over the sampled rows; candidates (visible, not mandatory) are sorted
+// by (score ascending, id descending) with an LDS bitonic sort; the cut is the
+// first prefix whose per-row bound sum I / (1 - sum m), maximised over rows,
+// exceeds tau (prefix sums in fp64). The kept ids are compacted in ascending order.
+// CSR: an exclusive scan of the per-row counts and a scatter.
+#include "poem_internal.hpp"
+
+namespace poem {
+
+constexpr int kSelThreads = 256;
+constexpr int kSelWaves = 4;
+
+template <typename T, int D, int BLK, bool PASS2>
+__global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) {
+  using St = Stage<T, D, kSelThreads>;
+  constexpr int SUBS = BLK / kStageKeys;
+  constexpr bool SPLIT = sizeof(T) == 2;
+  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int jcol = lane & 31, g2 = lane >> 5;
+  const int CT = p.col_tiles;
+  const int TG = max(1, kSelWaves / CT);
+
+  const int gk = blockIdx.x % p.hkv;
+  const int rank = blockIdx.x / p.hkv;
+  int seq, tile0;
+  rank_to_item(p.seqs, TG, rank, seq, tile0);
+  if (seq < 0) return;
+  const int n_q = p.seqs.n_q[seq], n_k = p.seqs.n_k[seq], n_tiles = p.seqs.n_tiles[seq];
+  const int diag0 = p.seqs.diag0[seq];
+  const int t_last = min(tile0 + TG - 1, n_tiles - 1);
+  const int nblk_wg = diag0 + t_last + 1;
+
+  // this wave's unit: tile t, column tile ct
+  const int t = tile0 + wave / CT, ct = wave % CT;
+  const bool wave_on = wave < TG * CT && t < n_tiles;
+  const int diag = diag0 + t;
+  const int n_rows_t = wave_on ? min(BLK, n_q - t * BLK) : 1;
+  const int s_t = min(p.S, n_rows_t);
+  const int f = 32 * ct + jcol;
+  const int hg = f / p.S, jr = f % p.S;
+  const bool col_on = wave_on && hg < p.group && jr < s_t;
+  const int h = gk * p.group + (col_on ? hg : 0);
+  const int r_local = col_on ? ((jr + 1) * n_rows_t + s_t - 1) / s_t - 1 : 0;
+  const int tile_pos0 = (n_k - n_q) + t * BLK;
+  const int my_pos = tile_pos0 + r_local;
+  const int wave_pos_min = wave_on ? tile_pos0 : 0;
+  const int wave_pos_max = wave_on ? tile_pos0 + n_rows_t - 1 : -1;
+  const int gtile = p.seqs.tile_start[seq] + t;
+
+  const int64_t qrow = (int64_t)p.seqs.q_start[seq] + t * BLK + r_local;
+  QFrag<T, D> qf;
+  qf.load(reinterpret_cast<const T*>(p.q) + (qrow * p.hq + h) * D, col_on, g2);
+
+  const int64_t row_stride = (int64_t)p.hkv * D;
+  const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+  const T* vbase = reinterpret_cast<const T*>(p.v) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+  // per column: M2, l, two pad words, then o (16-byte aligned)
+  float* rs_col = p.row_stats +
+                  ((((int64_t)gk * p.seqs.total_tiles + (wave_on ? gtile : 0)) * CT + ct) * 32 + jcol) * (D + 4);
+  const float c = p.scale_log2;
+
+  f32x16 O[D / 32];
+#pragma unroll
+  for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
+  // pass 1: running max and sum; pass 2: M2, l, dense output o, block weight sum
+  float m_run = -INFINITY, l_run = 0.f;
+  float m2 = 0.f, inv_l = 0.f, mloc = 0.f;
+  f32x16 Od[D / 32];
+  if constexpr (PASS2) {
+    if (col_on) {
+      m2 = rs_col[0];
+      inv_l = 1.f / rs_col[1];
+    }
+#pragma unroll
+    for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+      for (int a = 0; a < 4; ++a) {
+        f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
+        if (col_on) v4 = *reinterpret_cast<const f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Od[dt][4 * a + e] = v4[e];
+      }
+  }
+  float* blk_I = nullptr;
+  float* blk_m = nullptr;
+  if constexpr (PASS2) {
+    if (col_on) {
+      const int n_vis = diag + 1;
+      blk_I = p.blk_stats + ((int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * p.S * 2 +
+              (int64_t)jr * n_vis;
+      blk_m = blk_I + (int64_t)p.S * n_vis;
+    }
+  }
+
+  const int total = nblk_wg * SUBS;
+  typename St::Regs regs;
+  St::load(regs, kbase, vbase, row_stride, 0, n_k, tid);
+  St::store(regs, smem, tid);
+  __syncthreads();
+  for (int it = 0; it < total; ++it) {
+    char* cur = smem + (it & 1) * St::BYTES;
+    const int blk = it / SUBS, sub = it % SUBS;
+    if (it + 1 < total) {
+      const int nb = (it + 1) / SUBS, ns = (it + 1) % SUBS;
+      St::load(regs, kbase, vbase, row_stride, nb * BLK + ns * kStageKeys, n_k, tid);
+    }
+    const int key0 = blk * BLK + sub * kStageKeys;
+    if (PASS2 && sub == 0) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
+      mloc = 0.f;
+    }
+    if (key0 <= wave_pos_max) {
+      f32x16 S[2];
+      S[0] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 0, lane);
+      S[1] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 1, lane);
+      const bool need_mask = key0 + kStageKeys - 1 > wave_pos_min;
+      if constexpr (!PASS2) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float s = (need_mask && key0 + acc_key(kt, r, g2) > my_pos) ? -INFINITY : S[kt][r];
+            S[kt][r] = s;
+            mx = fmaxf(mx, s);
+          }
+        mx = fmaxf(mx, wave_xor32(mx));
+        const float m_new = fmaxf(m_run, mx * c);
+        const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+        float rs = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
+            S[kt][r] = e;
+            rs += e;
+          }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
+        }
+      } else {
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            float e = (need_mask && key0 + acc_key(kt, r, g2) > my_pos)
+                          ? 0.f
+                          : __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m2));
+            S[kt][r] = e;
+            mloc += e;
+          }
+      }
+      pv_stage<T, D, St::V_STRIDE, SPLIT>(cur + St::K_BYTES, S, O, lane);
+    }
+    if constexpr (PASS2) {
+      if (sub == SUBS - 1 && wave_on && blk <= diag) {
+        const float mt = mloc + wave_xor32(mloc);
+        float ss = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float dv = __builtin_fmaf(-mt, Od[dt][r], O[dt][r]);
+            ss = __builtin_fmaf(dv, dv, ss);
+          }
+        ss += wave_xor32(ss);
+        if (col_on && g2 == 0) {
+          blk_I[blk] = __builtin_sqrtf(ss) * inv_l;
+          blk_m[blk] = mt * inv_l;
+        }
+      }
+    }
+    if (it + 1 < total) St::store(regs, smem + ((it + 1) & 1) * St::BYTES, tid);
+    __syncthreads();
+  }
+
+  if constexpr (!PASS2) {
+    const float l_tot = l_run + wave_xor32(l_run);
+    if (col_on) {
+      const float inv = 1.f / l_tot;
+      if (g2 == 0) {
+        rs_col[0] = m_run;
+        rs_col[1] = l_tot;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv};
+          *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2) = o;
+        }
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Threshold, ranking and compaction: one workgroup per (query head, tile).
+// ---------------------------------------------------------------------------
+
+constexpr int kThrThreads = 256;
+constexpr int kMaxVis = 4096;
+
+__device__ __forceinline__ int find_seq(const SeqTable& st, int gtile) {
+  int s = 0;
+  while (s + 1 < st.num_seqs && st.tile_start[s + 1] <= gtile) ++s;
+  return s;
+}
+
+// Exclusive prefix over the workgroup of (a, b) in thread order.
+__device__ __forceinline__ void block_excl_scan2(double a, double b, double& ea, double& eb, double* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  double ia = a, ib = b;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    double ta = __shfl_up(ia, o), tb = __shfl_up(ib, o);
+    if (lane >= o) { ia += ta; ib += tb; }
+  }
+  double xa = __shfl_up(ia, 1), xb = __shfl_up(ib, 1);
+  if (lane == 0) { xa = 0.0; xb = 0.0; }
+  if (lane == 63) { sh[wave] = ia; sh[4 + wave] = ib; }
+  __syncthreads();
+  double oa = 0.0, ob = 0.0;
+  for (int w = 0; w < wave; ++w) { oa += sh[w]; ob += sh[4 + w]; }
+  __syncthreads();
+  ea = oa + xa;
+  eb = ob + xb;
+}
+
+__device__ __forceinline__ int block_excl_scan_int(int a, int& total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ia = a;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int ta = __shfl_up(ia, o);
+    if (lane >= o) ia += ta;
+  }
+  if (lane == 63) sh[wave] = ia;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) off += sh[w];
+    total += sh[w];
+  }
+  __syncthreads();
+  return off + ia - a;
+}
+
+__device__ __forceinline__ int block_min_int(int v, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  if (lane == 0) sh[wave] = v;
+  __syncthreads();
+  int r = sh[0];
+  for (int w = 1; w < (int)(blockDim.x >> 6); ++w) r = min(r, sh[w]);
+  __syncthreads();
+  return r;
+}
+
+__global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
+  __shared__ uint64_t keys[kMaxVis];
+  __shared__ uint8_t keep[kMaxVis];
+  __shared__ double shd[8];
+  __shared__ int shi[8];
+  const int tid = threadIdx.x;
+  const int T = p.seqs.total_tiles;
+  const int R = blockIdx.x;
+  const int h = R / T, gtile = R % T;
+  const int seq = find_seq(p.seqs, gtile);
+  const int t = gtile - p.seqs.tile_start[seq];
+  const int B = p.seqs.block;
+  const int diag = p.seqs.diag0[seq] + t;
+  const int n_vis = diag + 1;
+  const int n_rows_t = min(B, p.seqs.n_q[seq] - t * B);
+  const int s_t = min(p.S, n_rows_t);
+  const int S = p.S;
+  const int64_t slot = (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
+  const float* Ib = p.blk_stats + slot * S * 2;
+  const float* Mb = Ib + (int64_t)S * n_vis;
+  const float tau = p.tau[h];
+  int n_pad = 2;
+  while (n_pad < n_vis) n_pad <<= 1;
+
+  auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
+  const float inv_s = 1.f / (float)s_t;
+  const int64_t diag_row = ((int64_t)h * T + gtile) * p.max_vis;
+  for (int b = tid; b < n_pad; b += kThrThreads) {
+    uint64_t key = ~0ull;
+    if (b < n_vis) {
+      float si = 0.f, sm = 0.f;
+      for (int i = 0; i < s_t; ++i) {
+        si += Ib[(int64_t)i * n_vis + b];
+        sm += Mb[(int64_t)i * n_vis + b];
+      }
+      const float score = si * inv_s, mass = sm * inv_s;
+      if (p.tile_scores) p.tile_scores[diag_row + b] = score;
+      if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
+      if (!mandatory(b)) key = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
+    }
+    keys[b] = key;
+  }
+  for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
+    if (p.tile_scores) p.tile_scores[diag_row + b] = -1.f;
+    if (p.tile_mass) p.tile_mass[diag_row + b] = -1.f;
+  }
+  __syncthreads();
+  // bitonic sort, ascending: discard order
+  for (int k = 2; k <= n_pad; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      for (int i = tid; i < n_pad; i += kThrThreads) {
+        const int ixj = i ^ j;
+        if (ixj > i) {
+          const uint64_t a = keys[i], b = keys[ixj];
+          const bool up = (i & k) == 0;
+          if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // |{b < n_sink} U {diag - n_local < b <= diag}| inside 0 .. diag
+  const int sink_hi = min(p.n_sink, n_vis);
+  const int loc_lo = max(0, diag - p.n_local + 1);
+  const int n_mand = sink_hi + (n_vis - loc_lo) - max(0, sink_hi - loc_lo);
+  const int n_cand = n_vis - n_mand;
+  const int E = n_pad >= kThrThreads ? n_pad / kThrThreads : 1;
+  auto id_at = [&](int k) { return (int)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull)); };
+
+  // first prefix length whose bound exceeds tau, over all sampled rows
+  int k_fail = n_cand + 1;
+  for (int i = 0; i < s_t; ++i) {
+    double a = 0.0, dl = 0.0;
+    for (int e = 0; e < E; ++e) {
+      const int k = tid * E + e;
+      if (k < n_cand) {
+        const int b = id_at(k);
+        a += (double)Ib[(int64_t)i * n_vis + b];
+        dl += (double)Mb[(int64_t)i * n_vis + b];
+      }
+    }
+    double pa, pd;
+    block_excl_scan2(a, dl, pa, pd, shd);
+    int local_fail = INT_MAX;
+    for (int e = 0; e < E; ++e) {
+      const int k = tid * E + e;
+      if (k < n_cand) {
+        const int b = id_at(k);
+        pa += (double)Ib[(int64_t)i * n_vis + b];
+        pd += (double)Mb[(int64_t)i * n_vis + b];
+        const double bound = (1.0 - pd > 0.0) ? pa / (1.0 - pd) : INFINITY;
+        if (bound > (double)tau && local_fail == INT_MAX) local_fail = k + 1;
+      }
+    }
+    k_fail = min(k_fail, block_min_int(local_fail, shi));
+  }
+  const int k_star = k_fail - 1;
+
+  if (p.row_bound) {
+    float* rb = p.row_bound + ((int64_t)h * T + gtile) * S;
+    for (int i = 0; i < s_t; ++i) {
+      double a = 0.0, dl = 0.0;
+      for (int e = 0; e < E; ++e) {
+        const int k = tid * E + e;
+        if (k < k_star) {
+          const int b = id_at(k);
+          a += (double)Ib[(int64_t)i * n_vis + b];
+          dl += (double)Mb[(int64_t)i * n_vis + b];
+        }
+      }
+      double pa, pd;
+      block_excl_scan2(a, dl, pa, pd, shd);
+      for (int e = 0; e < E; ++e) {
+        const int k = tid * E + e;
+        if (k < k_star) {
+          const int b = id_at(k);
+          pa += (double)Ib[(int64_t)i * n_vis + b];
+          pd += (double)Mb[(int64_t)i * n_vis + b];
+          if (k == k_star - 1) rb[i] = (float)((1.0 - pd > 0.0) ? pa / (1.0 - pd) : INFINITY);
+        }
+      }
+      if (k_star == 0 && tid == 0) rb[i] = 0.f;
+    }
+    for (int i = s_t + tid; i < S; i += kThrThreads) rb[i] = -1.f;
+  }
+
+  // retained set, compacted in ascending id order
+  for (int b = tid; b < n_vis; b += kThrThreads) keep[b] = 1;
+  __syncthreads();
+  for (int k = tid; k < k_star; k += kThrThreads) keep[id_at(k)] = 0;
+  __syncthreads();
+  const int E2 = (n_vis + kThrThreads - 1) / kThrThreads;
+  int cnt = 0;
+  for (int e = 0; e < E2; ++e) {
+    const int b = tid * E2 + e;
+    if (b < n_vis) cnt += keep[b];
+  }
+  int total;
+  int off = block_excl_scan_int(cnt, total, shi);
+  int32_t* out = p.slots + slot;
+  for (int e = 0; e < E2; ++e) {
+    const int b = tid * E2 + e;
+    if (b < n_vis && keep[b]) out[off++] = b;
+  }
+  if (tid == 0) p.counts[R] = total;
+}
+
+// Exclusive scan of the per-row counts into row_ptr (one workgroup).
+__global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t* __restrict__ counts, int32_t* __restrict__ row_ptr,
+                                                      int rows) {
+  __shared__ int sh[16];
+  const int tid = threadIdx.x;
+  const int E = (rows + 1023) / 1024;
+  int s = 0;
+  for (int e = 0; e < E; ++e) {
+    const int r = tid * E + e;
+    if (r < rows) s += counts[r];
+  }
+  int total;
+  int off = block_excl_scan_int(s, total, sh);
+  for (int e = 0; e < E; ++e) {
+    const int r = tid * E + e;
+    if (r < rows) {
+      row_ptr[r] = off;
+      off += counts[r];
+    }
+  }
+  if (tid == 0) row_ptr[rows] = total;
+}
+
+// Copy each row's ids from its slot to its CSR position.
+__global__ __launch_bounds__(64) void csr_scatter_kernel(SelectParams p) {
+  const int T = p.seqs.total_tiles;
+  const int R = blockIdx.x;
+  const int h = R / T, gtile = R % T;
+  const int seq = find_seq(p.seqs, gtile);
+  const int t = gtile - p.seqs.tile_start[seq];
+  const int32_t* src = p.slots + (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
+  const int n = p.counts[R];
+  int32_t* dst = p.block_idx + p.row_ptr[R];
+  for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
+}
+
+template <typename T, int D, int BLK>
+static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
+  const int TG = max(1, kSelWaves / p.col_tiles);
+  int items = 0;
+  for (int i = 0; i < p.seqs.num_seqs; ++i) items += (p.seqs.n_tiles[i] + TG - 1) / TG;
+  const int64_t rows = (int64_t)p.hq * p.seqs.total_tiles;
+  if (rows == 0) {
+    hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.row_ptr, 0);
+    return hipGetLastError();
+  }
+  const unsigned grid = (unsigned)((int64_t)items * p.hkv);
+  hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+  hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
+  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)rows), dim3(kThrThreads), 0, s, p);
+  hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.row_ptr, (int)rows);
+  hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)rows), dim3(64), 0, s, p);
+  return hipGetLastError();
+}
+
+template <typename T, int D>
+static hipError_t launch_sel_b(const SelectParams& p, int block, hipStream_t s) {
+  return block == 64 ? launch_sel<T, D, 64>(p, s) : launch_sel<T, D, 128>(p, s);
+}
+
+template <typename T>
+static hipError_t launch_sel_d(const SelectParams& p, int d, int block, hipStream_t s) {
+  return d == 64 ? launch_sel_b<T, 64>(p, block, s) : launch_sel_b<T, 128>(p, block, s);
+}
+
+hipError_t launch_select(const SelectParams& p, int in_dtype, int head_dim, int block, hipStream_t stream) {
+  return in_dtype == 0 ? launch_sel_d<uint16_t>(p, head_dim, block, stream)
+                       : launch_sel_d<float>(p, head_dim, block, stream);
+}
+
+}  // namespace poem

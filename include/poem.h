@@ -1,0 +1,172 @@
+/*
+ * poem.h - C ABI of libpoem: output-relative (POEM-style) block-sparse causal
+ * attention prefill for AMD Instinct MI355X (gfx950).
+ *
+ * The operation follows the POEM note on attention deletion error (Wu et al.,
+ * "POEM: Output-Relative Block-Sparse Attention for Long-Context Prefilling",
+ * arXiv:2611.13578): for one query and one head, a visible key block b carries
+ * the dense attention mass m_b and the weighted mean value v_b, the dense output
+ * is o = sum_b m_b v_b, dropping a set D of mass delta leaves an output error of
+ * exactly sum_D m_b (v_b - o) / (1 - delta) (its Section 4.1, Equation (3)), and
+ * the triangle inequality bounds its norm by sum_D I_b / (1 - delta) with the
+ * block score I_b = m_b ||v_b - o|| (Equation (4)). Head grouping, chunk
+ * positions, mandatory sink/local blocks and the tie rule follow "BFLA:
+ * Block-Filtered Long-Context Attention Mechanism" (Sections 3.3, 3.6, 5.1 and
+ * Appendix A, "Block ordering").
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * Pointers are DEVICE pointers unless the name ends in _host. Every call is
+ * asynchronous on the given HIP stream (pass a hipStream_t as void*; NULL is the
+ * default stream) and never synchronises the host. The library allocates no
+ * device memory and keeps no state between calls: the caller owns every buffer,
+ * including the selector workspace. Host arrays are read during the call only.
+ *
+ * Layout is packed "THD", token-major and contiguous in d:
+ *   Q [sum N_q][H_q][d], K and V [sum N_k][H_kv][d], sequences concatenated.
+ * Query head h reads KV head h / (H_q / H_kv) (BFLA Section 3.3).
+ * The N_q queries of a sequence sit at absolute positions N_k - N_q .. N_k - 1
+ * (BFLA Section 3.6); (N_k - N_q) must be a multiple of block_size. A query tile is
+ * block_size consecutive queries of ONE query head (the last one of a sequence may
+ * be shorter); key block b of a sequence holds keys b*B .. b*B+B-1. Tile t of a
+ * sequence has diagonal block T_t = (N_k - N_q)/B + t and sees blocks 0 .. T_t.
+ * Global tile index = sum over earlier sequences of ceil(N_q/B) + t.
+ * CSR row of (h, global tile) = h * num_tiles + global tile.
+ *
+ * Errors: every argument is validated on the host before anything is enqueued.
+ * A failing call returns a negative poem_status, writes nothing, and sets a
+ * thread-local message readable with poem_last_error(). A failed launch returns
+ * POEM_ERR_HIP. Nothing is thrown across the ABI. Calls are reentrant; calls on
+ * different streams may overlap.
+ */
+#ifndef POEM_H
+#define POEM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  POEM_OK = 0,
+  POEM_ERR_INVALID_ARG = -1, /* null pointer, negative size, bad enum, inconsistent shape */
+  POEM_ERR_UNSUPPORTED = -2, /* valid but outside the built kernels (head_dim, block_size, limits) */
+  POEM_ERR_WORKSPACE = -3,   /* workspace missing or smaller than poem_select_workspace_bytes() */
+  POEM_ERR_CAPACITY = -4,    /* block_idx capacity smaller than poem_csr_capacity() */
+  POEM_ERR_HIP = -5          /* a HIP runtime call or kernel launch failed */
+} poem_status;
+
+typedef enum { POEM_BF16 = 0, POEM_FP32 = 1 } poem_dtype;
+
+/* Limits of the built kernels (exceeding one returns POEM_ERR_UNSUPPORTED). */
+#define POEM_MAX_SEQS 64          /* sequences per call */
+#define POEM_MAX_ROWS_PER_TILE 32 /* sampled rows per tile in the selector */
+#define POEM_MAX_VISIBLE_BLOCKS 4096 /* key blocks visible to one tile in the selector */
+#define POEM_MAX_HEADS_Q 128       /* query heads in the selector (thresholds travel by value) */
+
+typedef struct {
+  int32_t num_seqs;              /* 1 .. POEM_MAX_SEQS */
+  const int32_t* seqlens_q_host; /* host [num_seqs]: N_q >= 0 per sequence */
+  const int32_t* seqlens_k_host; /* host [num_seqs]: N_k >= N_q, (N_k - N_q) % block_size == 0 */
+  int32_t num_heads_q;           /* H_q >= 1, a multiple of num_heads_kv */
+  int32_t num_heads_kv;          /* H_kv >= 1 */
+  int32_t head_dim;              /* d: 64 or 128 */
+  int32_t block_size;            /* B: 64 or 128 (query tile = key block) */
+  float softmax_scale;           /* <= 0 selects 1/sqrt(head_dim); must be finite */
+  int32_t in_dtype;              /* poem_dtype of Q, K and V */
+} poem_problem;
+
+/* Number of query tiles over all sequences (sum of ceil(N_q / B)); < 0 on error. */
+int64_t poem_num_tiles(const poem_problem* problem);
+
+/* Sum over (query head, tile) of the tile's visible blocks T_t + 1: the most ids a
+ * CSR produced by poem_select can hold. < 0 on error. */
+int64_t poem_csr_capacity(const poem_problem* problem);
+
+/* Largest T_t + 1 over all tiles (the row length of the selector's score outputs). */
+int64_t poem_max_visible_blocks(const poem_problem* problem);
+
+/* Bytes of device workspace poem_select needs (256-byte aligned start); < 0 on error. */
+int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile);
+
+/*
+ * poem_select: the output-relative block selector.
+ *
+ * For every (query head h, tile t) it samples S_t = min(rows_per_tile, n_t) rows
+ * r_j = ceil((j+1) n_t / S_t) - 1 of the tile (n_t = rows in the tile) and, for
+ * each sampled row i over the visible keys j <= its position, computes the dense
+ * softmax p_ij (scale * q.k, max subtracted), the dense output o_i, and per
+ * visible block b the mass m_ib = sum_{j in b} p_ij, the sum u_ib = sum_{j in b}
+ * p_ij v_j and the score I_ib = ||u_ib - m_ib o_i|| (= m_ib ||v_ib - o_i||; POEM
+ * note Section 4.1 and Equation (4)). The tile score is Ibar_b = mean_i I_ib.
+ * Mandatory blocks {b < n_sink_blocks} and {T_t - n_local_blocks < b <= T_t} are
+ * always kept (BFLA Sections 4 and 5.1). The other visible blocks are put in
+ * discard order: ascending Ibar_b, and among equal scores the larger id first (so
+ * the smaller id is retained first; BFLA Appendix A). With A_i(k), Delta_i(k) the
+ * sums of I_ib and m_ib over the first k blocks of that order, the bound is
+ * B(k) = max_i A_i(k) / (1 - Delta_i(k)) (+inf when 1 - Delta_i(k) <= 0), and the
+ * cut k* is the largest k with B(k') <= tau_host[h] for all k' <= k. The first k*
+ * blocks are discarded; the rest, with the mandatory blocks, form the tile's CSR
+ * row, in ascending id order (BFLA Appendix A).
+ *
+ *   q, k, v          device, in_dtype, THD layout above.
+ *   tau_host         host [H_q]: per-head threshold, finite and >= 0, in the units of V.
+ *   n_sink_blocks    >= 0;  n_local_blocks >= 1 (counts the diagonal block).
+ *   rows_per_tile    S, 1 .. POEM_MAX_ROWS_PER_TILE.
+ *   row_ptr          device int32 [H_q * num_tiles + 1]: CSR offsets (written).
+ *   block_idx        device int32 [block_idx_capacity]: CSR ids, local to the sequence (written).
+ *   block_idx_capacity  >= poem_csr_capacity(problem).
+ *   tile_scores      nullable device fp32 [H_q][num_tiles][max_visible]: Ibar_b; entries
+ *                    b > T_t are written as -1.
+ *   tile_mass        nullable, same shape: mean_i m_ib (-1 beyond T_t).
+ *   row_bound        nullable device fp32 [H_q][num_tiles][rows_per_tile]: the per-row bound
+ *                    A_i(k*) / (1 - Delta_i(k*)) at the cut (-1 for rows beyond S_t).
+ *   workspace        device, >= poem_select_workspace_bytes(problem, rows_per_tile) bytes,
+ *                    256-byte aligned; contents on entry are ignored.
+ * Requires every tile to see at most POEM_MAX_VISIBLE_BLOCKS blocks, H_q <= POEM_MAX_HEADS_Q
+ * and (H_q / H_kv) * rows_per_tile <= 128.
+ */
+poem_status poem_select(const poem_problem* problem, const void* q, const void* k, const void* v,
+                        const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                        int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                        int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
+                        float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * poem_sparse_prefill: causal softmax attention of each query tile over the key
+ * blocks its CSR row lists, i.e. the masked softmax over {j <= position : block(j)
+ * listed} with scores scale * q.k. This is the retained-block attention the POEM
+ * note's sparse output o_tilde denotes (Section 4.1); the loop skips unlisted
+ * blocks, as BFLA's support-restricted kernel does (Section 3.4).
+ *
+ *   row_ptr, block_idx  device int32 CSR as produced by poem_select (rows as above). Each
+ *                    row must be strictly ascending; ids > T_t are skipped; a row with
+ *                    no usable id yields O = 0 and LSE = -inf.
+ *   out              device [sum N_q][H_q][d] in out_dtype (POEM_BF16 or POEM_FP32).
+ *   lse              nullable device fp32 [H_q][sum N_q]: natural-log sum of exp of the scores.
+ */
+poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, const void* k,
+                                const void* v, const int32_t* row_ptr, const int32_t* block_idx,
+                                void* out, int32_t out_dtype, float* lse, void* stream);
+
+/*
+ * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t
+ * (dense causal attention, the speedup baseline). Arguments as above.
+ */
+poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k,
+                               const void* v, void* out, int32_t out_dtype, float* lse,
+                               void* stream);
+
+/* Message of the last failing call on this thread ("" if none); valid until the next call. */
+const char* poem_last_error(void);
+
+/* Library version string. */
+const char* poem_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* POEM_H */

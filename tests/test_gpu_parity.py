@@ -1,0 +1,372 @@
+"""GPU parity of libpoem (through its C ABI) against the fp64 oracle.
+
+Small problems are compared element by element; the full-size workloads run in
+the benchmark's launch configuration and are checked on stratified tiles the
+oracle computes one by one.
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+
+from block_sparse_attention_poem_amd import _lib as L
+from block_sparse_attention_poem_amd import synth
+from oracle import poem_oracle as O
+
+from . import helpers as H
+
+pytestmark = pytest.mark.gpu
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    L.load()
+    yield
+    torch.cuda.synchronize()
+
+
+def _sync():
+    import torch
+    torch.cuda.synchronize()
+
+
+# ---------------------------------------------------------------------------
+# the three-block toy through the C ABI
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("shift", [0.0, 10.0])
+def test_toy_through_c_abi(shift):
+    import torch
+    q, k, v, meta = synth.toy_block_inputs(shift)
+    p = L.Problem([meta["n_q"]], [meta["n_k"]], 1, 1, meta["d"], meta["block"], 1.0, "fp32")
+    qd, kd, vd = (torch.from_numpy(x).cuda() for x in (q, k, v))
+    say("toy shift", shift)
+    dense, _ = L.dense_prefill(p, qd, kd, vd, out_dtype="fp32")
+    for tau, drop in ((0.5, []), (0.7, [2]), (2.0, [1, 2])):
+        r = L.select(p, qd, kd, vd, [tau], 1, 1, 8, diagnostics=True)
+        sp, _ = L.sparse_prefill(p, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+        _sync()
+        sc = r["tile_scores"][0, 0, :4].cpu().numpy()
+        assert np.allclose(sc, [0, 0.5, 0.5, 0], atol=1e-6), sc
+        rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+        kept = H.retained(rp, bi, 0)
+        assert kept == sorted(set(range(4)) - set(drop)), (tau, kept)
+        err = (dense[:, 0, 0] - sp[:, 0, 0]).abs().max().item()
+        expect = {0.5: 0.0, 0.7: 2 / 3, 2.0: 0.0}[tau]
+        assert abs(err - expect) < 1e-5, (tau, err)
+        assert np.allclose(dense[:, 0, 0].cpu().numpy(), 2.0 + shift, atol=1e-6)
+        rb = r["row_bound"][0, 0].cpu().numpy()
+        assert np.all(rb <= tau + 1e-6)
+
+
+# ---------------------------------------------------------------------------
+# dense and sparse attention on small problems, element by element
+# ---------------------------------------------------------------------------
+
+SMALL = [
+    # (n_q, n_k, hq, hkv, d, B, dtype, seqs)
+    (300, 428, 4, 2, 64, 64, "bf16", 1),
+    (300, 300, 4, 1, 128, 128, "bf16", 1),
+    (200, 456, 8, 2, 128, 128, "bf16", 1),
+    (130, 258, 2, 2, 64, 128, "bf16", 1),
+    (190, 318, 4, 4, 128, 64, "bf16", 1),
+    (300, 428, 2, 1, 64, 64, "fp32", 1),
+    (129, 385, 2, 1, 128, 128, "fp32", 1),
+    (100, 356, 4, 2, 128, 128, "bf16", 3),
+]
+
+
+def _small(case, seed=0):
+    n_q, n_k, hq, hkv, d, B, dt, seqs = case
+    w = synth.small_workload(n_q=n_q, n_k=n_k, hq=hq, hkv=hkv, d=d, block=B, dtype=dt, seqs=seqs, seed=seed)
+    if seqs > 1:  # varlen: different prefix lengths per sequence, same chunk size
+        w = w.with_(seqlens_k=tuple(n_k + B * i for i in range(seqs)), seqlens_q=tuple(n_q - 17 * i for i in range(seqs)))
+        w = w.with_(seqlens_k=tuple(nk - 17 * i for i, nk in enumerate(w.seqlens_k)))
+    return w
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "q%d_k%d_h%d-%d_d%d_B%d_%s_s%d" % c)
+def test_dense_matches_oracle(case):
+    w = _small(case)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("dense", case)
+    out, lse = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    _sync()
+    out = out.cpu().numpy()
+    lse = lse.cpu().numpy()
+    q, k, v = H.f64(inp)
+    ref = O.dense_prefill(op, q, k, v)
+    atol = H.OUT_ATOL_FP32 if w.dtype == "fp32" else H.OUT_ATOL_BF16
+    latol = H.LSE_ATOL_FP32 if w.dtype == "fp32" else H.LSE_ATOL_BF16
+    worst = 0.0
+    for (h, gt), (Or, lr) in ref.items():
+        r0, n = H.tile_rows(op, gt)
+        err = np.abs(out[r0:r0 + n, h, :] - Or).max()
+        worst = max(worst, err)
+        assert err <= atol, (h, gt, err)
+        assert H.lse_close(lse[h, r0:r0 + n], lr, latol), (h, gt)
+    say("  max abs err", worst)
+
+
+def _random_csr(op, rng, p_keep=0.4, empty_rows=True):
+    tl = O.tiles(op)
+    rows = []
+    for h in range(op.num_heads_q):
+        for t in tl:
+            ids = [b for b in range(t.diag + 1) if rng.uniform() < p_keep or b in (0, t.diag)]
+            if empty_rows and rng.uniform() < 0.1:
+                ids = []
+            rows.append(ids)
+    rp = np.zeros(len(rows) + 1, np.int64)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    bi = np.array([b for r in rows for b in r], np.int32)
+    return rp, bi
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "q%d_k%d_h%d-%d_d%d_B%d_%s_s%d" % c)
+def test_sparse_given_mask_matches_oracle(case):
+    import torch
+    w = _small(case, seed=1)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    rng = np.random.default_rng(7)
+    rp, bi = _random_csr(op, rng)
+    rpd = torch.from_numpy(rp.astype(np.int32)).cuda()
+    bid = torch.from_numpy(np.concatenate([bi, np.zeros(1, np.int32)])).cuda()
+    say("sparse given mask", case)
+    out, lse = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32")
+    _sync()
+    out = out.cpu().numpy()
+    lse = lse.cpu().numpy()
+    q, k, v = H.f64(inp)
+    ref = O.sparse_prefill(op, q, k, v, rp, bi)
+    atol = H.OUT_ATOL_FP32 if w.dtype == "fp32" else H.OUT_ATOL_BF16
+    latol = H.LSE_ATOL_FP32 if w.dtype == "fp32" else H.LSE_ATOL_BF16
+    for (h, gt), (Or, lr) in ref.items():
+        r0, n = H.tile_rows(op, gt)
+        err = np.abs(out[r0:r0 + n, h, :] - Or).max()
+        assert err <= atol, (h, gt, err)
+        assert H.lse_close(lse[h, r0:r0 + n], lr, latol), (h, gt)
+
+
+@pytest.mark.parametrize("case", [SMALL[0], SMALL[2], SMALL[5]], ids=lambda c: "q%d_k%d_h%d-%d_d%d_B%d_%s_s%d" % c)
+def test_sparse_full_list_is_bitwise_dense(case):
+    import torch
+    w = _small(case, seed=2)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    tl = O.tiles(op)
+    rows = [list(range(t.diag + 1)) for h in range(op.num_heads_q) for t in tl]
+    rp = np.zeros(len(rows) + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    bi = np.array([b for r in rows for b in r], np.int32)
+    say("bitwise", case)
+    for od in ("fp32", "bf16"):
+        d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype=od)
+        s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, torch.from_numpy(rp).cuda(), torch.from_numpy(bi).cuda(),
+                                        out_dtype=od)
+        _sync()
+        assert torch.equal(d_out.view(torch.int16) if od == "bf16" else d_out.view(torch.int32),
+                           s_out.view(torch.int16) if od == "bf16" else s_out.view(torch.int32))
+        assert torch.equal(d_lse, s_lse)
+
+
+def test_empty_and_out_of_range_rows():
+    import torch
+    w = _small(SMALL[0], seed=3)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    tl = O.tiles(op)
+    rows = []
+    for h in range(op.num_heads_q):
+        for t in tl:
+            rows.append([] if (h + t.gtile) % 2 == 0 else [0, t.diag + 1, t.diag + 5])
+    rp = np.zeros(len(rows) + 1, np.int32)
+    rp[1:] = np.cumsum([len(r) for r in rows])
+    bi = np.array([b for r in rows for b in r], np.int32)
+    say("empty rows")
+    out, lse = L.sparse_prefill(gp, qd, kd, vd, torch.from_numpy(rp).cuda(), torch.from_numpy(bi).cuda(),
+                                out_dtype="fp32")
+    _sync()
+    out, lse = out.cpu().numpy(), lse.cpu().numpy()
+    q, k, v = H.f64(inp)
+    for h in range(op.num_heads_q):
+        for t in tl:
+            r0, n = t.q_row0, t.n_rows
+            if (h + t.gtile) % 2 == 0:
+                assert np.all(out[r0:r0 + n, h] == 0.0)
+                assert np.all(np.isneginf(lse[h, r0:r0 + n]))
+            else:  # ids above the diagonal are skipped: only block 0 is used
+                Or, lr = O.tile_attention(op, q, k, v, h, t, [0])
+                assert np.abs(out[r0:r0 + n, h] - Or).max() <= H.OUT_ATOL_BF16
+
+
+def test_bf16_output_is_rounded_fp32_output():
+    import torch
+    w = _small(SMALL[1], seed=4)
+    inp = synth.make(w)
+    gp, _ = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("bf16 output")
+    o32, l32 = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    o16, l16 = L.dense_prefill(gp, qd, kd, vd, out_dtype="bf16")
+    _sync()
+    assert torch.equal(o32.to(torch.bfloat16).view(torch.int16), o16.view(torch.int16))
+    assert torch.equal(l32, l16)
+
+
+# ---------------------------------------------------------------------------
+# selector on small problems
+# ---------------------------------------------------------------------------
+
+SEL = [
+    # (n_q, n_k, hq, hkv, d, B, dtype, seqs), sink_offset, n_local
+    ((300, 428, 4, 1, 64, 64, "bf16", 1), 6.0, 1),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 6.0, 1),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), 5.0, 2),
+    ((300, 428, 2, 1, 64, 64, "fp32", 1), 6.0, 1),
+    ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1),
+    ((64, 4160, 2, 1, 64, 64, "bf16", 1), 7.0, 1),
+]
+
+
+def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_sparse=None):
+    """Scores, masks (with exemptions) and the bound theorem on the (h, gtile) pairs in which."""
+    T = L.num_tiles(gp)
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    scores = r["tile_scores"].cpu().numpy()
+    bounds = r["row_bound"].cpu().numpy()
+    sels = O.select(op, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which)
+    n_cand = n_match = 0
+    worst_score = 0.0
+    for (h, gt), sel in sels.items():
+        tau = float(inp.tau[h])
+        n_vis = sel.tile.diag + 1
+        se, sm, info = H.score_errors(sel, scores[h, gt], tau)
+        worst_score = max(worst_score, se)
+        assert se <= H.SCORE_RTOL, (h, gt, se, info)
+        assert sm <= H.MANDATORY_SCORE_RTOL, (h, gt, sm)
+        assert np.all(scores[h, gt, n_vis:] == -1.0)
+        kept = H.retained(rp, bi, h * T + gt)
+        assert kept == sorted(kept) and len(set(kept)) == len(kept)
+        assert set(sel.mandatory) <= set(kept)
+        nc, nm, bad = H.mask_agreement(sel, kept, tau, tau / n_vis)
+        n_cand += nc
+        n_match += nm
+        assert not bad, (h, gt, bad)
+        # the bound theorem for each sampled row, exact arithmetic on the GPU's mask
+        t = sel.tile
+        od, _ = O.tile_attention(op, q, k, v, h, t)
+        osp, _ = O.tile_attention(op, q, k, v, h, t, kept)
+        for j, row in enumerate(sel.rows):
+            err = float(np.linalg.norm(od[row] - osp[row]))
+            b = float(bounds[h, gt, j])
+            assert b <= tau * (1 + 1e-6), (h, gt, j, b, tau)
+            assert err <= b * (1 + 1e-3) + 1e-6, (h, gt, j, err, b)
+            if gpu_dense is not None:
+                ge = float(np.linalg.norm(gpu_dense[t.q_row0 + row, h].astype(np.float64) -
+                                          gpu_sparse[t.q_row0 + row, h].astype(np.float64)))
+                assert ge <= b * (1 + 1e-3) + 2e-4, (h, gt, j, ge, b)
+        assert np.all(bounds[h, gt, len(sel.rows):] == -1.0)
+    return n_cand, n_match, worst_score
+
+
+@pytest.mark.parametrize("case,sink,n_local", SEL, ids=lambda x: str(x))
+def test_selector_matches_oracle(case, sink, n_local):
+    w = _small(case, seed=5).with_(sink_offset=sink, n_local_blocks=n_local)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("selector", case, sink, n_local)
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy())
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
+# ---------------------------------------------------------------------------
+# the workloads at full size
+# ---------------------------------------------------------------------------
+
+
+def test_workload1_full():
+    """Single head, d=64, N=2048, fp32, B=64: every tile, every output."""
+    w = synth.WORKLOADS[1]
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("workload 1 full")
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(0, t.gtile) for t in O.tiles(op)]
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy())
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    ref_d = O.dense_prefill(op, q, k, v)
+    ref_s = O.sparse_prefill(op, q, k, v, rp, bi)
+    do, so = d_out.cpu().numpy(), s_out.cpu().numpy()
+    for key in ref_d:
+        r0, n = H.tile_rows(op, key[1])
+        assert np.abs(do[r0:r0 + n, 0] - ref_d[key][0]).max() <= H.OUT_ATOL_FP32
+        assert np.abs(so[r0:r0 + n, 0] - ref_s[key][0]).max() <= H.OUT_ATOL_FP32
+
+
+@pytest.mark.parametrize("wid", [2, 3, 4, 5])
+def test_workload_full_size_sampled(wid):
+    """Full-size run in the benchmark's configuration; oracle on stratified tiles."""
+    import torch
+    w = synth.WORKLOADS[wid]
+    say("workload", wid, "generate")
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("workload", wid, "select + dense + sparse")
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    keep = len(bi[:rp[-1]]) / L.csr_capacity(gp)
+    say("  keep fraction", keep)
+    q, k, v = H.f64(inp)
+    heads = sorted({0, w.num_heads_q - 1, w.num_heads_q // 2 + 1})
+    which = H.stratified_tiles(op, heads, per_head=3, seed=wid)
+    do, so = d_out.cpu().numpy(), s_out.cpu().numpy()
+    del d_out, s_out
+    torch.cuda.empty_cache()
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, do, so)
+    say("  sampled candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+    dl, sl = d_lse.cpu().numpy(), s_lse.cpu().numpy()
+    T = L.num_tiles(gp)
+    for (h, gt) in which[:8]:
+        t = O.tiles(op)[gt]
+        Od, ld = O.tile_attention(op, q, k, v, h, t)
+        ids = H.retained(rp, bi, h * T + gt)
+        Os, ls = O.tile_attention(op, q, k, v, h, t, ids)
+        r0, n = t.q_row0, t.n_rows
+        assert np.abs(do[r0:r0 + n, h] - Od).max() <= H.OUT_ATOL_BF16
+        assert np.abs(so[r0:r0 + n, h] - Os).max() <= H.OUT_ATOL_BF16
+        assert H.lse_close(dl[h, r0:r0 + n], ld, H.LSE_ATOL_BF16)
+        assert H.lse_close(sl[h, r0:r0 + n], ls, H.LSE_ATOL_BF16)

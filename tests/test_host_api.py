@@ -1,0 +1,168 @@
+"""Host-side tests of libpoem's C ABI (no GPU needed).
+
+The library must load without a GPU, export every symbol include/poem.h declares,
+and reject every invalid argument with the documented status before anything is
+enqueued (so these calls never touch the HIP runtime's device paths).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+from block_sparse_attention_poem_amd import _lib as L
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = ctypes.c_void_p(0x100000)  # never dereferenced: validation fails first
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(L.LIB_PATH):
+        pytest.fail("libpoem.so is not built; run python -m block_sparse_attention_poem_amd.build")
+    return L.load()
+
+
+def header_functions():
+    src = open(os.path.join(ROOT, "include", "poem.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(poem_[a-z_]+)\s*\(", src)))
+
+
+def test_exports_every_declared_symbol(lib):
+    declared = header_functions()
+    assert set(declared) == set(L.SYMBOLS), declared
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert "gfx950" in L.version()
+
+
+def prob(**kw):
+    d = dict(seqlens_q=[300], seqlens_k=[428], num_heads_q=4, num_heads_kv=2, head_dim=64, block_size=64,
+             softmax_scale=0.0, dtype="bf16")
+    d.update(kw)
+    return L.Problem(**d)
+
+
+def test_geometry_queries(lib):
+    p = prob()
+    # tiles of 64 rows: 5 tiles, diagonals 2..6 -> visible 3..7
+    assert L.num_tiles(p) == 5
+    assert L.max_visible_blocks(p) == 7
+    assert L.csr_capacity(p) == 4 * (3 + 4 + 5 + 6 + 7)
+    p2 = prob(seqlens_q=[64, 0, 100], seqlens_k=[128, 64, 100])
+    assert L.num_tiles(p2) == 1 + 0 + 2
+    assert L.csr_capacity(p2) == 4 * (2 + 1 + 2)
+    ws = L.select_workspace_bytes(p, 8)
+    assert ws > 0 and ws % 256 == 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seqlens_q=[300], seqlens_k=[429]), L.POEM_ERR_INVALID_ARG),   # N_k - N_q not a multiple of B
+    (dict(seqlens_q=[300], seqlens_k=[200]), L.POEM_ERR_INVALID_ARG),   # N_k < N_q
+    (dict(seqlens_q=[-1], seqlens_k=[64]), L.POEM_ERR_INVALID_ARG),
+    (dict(num_heads_q=3, num_heads_kv=2), L.POEM_ERR_INVALID_ARG),
+    (dict(num_heads_q=0), L.POEM_ERR_INVALID_ARG),
+    (dict(head_dim=96), L.POEM_ERR_UNSUPPORTED),
+    (dict(head_dim=0), L.POEM_ERR_INVALID_ARG),
+    (dict(block_size=32), L.POEM_ERR_UNSUPPORTED),
+    (dict(block_size=-64), L.POEM_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("nan")), L.POEM_ERR_INVALID_ARG),
+    (dict(softmax_scale=float("inf")), L.POEM_ERR_INVALID_ARG),
+    (dict(seqlens_q=[64] * 65, seqlens_k=[64] * 65), L.POEM_ERR_UNSUPPORTED),
+    (dict(seqlens_q=[], seqlens_k=[]), L.POEM_ERR_INVALID_ARG),
+])
+def test_problem_validation(lib, kw, status):
+    p = prob(**kw).c()
+    assert lib.poem_num_tiles(ctypes.byref(p)) == status
+    assert lib.poem_last_error().decode() != ""
+    rc = lib.poem_dense_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None)
+    assert rc == status
+
+
+def test_bad_dtype_and_null_problem(lib):
+    p = prob().c()
+    p.in_dtype = 7
+    assert lib.poem_num_tiles(ctypes.byref(p)) == L.POEM_ERR_INVALID_ARG
+    assert lib.poem_num_tiles(None) == L.POEM_ERR_INVALID_ARG
+    assert "NULL" in lib.poem_last_error().decode()
+
+
+def _select(lib, p, **over):
+    cp = p.c()
+    H = p.num_heads_q
+    args = dict(q=FAKE, k=FAKE, v=FAKE, tau=(ctypes.c_float * H)(*([0.05] * H)), sink=1, local=1, S=8,
+                row_ptr=FAKE, block_idx=FAKE, cap=L.csr_capacity(p), ts=None, tm=None, rb=None,
+                ws=ctypes.c_void_p(0x200000), ws_bytes=L.select_workspace_bytes(p, 8))
+    args.update(over)
+    return lib.poem_select(ctypes.byref(cp), args["q"], args["k"], args["v"], args["tau"], args["sink"],
+                           args["local"], args["S"], args["row_ptr"], args["block_idx"], args["cap"], args["ts"],
+                           args["tm"], args["rb"], args["ws"], args["ws_bytes"], None)
+
+
+def test_select_validation(lib):
+    p = prob()
+    H = p.num_heads_q
+    cases = [
+        (dict(q=None), L.POEM_ERR_INVALID_ARG),
+        (dict(row_ptr=None), L.POEM_ERR_INVALID_ARG),
+        (dict(tau=None), L.POEM_ERR_INVALID_ARG),
+        (dict(tau=(ctypes.c_float * H)(0.05, -0.1, 0.05, 0.05)), L.POEM_ERR_INVALID_ARG),
+        (dict(tau=(ctypes.c_float * H)(0.05, float("nan"), 0.05, 0.05)), L.POEM_ERR_INVALID_ARG),
+        (dict(tau=(ctypes.c_float * H)(0.05, float("inf"), 0.05, 0.05)), L.POEM_ERR_INVALID_ARG),
+        (dict(sink=-1), L.POEM_ERR_INVALID_ARG),
+        (dict(local=0), L.POEM_ERR_INVALID_ARG),
+        (dict(S=0), L.POEM_ERR_INVALID_ARG),
+        (dict(S=33), L.POEM_ERR_UNSUPPORTED),
+        (dict(cap=L.csr_capacity(p) - 1), L.POEM_ERR_CAPACITY),
+        (dict(ws=None), L.POEM_ERR_WORKSPACE),
+        (dict(ws_bytes=L.select_workspace_bytes(p, 8) - 1), L.POEM_ERR_WORKSPACE),
+        (dict(ws=ctypes.c_void_p(0x200010)), L.POEM_ERR_WORKSPACE),
+    ]
+    for over, status in cases:
+        assert _select(lib, p, **over) == status, over
+        assert lib.poem_last_error().decode() != ""
+
+
+def test_select_limits(lib):
+    # 16 query heads per KV head x 16 rows = 256 columns > 128
+    p = prob(num_heads_q=16, num_heads_kv=1)
+    assert L.select_workspace_bytes(p, 8) > 0
+    cp = p.c()
+    assert lib.poem_select_workspace_bytes(ctypes.byref(cp), 16) == L.POEM_ERR_UNSUPPORTED
+    # more than POEM_MAX_VISIBLE_BLOCKS blocks visible to a tile
+    big = prob(seqlens_q=[64], seqlens_k=[64 * 5000])
+    assert _select(lib, big) == L.POEM_ERR_UNSUPPORTED
+    heads = prob(num_heads_q=130, num_heads_kv=65)
+    tau = (ctypes.c_float * 130)(*([0.05] * 130))
+    assert _select(lib, heads, tau=tau) == L.POEM_ERR_UNSUPPORTED
+
+
+def test_attention_validation(lib):
+    cp = prob().c()
+    assert lib.poem_dense_prefill(ctypes.byref(cp), None, FAKE, FAKE, FAKE, L.POEM_FP32, None, None) == \
+        L.POEM_ERR_INVALID_ARG
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, L.POEM_FP32, None, None) == \
+        L.POEM_ERR_INVALID_ARG
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 5, None, None) == \
+        L.POEM_ERR_INVALID_ARG
+    assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, FAKE, FAKE, L.POEM_FP32, None,
+                                   None) == L.POEM_ERR_INVALID_ARG
+    assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, None, FAKE, L.POEM_FP32, None,
+                                   None) == L.POEM_ERR_INVALID_ARG
+
+
+def test_error_is_thread_local(lib):
+    import threading
+    cp = prob(head_dim=96).c()
+    assert lib.poem_num_tiles(ctypes.byref(cp)) == L.POEM_ERR_UNSUPPORTED
+    seen = {}
+
+    def other():
+        seen["msg"] = lib.poem_last_error().decode()
+
+    th = threading.Thread(target=other)
+    th.start()
+    th.join()
+    assert seen["msg"] == ""
+    assert "head_dim" in lib.poem_last_error().decode()
