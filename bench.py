@@ -145,6 +145,7 @@ def main():
     gp = L.Problem(list(w.seqlens_q), list(w.seqlens_k), w.num_heads_q, w.num_heads_kv, w.head_dim, w.block_size,
                    0.0, w.dtype)
     ws = L.SelectWorkspace(gp, w.rows_per_tile)
+    sws = L.SparseWorkspace(gp)
     T = L.num_tiles(gp)
     cap = L.csr_capacity(gp)
     row_ptr = torch.empty(w.num_heads_q * T + 1, dtype=torch.int32, device="cuda")
@@ -168,7 +169,7 @@ def main():
     def sparse():
         L._check(lib.poem_sparse_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(row_ptr),
                                          L._ptr(block_idx), L._ptr(out), odt, L._ptr(lse),
-                                         ctypes.c_void_p(stream.cuda_stream)))
+                                         ctypes.c_void_p(sws.ptr), sws.nbytes, ctypes.c_void_p(stream.cuda_stream)))
 
     def dense():
         L._check(lib.poem_dense_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(out), odt,
@@ -241,6 +242,8 @@ def main():
         "eff_tflops_sparse_kernel": attn_tflops,
         "dense_tflops": (flop_dense / (float(np.median(t_dense)) * 1e-3) / 1e12) if t_dense is not None else None,
         "keep_fraction_blocks": kept_blocks / cap,
+        "keep_fraction_per_head": [round(float(x), 4) for x in
+                                   (np.diff(rp).reshape(w.num_heads_q, T).sum(1) / (cap / w.num_heads_q))],
         "keep_fraction_pairs": p_ret / p_dense,
         "roofline": roofline,
     }

@@ -5,6 +5,6 @@ declared in include/poem.h). This package holds the ctypes binding
 (``_lib``), the in-tree build (``build``) and the seeded synthetic inputs
 (``synth``).
 """
-from ._lib import (POEM_BF16, POEM_FP32, PoemError, Problem, SelectWorkspace, csr_capacity,  # noqa: F401
-                   dense_prefill, flops_dense, load, max_visible_blocks, num_tiles, select,
-                   select_workspace_bytes, sparse_prefill, version)
+from ._lib import (POEM_BF16, POEM_FP32, PoemError, Problem, SelectWorkspace, SparseWorkspace,  # noqa: F401
+                   csr_capacity, dense_prefill, flops_dense, load, max_visible_blocks, num_tiles, select,
+                   select_workspace_bytes, sparse_prefill, sparse_workspace_bytes, version)

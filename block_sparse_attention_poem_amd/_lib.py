@@ -21,7 +21,8 @@ POEM_BF16, POEM_FP32 = 0, 1
 STATUS_NAMES = {0: "POEM_OK", -1: "POEM_ERR_INVALID_ARG", -2: "POEM_ERR_UNSUPPORTED", -3: "POEM_ERR_WORKSPACE",
                 -4: "POEM_ERR_CAPACITY", -5: "POEM_ERR_HIP"}
 SYMBOLS = ["poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_select_workspace_bytes",
-           "poem_select", "poem_sparse_prefill", "poem_dense_prefill", "poem_last_error", "poem_version"]
+           "poem_sparse_workspace_bytes", "poem_select", "poem_sparse_prefill", "poem_dense_prefill",
+           "poem_last_error", "poem_version"]
 
 
 class PoemError(RuntimeError):
@@ -53,17 +54,22 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"libpoem is not built ({path} missing): run python -m block_sparse_attention_poem_amd.build")
+    # torch ships its own HIP runtime with the same soname as ROCm's. Importing torch
+    # first makes libpoem bind to that runtime, so the process has one HIP runtime and
+    # torch's stream handles are valid inside the library. Loaded the other way round,
+    # two runtimes coexist and launches from the library find no device.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(CProblem)
     vp, i32, i64, f32p = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_float)
-    for name in ("poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks"):
+    for name in ("poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_sparse_workspace_bytes"):
         getattr(lib, name).argtypes = [P]
         getattr(lib, name).restype = i64
     lib.poem_select_workspace_bytes.argtypes = [P, i32]
     lib.poem_select_workspace_bytes.restype = i64
     lib.poem_select.argtypes = [P, vp, vp, vp, f32p, i32, i32, i32, vp, vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
     lib.poem_select.restype = ctypes.c_int
-    lib.poem_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.poem_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.poem_sparse_prefill.restype = ctypes.c_int
     lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp]
     lib.poem_dense_prefill.restype = ctypes.c_int
@@ -128,6 +134,10 @@ def max_visible_blocks(problem: Problem) -> int:
     return _i64(load().poem_max_visible_blocks(ctypes.byref(problem.c())))
 
 
+def sparse_workspace_bytes(problem: Problem) -> int:
+    return _i64(load().poem_sparse_workspace_bytes(ctypes.byref(problem.c())))
+
+
 def select_workspace_bytes(problem: Problem, rows_per_tile: int) -> int:
     return _i64(load().poem_select_workspace_bytes(ctypes.byref(problem.c()), int(rows_per_tile)))
 
@@ -172,15 +182,29 @@ def _check_qkv(problem: Problem, q, k, v):
             raise ValueError(f"{name} must be contiguous")
 
 
-class SelectWorkspace:
-    """A reusable device workspace for select() (bytes from poem_select_workspace_bytes)."""
+class Workspace:
+    """A reusable 256-byte-aligned device workspace of nbytes bytes."""
 
-    def __init__(self, problem: Problem, rows_per_tile: int, device="cuda"):
+    def __init__(self, nbytes: int, device="cuda"):
         torch = _torch()
-        self.nbytes = select_workspace_bytes(problem, rows_per_tile)
+        self.nbytes = int(nbytes)
         self.buf = torch.empty(max(self.nbytes, 256) + 256, dtype=torch.uint8, device=device)
         base = self.buf.data_ptr()
         self.ptr = (base + 255) & ~255
+
+
+class SelectWorkspace(Workspace):
+    """Workspace for select() (poem_select_workspace_bytes)."""
+
+    def __init__(self, problem: Problem, rows_per_tile: int, device="cuda"):
+        super().__init__(select_workspace_bytes(problem, rows_per_tile), device)
+
+
+class SparseWorkspace(Workspace):
+    """Workspace for sparse_prefill()'s row schedule (poem_sparse_workspace_bytes)."""
+
+    def __init__(self, problem: Problem, device="cuda"):
+        super().__init__(sparse_workspace_bytes(problem), device)
 
 
 def select(problem: Problem, q, k, v, tau, n_sink_blocks: int = 1, n_local_blocks: int = 1,
@@ -222,14 +246,21 @@ def _alloc_out(problem: Problem, out_dtype: str, want_lse: bool, device):
 
 
 def sparse_prefill(problem: Problem, q, k, v, row_ptr, block_idx, out_dtype: str = "bf16", want_lse: bool = True,
-                   out=None, lse=None, stream=None):
-    """Run poem_sparse_prefill. Returns (out, lse)."""
+                   out=None, lse=None, workspace="auto", stream=None):
+    """Run poem_sparse_prefill. Returns (out, lse).
+
+    workspace: a SparseWorkspace, "auto" (allocate one: persistent, count-ordered
+    schedule) or None (one workgroup per row)."""
     _check_qkv(problem, q, k, v)
     if out is None:
         out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+    if isinstance(workspace, str):
+        workspace = SparseWorkspace(problem, q.device)
+    wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.nbytes if workspace is not None else 0
     _check(load().poem_sparse_prefill(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
                                       _ptr(block_idx), _ptr(out), POEM_FP32 if out_dtype == "fp32" else POEM_BF16,
-                                      _ptr(lse), _stream_ptr(stream)))
+                                      _ptr(lse), wp, wb, _stream_ptr(stream)))
     return out, lse
 
 

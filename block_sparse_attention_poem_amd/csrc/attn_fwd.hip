@@ -21,27 +21,24 @@ namespace poem {
 template <typename T, int D>
 constexpr int attn_waves_per_eu() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
-template <typename T, int D, int BLK, bool SPARSE>
-__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
-void attn_fwd_kernel(AttnParams p) {
-  constexpr int WAVES = BLK / 32;
-  constexpr int NT = WAVES * 64;
+template <typename T, int D, int BLK>
+struct AttnCfg {
+  static constexpr int WAVES = BLK / 32;
+  static constexpr int NT = WAVES * 64;
   using St = Stage<T, D, NT>;
-  constexpr int SUBS = BLK / kStageKeys;
-  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
+  static constexpr int SUBS = BLK / kStageKeys;
+  static constexpr int LDS_BYTES = 2 * St::BYTES;
+};
 
+// One (query head h, tile t of sequence seq): the whole workgroup, B rows.
+template <typename T, int D, int BLK, bool SPARSE>
+__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* smem) {
+  using C = AttnCfg<T, D, BLK>;
+  using St = typename C::St;
+  constexpr int SUBS = C::SUBS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
-
-  const int bid = blockIdx.x;
-  const int gk = bid % p.hkv;
-  const int rest = bid / p.hkv;
-  const int hg = rest % p.group;
-  const int rank = rest / p.group;
-  int seq, t;
-  rank_to_item(p.seqs, 1, rank, seq, t);
-  if (seq < 0) return;
-  const int h = gk * p.group + hg;
+  const int gk = h / p.group;
   const int n_q = p.seqs.n_q[seq], n_k = p.seqs.n_k[seq];
   const int diag = p.seqs.diag0[seq] + t;
   const int row0 = t * BLK;
@@ -55,6 +52,7 @@ void attn_fwd_kernel(AttnParams p) {
   const int64_t qrow = (int64_t)p.seqs.q_start[seq] + row0 + wrow;
   QFrag<T, D> qf;
   qf.load(reinterpret_cast<const T*>(p.q) + (qrow * p.hq + h) * D, row_ok, g2);
+  wait_vmem_all();
 
   const int64_t row_stride = (int64_t)p.hkv * D;
   const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
@@ -168,10 +166,104 @@ void attn_fwd_kernel(AttnParams p) {
   }
 }
 
+// Static schedule: one workgroup per (head, tile), ranked by the tile's diagonal block
+// (longest first) with the KV head as the fastest-varying index (see the file header).
+template <typename T, int D, int BLK, bool SPARSE>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
+void attn_fwd_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[AttnCfg<T, D, BLK>::LDS_BYTES];
+  const int bid = blockIdx.x;
+  const int gk = bid % p.hkv;
+  const int rest = bid / p.hkv;
+  const int hg = rest % p.group;
+  const int rank = rest / p.group;
+  int seq, t;
+  rank_to_item(p.seqs, 1, rank, seq, t);
+  if (seq < 0) return;
+  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, smem);
+}
+
+// Persistent schedule for sparse rows, whose lengths vary from a few blocks to
+// thousands: one workgroup per resident slot pulls CSR rows from a queue that the
+// schedule kernel ordered by retained count, longest first. Rows are independent,
+// so the results do not depend on which workgroup takes which row.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
+void attn_sparse_persistent_kernel(AttnParams p) {
+  __shared__ __attribute__((aligned(16))) char smem[AttnCfg<T, D, BLK>::LDS_BYTES];
+  __shared__ int item_sh;
+  const int n_tiles = p.seqs.total_tiles;
+  for (;;) {
+    if (threadIdx.x == 0) item_sh = atomicAdd(p.queue, 1);
+    __syncthreads();
+    const int item = item_sh;
+    __syncthreads();
+    if (item >= p.num_rows) break;
+    const int r = p.order[item];
+    const int h = r / n_tiles, gtile = r % n_tiles;
+    const int seq = find_seq(p.seqs, gtile);
+    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], smem);
+  }
+}
+
+// Orders the CSR rows by retained count, descending (a counting sort in LDS), and
+// resets the queue head. One workgroup.
+constexpr int kSchedThreads = 1024;
+constexpr int kSchedBins = 4097;  // counts are clamped to 4096 for ordering only
+__global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const int32_t* __restrict__ row_ptr,
+                                                                       int rows, int32_t* __restrict__ order,
+                                                                       int32_t* __restrict__ queue) {
+  __shared__ int hist[kSchedBins];
+  __shared__ int sh[16];
+  const int tid = threadIdx.x;
+  for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
+  __syncthreads();
+  auto bin = [&](int r) {
+    const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), kSchedBins - 1);
+    return kSchedBins - 1 - c;  // longest first
+  };
+  for (int r = tid; r < rows; r += kSchedThreads) atomicAdd(&hist[bin(r)], 1);
+  __syncthreads();
+  constexpr int PER = (kSchedBins + kSchedThreads - 1) / kSchedThreads;
+  int local = 0;
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid * PER + e;
+    if (i < kSchedBins) local += hist[i];
+  }
+  int total;
+  int off = block_excl_scan_int(local, total, sh);
+  __syncthreads();
+  for (int e = 0; e < PER; ++e) {
+    const int i = tid * PER + e;
+    if (i < kSchedBins) {
+      const int c = hist[i];
+      hist[i] = off;
+      off += c;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < rows; r += kSchedThreads) order[atomicAdd(&hist[bin(r)], 1)] = r;
+  if (tid == 0) *queue = 0;
+}
+
 template <typename T, int D, int BLK, bool SPARSE>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.seqs.total_tiles * p.hq;
   if (grid == 0) return hipSuccess;
+  if (SPARSE && p.queue != nullptr) {
+    hipLaunchKernelGGL(sparse_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, p.row_ptr, p.num_rows,
+                       p.order, p.queue);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_sparse_persistent_kernel<T, D, BLK>, BLK * 2, 0);
+    if (e != hipSuccess) return e;
+    const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    hipLaunchKernelGGL((attn_sparse_persistent_kernel<T, D, BLK>), dim3((unsigned)(slots < grid ? slots : grid)),
+                       dim3(BLK * 2), 0, stream, p);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, SPARSE>), dim3((unsigned)grid), dim3(BLK * 2), 0, stream, p);
   return hipGetLastError();
 }

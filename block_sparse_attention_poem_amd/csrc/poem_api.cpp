@@ -250,12 +250,22 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                     "poem_select launch");
 }
 
+static size_t sparse_ws_bytes(const poem_problem* p, const Geometry& g) {
+  return 256 + align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.num_tiles);
+}
+
 static poem_status attention(const poem_problem* problem, const void* q, const void* k, const void* v,
                              const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
-                             float* lse, void* stream, bool sparse) {
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream, bool sparse) {
   Geometry g;
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
+  if (workspace != nullptr) {
+    if (workspace_bytes < sparse_ws_bytes(problem, g))
+      return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
+                  sparse_ws_bytes(problem, g));
+    if (((uintptr_t)workspace & 255) != 0) return fail(POEM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
+  }
   if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
   if (out == nullptr) return fail(POEM_ERR_INVALID_ARG, "out is NULL");
   if (sparse && (row_ptr == nullptr || block_idx == nullptr))
@@ -277,21 +287,35 @@ static poem_status attention(const poem_problem* problem, const void* q, const v
   ap.out_f32 = out_dtype == POEM_FP32 ? 1 : 0;
   ap.total_q = (int32_t)g.total_q;
   ap.scale_log2 = g.scale * poem::kLog2e;
+  ap.num_rows = (int32_t)(problem->num_heads_q * g.num_tiles);
+  if (sparse && workspace != nullptr) {
+    ap.queue = static_cast<int32_t*>(workspace);
+    ap.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
+  }
   ap.seqs = g.st;
   return hip_status(poem::launch_attention(ap, problem->in_dtype, problem->head_dim, problem->block_size, sparse,
                                            static_cast<hipStream_t>(stream)),
                     sparse ? "poem_sparse_prefill launch" : "poem_dense_prefill launch");
 }
 
+int64_t poem_sparse_workspace_bytes(const poem_problem* problem) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  ok();
+  return (int64_t)sparse_ws_bytes(problem, g);
+}
+
 poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, const void* k, const void* v,
                                 const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
-                                float* lse, void* stream) {
-  return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, stream, true);
+                                float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, workspace, workspace_bytes, stream,
+                   true);
 }
 
 poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k, const void* v, void* out,
                                int32_t out_dtype, float* lse, void* stream) {
-  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, stream, false);
+  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, nullptr, 0, stream, false);
 }
 
 const char* poem_last_error(void) { return g_error.c_str(); }

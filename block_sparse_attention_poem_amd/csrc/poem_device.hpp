@@ -88,6 +88,35 @@ __host__ __device__ __forceinline__ void rank_to_item(const SeqTable& st, int TG
   }
 }
 
+// Sequence holding global tile gtile.
+__host__ __device__ __forceinline__ int find_seq(const SeqTable& st, int gtile) {
+  int s = 0;
+  while (s + 1 < st.num_seqs && st.tile_start[s + 1] <= gtile) ++s;
+  return s;
+}
+
+// Exclusive prefix sum over the workgroup in thread order; total receives the sum.
+// sh holds one int per wave.
+__device__ __forceinline__ int block_excl_scan_int(int a, int& total, int* sh) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int ia = a;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int ta = __shfl_up(ia, o);
+    if (lane >= o) ia += ta;
+  }
+  if (lane == 63) sh[wave] = ia;
+  __syncthreads();
+  int off = 0;
+  total = 0;
+  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
+    if (w < wave) off += sh[w];
+    total += sh[w];
+  }
+  __syncthreads();
+  return off + ia - a;
+}
+
 // Key position inside a 16-key group of the transposed-V LDS rows: bits 2 and 3 of
 // the key swapped. It places the keys a lane group holds in one PV k-step next to
 // each other, so each PV operand is one contiguous LDS read.
@@ -142,7 +171,7 @@ struct Stage {
 #pragma unroll
       for (int j = 0; j < 4; ++j) r.v[i][j] = u32x4{0, 0, 0, 0};
       if (u < V_UNITS) {
-        int kq = u / CH_PER_ROW, ch = u % CH_PER_ROW;
+        const int kq = u % (kStageKeys / 4), ch = u / (kStageKeys / 4);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           int key = key0 + 4 * kq + j;
@@ -168,8 +197,10 @@ struct Stage {
     for (int i = 0; i < V_ITERS; ++i) {
       int u = tid + i * NT;
       if (u < V_UNITS) {
-        int kq = u / CH_PER_ROW, ch = u % CH_PER_ROW;
-        int pos = vt_pos(4 * kq);  // keys 4kq .. 4kq+3 stay contiguous
+        // consecutive lanes take consecutive key quads of one d-chunk, so the 16 lanes
+        // that write one V^T row together cover its 128 bytes without bank conflicts
+        const int kq = u % (kStageKeys / 4), ch = u / (kStageKeys / 4);
+        const int pos = vt_pos(4 * kq);  // keys 4kq .. 4kq+3 stay contiguous
         if constexpr (EB == 2) {
           // 4 keys x 8 d (bf16) -> 8 rows of V^T, 4 keys (8 bytes) each
 #pragma unroll
@@ -317,5 +348,10 @@ __device__ __forceinline__ void pv_stage(const char* vt, const f32x16 (&p)[2], f
 }
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued once after the
+// per-column loads that precede a sweep: otherwise those loads stay "pending" at the
+// loop header on some path and every iteration waits for its own K/V prefetch too.
+__device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 }  // namespace poem

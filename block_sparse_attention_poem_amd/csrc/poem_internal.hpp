@@ -22,6 +22,10 @@ struct AttnParams {
   int32_t out_f32;
   int32_t total_q;
   float scale_log2;          // softmax scale * log2(e)
+  // sparse persistent schedule (queue == nullptr: one workgroup per row)
+  int32_t* queue;            // queue head, reset by the schedule kernel
+  int32_t* order;            // [num_rows] rows by retained count, descending
+  int32_t num_rows;          // hq * total_tiles
   SeqTable seqs;
 };
 

@@ -117,6 +117,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
     }
   }
 
+  wait_vmem_all();
   const int total = nblk_wg * SUBS;
   typename St::Regs regs;
   St::load(regs, kbase, vbase, row_stride, 0, n_k, tid);
@@ -231,11 +232,6 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
 constexpr int kThrThreads = 256;
 constexpr int kMaxVis = 4096;
 
-__device__ __forceinline__ int find_seq(const SeqTable& st, int gtile) {
-  int s = 0;
-  while (s + 1 < st.num_seqs && st.tile_start[s + 1] <= gtile) ++s;
-  return s;
-}
 
 // Exclusive prefix over the workgroup of (a, b) in thread order.
 __device__ __forceinline__ void block_excl_scan2(double a, double b, double& ea, double& eb, double* sh) {
@@ -257,25 +253,6 @@ __device__ __forceinline__ void block_excl_scan2(double a, double b, double& ea,
   eb = ob + xb;
 }
 
-__device__ __forceinline__ int block_excl_scan_int(int a, int& total, int* sh) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int ia = a;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    int ta = __shfl_up(ia, o);
-    if (lane >= o) ia += ta;
-  }
-  if (lane == 63) sh[wave] = ia;
-  __syncthreads();
-  int off = 0;
-  total = 0;
-  for (int w = 0; w < (int)(blockDim.x >> 6); ++w) {
-    if (w < wave) off += sh[w];
-    total += sh[w];
-  }
-  __syncthreads();
-  return off + ia - a;
-}
 
 __device__ __forceinline__ int block_min_int(int v, int* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;

@@ -134,6 +134,10 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
                         float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
 
+/* Bytes of the optional device workspace poem_sparse_prefill uses to schedule its rows
+ * (a queue head and one int32 per CSR row); < 0 on error. */
+int64_t poem_sparse_workspace_bytes(const poem_problem* problem);
+
 /*
  * poem_sparse_prefill: causal softmax attention of each query tile over the key
  * blocks its CSR row lists, i.e. the masked softmax over {j <= position : block(j)
@@ -146,10 +150,17 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
  *                    no usable id yields O = 0 and LSE = -inf.
  *   out              device [sum N_q][H_q][d] in out_dtype (POEM_BF16 or POEM_FP32).
  *   lse              nullable device fp32 [H_q][sum N_q]: natural-log sum of exp of the scores.
+ *   workspace        nullable device buffer of >= poem_sparse_workspace_bytes(problem) bytes,
+ *                    256-byte aligned, contents ignored on entry. With it, a schedule kernel
+ *                    orders the rows by retained count (longest first) and a persistent
+ *                    kernel pulls them from a queue; without it, one workgroup per row is
+ *                    launched in diagonal order. Results are identical either way. Calls that
+ *                    share a workspace must not overlap.
  */
 poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, const void* k,
                                 const void* v, const int32_t* row_ptr, const int32_t* block_idx,
-                                void* out, int32_t out_dtype, float* lse, void* stream);
+                                void* out, int32_t out_dtype, float* lse, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /*
  * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t

@@ -148,7 +148,9 @@ def test_sparse_given_mask_matches_oracle(case):
     bid = torch.from_numpy(np.concatenate([bi, np.zeros(1, np.int32)])).cuda()
     say("sparse given mask", case)
     out, lse = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32")
+    out2, lse2 = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32", workspace=None)
     _sync()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
     out = out.cpu().numpy()
     lse = lse.cpu().numpy()
     q, k, v = H.f64(inp)
@@ -177,12 +179,13 @@ def test_sparse_full_list_is_bitwise_dense(case):
     say("bitwise", case)
     for od in ("fp32", "bf16"):
         d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype=od)
-        s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, torch.from_numpy(rp).cuda(), torch.from_numpy(bi).cuda(),
-                                        out_dtype=od)
-        _sync()
-        assert torch.equal(d_out.view(torch.int16) if od == "bf16" else d_out.view(torch.int32),
-                           s_out.view(torch.int16) if od == "bf16" else s_out.view(torch.int32))
-        assert torch.equal(d_lse, s_lse)
+        bits = (lambda x: x.view(torch.int16)) if od == "bf16" else (lambda x: x.view(torch.int32))
+        for ws in ("auto", None):  # persistent queue and one-workgroup-per-row schedules
+            s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, torch.from_numpy(rp).cuda(),
+                                            torch.from_numpy(bi).cuda(), out_dtype=od, workspace=ws)
+            _sync()
+            assert torch.equal(bits(d_out), bits(s_out)), ws
+            assert torch.equal(d_lse, s_lse), ws
 
 
 def test_empty_and_out_of_range_rows():

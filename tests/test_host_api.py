@@ -147,9 +147,16 @@ def test_attention_validation(lib):
     assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 5, None, None) == \
         L.POEM_ERR_INVALID_ARG
     assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, FAKE, FAKE, L.POEM_FP32, None,
-                                   None) == L.POEM_ERR_INVALID_ARG
+                                   None, 0, None) == L.POEM_ERR_INVALID_ARG
     assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, None, FAKE, L.POEM_FP32, None,
-                                   None) == L.POEM_ERR_INVALID_ARG
+                                   None, 0, None) == L.POEM_ERR_INVALID_ARG
+    need = L.sparse_workspace_bytes(prob())
+    assert need == 256 + ((4 * 4 * 5 + 255) // 256) * 256
+    ws = ctypes.c_void_p(0x300000)
+    assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None,
+                                   ws, need - 1, None) == L.POEM_ERR_WORKSPACE
+    assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None,
+                                   ctypes.c_void_p(0x300004), need, None) == L.POEM_ERR_WORKSPACE
 
 
 def test_error_is_thread_local(lib):
