@@ -3,7 +3,7 @@
 // One workgroup computes one (query head, query tile): B rows, 32 per wave, over
 // the key blocks the tile retains (sparse: its CSR row; dense: 0 .. diagonal), the
 // retained-block attention of the POEM note (Section 4.1). K/V of each 64-key
-// stage are staged in LDS once and shared by the tile's waves; the loop visits
+// stage are loaded into LDS once and shared by the tile's waves; the loop visits
 // only listed blocks, as BFLA's support-restricted kernel does (Section 3.4).
 // Online softmax runs in the log2 domain in fp32; QK^T and PV run on bf16 (or
 // fp32) MFMAs with fp32 accumulation. Only the diagonal block is masked.
@@ -27,12 +27,12 @@ struct AttnCfg {
   static constexpr int NT = WAVES * 64;
   using St = Stage<T, D, NT>;
   static constexpr int SUBS = BLK / kStageKeys;
-  static constexpr int LDS_BYTES = 2 * St::BYTES;
+  static constexpr int STAGE_BYTES = St::BYTES;
 };
 
 // One (query head h, tile t of sequence seq): the whole workgroup, B rows.
 template <typename T, int D, int BLK, bool SPARSE>
-__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* smem) {
+__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* buf0, char* buf1) {
   using C = AttnCfg<T, D, BLK>;
   using St = typename C::St;
   constexpr int SUBS = C::SUBS;
@@ -89,60 +89,49 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
-  typename St::Regs regs;
-  if (total > 0) {
-    St::load(regs, kbase, vbase, row_stride, stage_key0(0), n_k, tid);
-    St::store(regs, smem, tid);
-  }
-  __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    char* cur = smem + (it & 1) * St::BYTES;
-    if (it + 1 < total) St::load(regs, kbase, vbase, row_stride, stage_key0(it + 1), n_k, tid);
+  sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
     const int key0 = stage_key0(it);
-    if (key0 <= wave_pos_max) {
-      f32x16 S[2];
-      S[0] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 0, lane);
-      S[1] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 1, lane);
-      float mx = -INFINITY;
-      if (key0 + kStageKeys - 1 > wave_pos_min) {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            float s = (key0 + acc_key(kt, r, g2) > my_pos) ? -INFINITY : S[kt][r];
-            S[kt][r] = s;
-            mx = fmaxf(mx, s);
-          }
-      } else {
-#pragma unroll
-        for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-      }
-      mx = fmaxf(mx, wave_xor32(mx));
-      const float m_new = fmaxf(m_run, mx * c);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-      float rs = 0.f;
+    if (key0 > wave_pos_max) return;  // every key of the stage is above this wave's rows
+    f32x16 S[2];
+    S[0] = St::qk_tile(cur, qf, 0, lane);
+    S[1] = St::qk_tile(cur, qf, 1, lane);
+    float mx = -INFINITY;
+    if (key0 + kStageKeys - 1 > wave_pos_min) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
-          S[kt][r] = e;
-          rs += e;
+          float s = (key0 + acc_key(kt, r, g2) > my_pos) ? -INFINITY : S[kt][r];
+          S[kt][r] = s;
+          mx = fmaxf(mx, s);
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {
+    } else {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
-      }
-      pv_stage<T, D, St::V_STRIDE, false>(cur + St::K_BYTES, S, O, lane);
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     }
-    if (it + 1 < total) St::store(regs, smem + ((it + 1) & 1) * St::BYTES, tid);
-    __syncthreads();
-  }
+    mx = fmaxf(mx, wave_xor32(mx));
+    const float m_new = fmaxf(m_run, mx * c);
+    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
+        S[kt][r] = e;
+        rs += e;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
+    }
+    St::template pv<false>(cur, S, O, lane);
+  });
 
   const float l_tot = l_run + wave_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -171,7 +160,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 template <typename T, int D, int BLK, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[AttnCfg<T, D, BLK>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char buf0[AttnCfg<T, D, BLK>::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[AttnCfg<T, D, BLK>::STAGE_BYTES];
   const int bid = blockIdx.x;
   const int gk = bid % p.hkv;
   const int rest = bid / p.hkv;
@@ -180,7 +170,7 @@ void attn_fwd_kernel(AttnParams p) {
   int seq, t;
   rank_to_item(p.seqs, 1, rank, seq, t);
   if (seq < 0) return;
-  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, smem);
+  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, buf0, buf1);
 }
 
 // Persistent schedule for sparse rows, whose lengths vary from a few blocks to
@@ -190,7 +180,8 @@ void attn_fwd_kernel(AttnParams p) {
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_sparse_persistent_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char smem[AttnCfg<T, D, BLK>::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char buf0[AttnCfg<T, D, BLK>::STAGE_BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[AttnCfg<T, D, BLK>::STAGE_BYTES];
   __shared__ int item_sh;
   const int n_tiles = p.seqs.total_tiles;
   for (;;) {
@@ -202,7 +193,7 @@ void attn_sparse_persistent_kernel(AttnParams p) {
     const int r = p.order[item];
     const int h = r / n_tiles, gtile = r % n_tiles;
     const int seq = find_seq(p.seqs, gtile);
-    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], smem);
+    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], buf0, buf1);
   }
 }
 

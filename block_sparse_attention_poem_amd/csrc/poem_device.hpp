@@ -1,13 +1,17 @@
 // Device building blocks shared by the attention and selector sweeps (gfx950).
 //
-// A "sweep" walks key blocks of one sequence/KV head in 64-key stages. Each stage
-// is staged global -> registers -> LDS by the whole workgroup (K row-major, V
-// transposed so that PV operands are 16-byte LDS reads), double-buffered with one
-// barrier per stage. Every wave owns 32 query columns and runs 32x32 MFMAs:
+// A "sweep" walks key blocks of one sequence/KV head in 64-key stages, double-
+// buffered in LDS with one barrier per stage. Every wave owns 32 query columns and
+// runs 32x32 MFMAs:
 //   S^T[key][col]  = K[key][:] . Q[col][:]        (A = K from LDS, B = Q in registers)
 //   O^T[d][col]   += V^T[d][key] . P^T[key][col]   (A = V^T from LDS, B = P in registers)
 // Computing the transposes keeps every per-column quantity (max, sum, scale) in one
 // lane pair (l, l^32), and lets the fp32 scores become PV operands without shuffles.
+//
+// bf16 stages are filled by direct global->LDS loads (no registers, no LDS stores)
+// into unpadded row-major K and V whose 16-byte chunks are XOR-swizzled per row; the
+// PV operand V^T is read with the transposing LDS load. fp32 stages go through
+// registers and store V transposed.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -117,42 +121,203 @@ __device__ __forceinline__ int block_excl_scan_int(int a, int& total, int* sh) {
   return off + ia - a;
 }
 
-// Key position inside a 16-key group of the transposed-V LDS rows: bits 2 and 3 of
-// the key swapped. It places the keys a lane group holds in one PV k-step next to
-// each other, so each PV operand is one contiguous LDS read.
-__device__ __forceinline__ int vt_pos(int key) {
-  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
-}
 
 template <typename T> struct ElemTraits;
 template <> struct ElemTraits<uint16_t> { static constexpr int bytes = 2; };
 template <> struct ElemTraits<float> { static constexpr int bytes = 4; };
 
-// LDS stage geometry for element type T and head dim D with NT threads.
-template <typename T, int D, int NT>
-struct Stage {
-  static constexpr int EB = ElemTraits<T>::bytes;
-  static constexpr int K_STRIDE = D * EB + 16;              // bytes per K row (16-byte pad)
-  static constexpr int V_STRIDE = kStageKeys * EB + 16;     // bytes per V^T row
+typedef __attribute__((address_space(3))) char lds_char;
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Q fragments (B operand of S^T = K Q^T) for 32 columns. Lane l: column j = l % 32,
+// lane group g = l / 32. bf16: 16-d steps, lane group g holds d = 16s + 8g .. +7.
+// fp32: 2-d steps, lane group g holds d = (D/2) g + s.
+// 32x32 accumulator register r holds row 8*(r/4) + 4*g + r%4 of column j.
+// ---------------------------------------------------------------------------
+template <typename T, int D> struct QFrag;
+template <int D> struct QFrag<uint16_t, D> {
+  static constexpr int STEPS = D / 16;
+  bf16x8 q[STEPS];
+  __device__ __forceinline__ void load(const uint16_t* row, bool valid, int g) {
+#pragma unroll
+    for (int s = 0; s < STEPS; ++s) {
+      u32x4 w = {0, 0, 0, 0};
+      if (valid) w = *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * g);
+      q[s] = __builtin_bit_cast(bf16x8, w);
+    }
+  }
+};
+template <int D> struct QFrag<float, D> {
+  static constexpr int STEPS = D / 2;
+  float q[STEPS];
+  __device__ __forceinline__ void load(const float* row, bool valid, int g) {
+#pragma unroll
+    for (int s4 = 0; s4 < STEPS / 4; ++s4) {
+      f32x4 w = {0.f, 0.f, 0.f, 0.f};
+      if (valid) w = *reinterpret_cast<const f32x4*>(row + (D / 2) * g + 4 * s4);
+      q[4 * s4 + 0] = w[0]; q[4 * s4 + 1] = w[1]; q[4 * s4 + 2] = w[2]; q[4 * s4 + 3] = w[3];
+    }
+  }
+};
+
+// Key (0..63 inside the stage) of accumulator register r of key tile kt for lane group g.
+__device__ __forceinline__ int acc_key(int kt, int r, int g) {
+  return 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
+}
+
+// bf16 pack of two floats, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
+
+// P operand of one 16-key PV step s (bf16): registers 8(s&1) .. +7 of key tile s/2.
+// Lane group g then holds keys 16s + 4g + 0..3 (elements 0..3) and 16s + 8 + 4g + 0..3
+// (elements 4..7). With SPLIT the bf16 rounding residual is packed into lo.
+template <bool SPLIT>
+__device__ __forceinline__ void p_step(const f32x16 (&p)[2], int s, bf16x8& hi, bf16x8& lo) {
+  const int kt = s >> 1, r0 = 8 * (s & 1);
+  u32x4 w, wl;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float a = p[kt][r0 + 2 * e], b = p[kt][r0 + 2 * e + 1];
+    w[e] = pack_bf16(a, b);
+    if constexpr (SPLIT) wl[e] = pack_bf16(a - bf16_lo_to_f32(w[e]), b - bf16_hi_to_f32(w[e]));
+  }
+  hi = __builtin_bit_cast(bf16x8, w);
+  if constexpr (SPLIT) lo = __builtin_bit_cast(bf16x8, wl);
+}
+
+// ---------------------------------------------------------------------------
+// bf16 stage: 64 keys of K then 64 keys of V, each row-major [key][D] (no padding).
+// Chunk c (16 bytes) of row r sits at chunk position c ^ swizzle(r): the K swizzle
+// spreads the 16 rows that 16 lanes read together for QK over all banks; the V
+// swizzle does the same for the 4 rows x 4 chunks one transposing read touches per
+// 32 lanes. Rows past the sequence end re-read its last key (their scores are masked).
+// ---------------------------------------------------------------------------
+template <int D, int NT>
+struct StageB16 {
+  static constexpr int ROW = D * 2;
+  static constexpr int CH = D / 8;  // 16-byte chunks per row
+  static constexpr int TENSOR = kStageKeys * ROW;
+  static constexpr int BYTES = 2 * TENSOR;
+  static constexpr int WAVES = NT / 64;
+  static constexpr int INSTR = TENSOR / 1024;  // 1 KB per wave-wide direct load
+  static_assert(INSTR % WAVES == 0, "stage must split evenly over the waves");
+  struct Regs {};
+
+  static __device__ __forceinline__ int kswz(int r) { return r & (CH - 1); }
+  static __device__ __forceinline__ int vswz(int r) {
+    return CH >= 16 ? (2 * (r & 3) + 8 * (r & 1)) : (2 * (r & 3));
+  }
+
+  static __device__ __forceinline__ void load(Regs&, const uint16_t* __restrict__ kbase,
+                                              const uint16_t* __restrict__ vbase, int64_t row_stride, int key0,
+                                              int n_valid, int tid, char* lds) {
+    const int wave = tid >> 6, lane = tid & 63;
+    const char* kb = reinterpret_cast<const char*>(kbase);
+    const char* vb = reinterpret_cast<const char*>(vbase);
+#pragma unroll
+    for (int j = 0; j < INSTR / WAVES; ++j) {
+      const int blk = j * WAVES + wave;
+      const int off = blk * 1024 + lane * 16;
+      const int r = off / ROW, pos = (off % ROW) / 16;
+      const int key = min(key0 + r, n_valid - 1);
+      const int64_t g = (int64_t)key * row_stride * 2;
+      __builtin_amdgcn_global_load_lds(kb + g + (pos ^ kswz(r)) * 16, (lds_char*)(lds + blk * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(vb + g + (pos ^ vswz(r)) * 16, (lds_char*)(lds + TENSOR + blk * 1024), 16,
+                                       0, 0);
+    }
+  }
+  static __device__ __forceinline__ void store(const Regs&, char*, int) {}
+  // the direct loads write LDS asynchronously: wait for this wave's before the barrier
+  static constexpr bool ASYNC = true;
+
+  // S^T for 32-key tile kt: acc = K[32kt + i][:] . Q[:][j]
+  static __device__ __forceinline__ f32x16 qk_tile(const char* lds, const QFrag<uint16_t, D>& qf, int kt, int lane) {
+    f32x16 acc = {};
+    const int r = 32 * kt + (lane & 31), g = lane >> 5;
+    const char* rowp = lds + r * ROW;
+#pragma unroll
+    for (int s = 0; s < D / 16; ++s) {
+      const bf16x8 a =
+          __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + ((2 * s + g) ^ kswz(r)) * 16));
+      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[s], acc, 0, 0, 0);
+    }
+    return acc;
+  }
+
+  // V^T operand of d-tile dt, key step s: lane l gets d = 32dt + l%32 and the keys its
+  // lane group's P elements hold (16s + 4g + 0..3, then 16s + 8 + 4g + 0..3). In each
+  // group of 16 lanes the transposing read hands lane i element (i & 3) of the 8 bytes
+  // addressed by lane 4e + (i >> 2), as its element e; so lane 4e + k addresses key
+  // base + e, d = 16-column base + 4k.
+  static __device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int s, int lane) {
+    const int q = lane >> 4, i = lane & 15, g = q >> 1;
+    const int d = 32 * dt + 16 * (q & 1) + 4 * (i & 3);
+    const int c = d >> 3, half = (d >> 2) & 1;
+    const int r0 = 16 * s + 4 * g + (i >> 2), r1 = r0 + 8;
+    const char* vt = lds + TENSOR;
+    const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16 __attribute__((address_space(3)))*)(vt + r0 * ROW + (c ^ vswz(r0)) * 16 + half * 8));
+    const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (v4i16 __attribute__((address_space(3)))*)(vt + r1 * ROW + (c ^ vswz(r1)) * 16 + half * 8));
+    typedef short v8i16 __attribute__((ext_vector_type(8)));
+    const v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    return __builtin_bit_cast(bf16x8, ab);
+  }
+
+  // O^T[dt] += V^T . P^T over the stage's 64 keys, one 16-key step at a time.
+  template <bool SPLIT>
+  static __device__ __forceinline__ void pv(const char* lds, const f32x16 (&p)[2], f32x16* O, int lane) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      bf16x8 ph, pl;
+      p_step<SPLIT>(p, s, ph, pl);
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) {
+        const bf16x8 a = v_frag(lds, dt, s, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ph, O[dt], 0, 0, 0);
+        if constexpr (SPLIT) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl, O[dt], 0, 0, 0);
+      }
+    }
+  }
+};
+
+// ---------------------------------------------------------------------------
+// fp32 stage: registers -> LDS. K row-major with a 16-byte pad per row; V stored
+// transposed, V^T[d][vt_pos(key)], where vt_pos swaps bits 2 and 3 of the key so
+// the keys a lane group holds in one PV step sit together.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ int vt_pos(int key) {
+  return (key & ~12) | ((key & 4) << 1) | ((key & 8) >> 1);
+}
+
+template <int D, int NT>
+struct StageF32 {
+  static constexpr int EB = 4;
+  static constexpr int K_STRIDE = D * EB + 16;
+  static constexpr int V_STRIDE = kStageKeys * EB + 16;
   static constexpr int K_BYTES = kStageKeys * K_STRIDE;
   static constexpr int V_BYTES = D * V_STRIDE;
   static constexpr int BYTES = K_BYTES + V_BYTES;
-  static constexpr int CH_PER_ROW = D * EB / 16;            // 16-byte chunks per key row
+  static constexpr int CH_PER_ROW = D * EB / 16;
   static constexpr int K_CHUNKS = kStageKeys * CH_PER_ROW;
   static constexpr int K_ITERS = (K_CHUNKS + NT - 1) / NT;
   static constexpr int V_UNITS = (kStageKeys / 4) * CH_PER_ROW;  // 4 keys x 16 bytes
   static constexpr int V_ITERS = (V_UNITS + NT - 1) / NT;
+  static constexpr bool ASYNC = false;
 
   struct Regs {
     u32x4 k[K_ITERS];
     u32x4 v[V_ITERS][4];
   };
 
-  // Global -> registers for keys [key0, key0 + 64) of one KV head (K and V bases point
-  // at key 0 of the sequence for that head). Keys at or past n_valid read as zero.
-  // row_stride is the element stride between consecutive keys.
-  static __device__ __forceinline__ void load(Regs& r, const T* __restrict__ kbase, const T* __restrict__ vbase,
-                                              int64_t row_stride, int key0, int n_valid, int tid) {
+  static __device__ __forceinline__ void load(Regs& r, const float* __restrict__ kbase, const float* __restrict__ vbase,
+                                              int64_t row_stride, int key0, int n_valid, int tid, char*) {
     const char* b = reinterpret_cast<const char*>(kbase);
     const char* bv = reinterpret_cast<const char*>(vbase);
 #pragma unroll
@@ -182,7 +347,8 @@ struct Stage {
     }
   }
 
-  // Registers -> LDS stage. K rows as they are; V transposed to V^T[d][vt_pos(key)].
+  // consecutive lanes take consecutive key quads of one d-chunk, so the 16 lanes
+  // that write one V^T row together cover it without bank conflicts
   static __device__ __forceinline__ void store(const Regs& r, char* lds, int tid) {
 #pragma unroll
     for (int i = 0; i < K_ITERS; ++i) {
@@ -197,81 +363,21 @@ struct Stage {
     for (int i = 0; i < V_ITERS; ++i) {
       int u = tid + i * NT;
       if (u < V_UNITS) {
-        // consecutive lanes take consecutive key quads of one d-chunk, so the 16 lanes
-        // that write one V^T row together cover its 128 bytes without bank conflicts
         const int kq = u % (kStageKeys / 4), ch = u / (kStageKeys / 4);
-        const int pos = vt_pos(4 * kq);  // keys 4kq .. 4kq+3 stay contiguous
-        if constexpr (EB == 2) {
-          // 4 keys x 8 d (bf16) -> 8 rows of V^T, 4 keys (8 bytes) each
+        const int pos = vt_pos(4 * kq);
 #pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            uint32_t a0 = r.v[i][0][c], a1 = r.v[i][1][c], a2 = r.v[i][2][c], a3 = r.v[i][3][c];
-            u32x2 lo = {(a0 & 0xffffu) | (a1 << 16), (a2 & 0xffffu) | (a3 << 16)};
-            u32x2 hi = {(a0 >> 16) | (a1 & 0xffff0000u), (a2 >> 16) | (a3 & 0xffff0000u)};
-            int d = ch * 8 + 2 * c;
-            *reinterpret_cast<u32x2*>(vt + d * V_STRIDE + pos * 2) = lo;
-            *reinterpret_cast<u32x2*>(vt + (d + 1) * V_STRIDE + pos * 2) = hi;
-          }
-        } else {
-          // 4 keys x 4 d (fp32) -> 4 rows of V^T, 4 keys (16 bytes) each
-#pragma unroll
-          for (int c = 0; c < 4; ++c) {
-            u32x4 w = {r.v[i][0][c], r.v[i][1][c], r.v[i][2][c], r.v[i][3][c]};
-            int d = ch * 4 + c;
-            *reinterpret_cast<u32x4*>(vt + d * V_STRIDE + pos * 4) = w;
-          }
+        for (int c = 0; c < 4; ++c) {
+          u32x4 w = {r.v[i][0][c], r.v[i][1][c], r.v[i][2][c], r.v[i][3][c]};
+          *reinterpret_cast<u32x4*>(vt + (ch * 4 + c) * V_STRIDE + pos * 4) = w;
         }
       }
     }
   }
-};
 
-// ---------------------------------------------------------------------------
-// MFMA fragments. Lane l: column j = l % 32, lane group g = l / 32.
-// 32x32 accumulator register r holds row 8*(r/4) + 4*g + r%4 of column j.
-// ---------------------------------------------------------------------------
-
-// Q (B operand of S^T = K Q^T) for 32 columns. bf16: 16-d steps, lane group g
-// holds d = 16s + 8g .. +7. fp32: 2-d steps, lane group g holds d = (D/2) g + s.
-template <typename T, int D> struct QFrag;
-template <int D> struct QFrag<uint16_t, D> {
-  static constexpr int STEPS = D / 16;
-  bf16x8 q[STEPS];
-  __device__ __forceinline__ void load(const uint16_t* row, bool valid, int g) {
-#pragma unroll
-    for (int s = 0; s < STEPS; ++s) {
-      u32x4 w = {0, 0, 0, 0};
-      if (valid) w = *reinterpret_cast<const u32x4*>(row + 16 * s + 8 * g);
-      q[s] = __builtin_bit_cast(bf16x8, w);
-    }
-  }
-};
-template <int D> struct QFrag<float, D> {
-  static constexpr int STEPS = D / 2;
-  float q[STEPS];
-  __device__ __forceinline__ void load(const float* row, bool valid, int g) {
-#pragma unroll
-    for (int s4 = 0; s4 < STEPS / 4; ++s4) {
-      f32x4 w = {0.f, 0.f, 0.f, 0.f};
-      if (valid) w = *reinterpret_cast<const f32x4*>(row + (D / 2) * g + 4 * s4);
-      q[4 * s4 + 0] = w[0]; q[4 * s4 + 1] = w[1]; q[4 * s4 + 2] = w[2]; q[4 * s4 + 3] = w[3];
-    }
-  }
-};
-
-// S^T for one 32-key tile kt of the LDS stage: acc = K[32kt + i][:] . Q[:][j].
-template <typename T, int D, int K_STRIDE>
-__device__ __forceinline__ f32x16 qk_tile(const char* klds, const QFrag<T, D>& qf, int kt, int lane) {
-  f32x16 acc = {};
-  const int i = lane & 31, g = lane >> 5;
-  const char* rowp = klds + (32 * kt + i) * K_STRIDE;
-  if constexpr (sizeof(T) == 2) {
-#pragma unroll
-    for (int s = 0; s < QFrag<T, D>::STEPS; ++s) {
-      bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + (16 * s + 8 * g) * 2));
-      acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf.q[s], acc, 0, 0, 0);
-    }
-  } else {
+  static __device__ __forceinline__ f32x16 qk_tile(const char* lds, const QFrag<float, D>& qf, int kt, int lane) {
+    f32x16 acc = {};
+    const int i = lane & 31, g = lane >> 5;
+    const char* rowp = lds + (32 * kt + i) * K_STRIDE;
 #pragma unroll
     for (int s4 = 0; s4 < D / 8; ++s4) {
       f32x4 a = *reinterpret_cast<const f32x4*>(rowp + ((D / 2) * g + 4 * s4) * 4);
@@ -279,55 +385,13 @@ __device__ __forceinline__ f32x16 qk_tile(const char* klds, const QFrag<T, D>& q
       for (int e = 0; e < 4; ++e)
         acc = __builtin_amdgcn_mfma_f32_32x32x2f32(a[e], qf.q[4 * s4 + e], acc, 0, 0, 0);
     }
+    return acc;
   }
-  return acc;
-}
 
-// Key (0..63 inside the stage) of accumulator register r of key tile kt for lane group g.
-__device__ __forceinline__ int acc_key(int kt, int r, int g) {
-  return 32 * kt + 8 * (r >> 2) + 4 * g + (r & 3);
-}
-
-// bf16 pack of two floats, round to nearest even (v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-  f32x2 v = {a, b};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
-__device__ __forceinline__ float bf16_lo_to_f32(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
-__device__ __forceinline__ float bf16_hi_to_f32(uint32_t w) { return __builtin_bit_cast(float, w & 0xffff0000u); }
-
-// O^T[dt] += V^T[32dt + i][keys] . P^T[keys][j] over the 64 keys of the stage.
-// p holds the probabilities in the S^T accumulator layout (two key tiles).
-// SPLIT (bf16 only) adds a second MFMA with the bf16 rounding residual of P.
-template <typename T, int D, int V_STRIDE, bool SPLIT>
-__device__ __forceinline__ void pv_stage(const char* vt, const f32x16 (&p)[2], f32x16* O, int lane) {
-  const int i = lane & 31, g = lane >> 5;
-  if constexpr (sizeof(T) == 2) {
-    bf16x8 ph[4], pl[4];
-#pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const int kt = s >> 1, r0 = 8 * (s & 1);
-      u32x4 w, wl;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        float a = p[kt][r0 + 2 * e], b = p[kt][r0 + 2 * e + 1];
-        w[e] = pack_bf16(a, b);
-        if constexpr (SPLIT) wl[e] = pack_bf16(a - bf16_lo_to_f32(w[e]), b - bf16_hi_to_f32(w[e]));
-      }
-      ph[s] = __builtin_bit_cast(bf16x8, w);
-      if constexpr (SPLIT) pl[s] = __builtin_bit_cast(bf16x8, wl);
-    }
-#pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt) {
-      const char* rowp = vt + (32 * dt + i) * V_STRIDE;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        bf16x8 a = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(rowp + (16 * s + 8 * g) * 2));
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ph[s], O[dt], 0, 0, 0);
-        if constexpr (SPLIT) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl[s], O[dt], 0, 0, 0);
-      }
-    }
-  } else {
+  template <bool SPLIT>
+  static __device__ __forceinline__ void pv(const char* lds, const f32x16 (&p)[2], f32x16* O, int lane) {
+    const int i = lane & 31, g = lane >> 5;
+    const char* vt = lds + K_BYTES;
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt) {
       const char* rowp = vt + (32 * dt + i) * V_STRIDE;
@@ -345,7 +409,12 @@ __device__ __forceinline__ void pv_stage(const char* vt, const f32x16 (&p)[2], f
       }
     }
   }
-}
+};
+
+template <typename T, int D, int NT> struct StageSel;
+template <int D, int NT> struct StageSel<uint16_t, D, NT> { using type = StageB16<D, NT>; };
+template <int D, int NT> struct StageSel<float, D, NT> { using type = StageF32<D, NT>; };
+template <typename T, int D, int NT> using Stage = typename StageSel<T, D, NT>::type;
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
@@ -353,5 +422,33 @@ __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32);
 // per-column loads that precede a sweep: otherwise those loads stay "pending" at the
 // loop header on some path and every iteration waits for its own K/V prefetch too.
 __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// Double-buffered sweep over `total` stages. Stage it lives in buf0 for even it and
+// in buf1 for odd it (two distinct LDS objects, so the compiler sees that reading one
+// never waits on the loads filling the other). body(it, lds) computes on stage it
+// while stage it+1 is being fetched; one barrier per stage.
+template <typename St, typename T, typename KeyFn, typename Body>
+__device__ __forceinline__ void sweep(int total, KeyFn key0_of, const T* kbase, const T* vbase, int64_t row_stride,
+                                      int n_valid, int tid, char* buf0, char* buf1, Body&& body) {
+  typename St::Regs regs;
+  if (total > 0) {
+    St::load(regs, kbase, vbase, row_stride, key0_of(0), n_valid, tid, buf0);
+    St::store(regs, buf0, tid);
+  }
+  wait_vmem_all();
+  __syncthreads();
+  auto one = [&](int it, char* cur, char* nxt) {
+    const bool more = it + 1 < total;
+    if (more) St::load(regs, kbase, vbase, row_stride, key0_of(it + 1), n_valid, tid, nxt);
+    body(it, static_cast<const char*>(cur));
+    if (more) St::store(regs, nxt, tid);
+    if constexpr (St::ASYNC) wait_vmem_all();
+    __syncthreads();
+  };
+  for (int it = 0; it < total; it += 2) {
+    one(it, buf0, buf1);
+    if (it + 1 < total) one(it + 1, buf1, buf0);
+  }
+}
 
 }  // namespace poem

@@ -34,11 +34,13 @@ constexpr int kSelThreads = 256;
 constexpr int kSelWaves = 4;
 
 template <typename T, int D, int BLK, bool PASS2>
-__global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) {
+__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void sel_sweep_kernel(SelectParams p) {
   using St = Stage<T, D, kSelThreads>;
   constexpr int SUBS = BLK / kStageKeys;
   constexpr bool SPLIT = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) char smem[2 * St::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
@@ -119,18 +121,10 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
 
   wait_vmem_all();
   const int total = nblk_wg * SUBS;
-  typename St::Regs regs;
-  St::load(regs, kbase, vbase, row_stride, 0, n_k, tid);
-  St::store(regs, smem, tid);
-  __syncthreads();
-  for (int it = 0; it < total; ++it) {
-    char* cur = smem + (it & 1) * St::BYTES;
+  auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
+  sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
     const int blk = it / SUBS, sub = it % SUBS;
-    if (it + 1 < total) {
-      const int nb = (it + 1) / SUBS, ns = (it + 1) % SUBS;
-      St::load(regs, kbase, vbase, row_stride, nb * BLK + ns * kStageKeys, n_k, tid);
-    }
-    const int key0 = blk * BLK + sub * kStageKeys;
+    const int key0 = stage_key0(it);
     if (PASS2 && sub == 0) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
@@ -138,8 +132,8 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
     }
     if (key0 <= wave_pos_max) {
       f32x16 S[2];
-      S[0] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 0, lane);
-      S[1] = qk_tile<T, D, St::K_STRIDE>(cur, qf, 1, lane);
+      S[0] = St::qk_tile(cur, qf, 0, lane);
+      S[1] = St::qk_tile(cur, qf, 1, lane);
       const bool need_mask = key0 + kStageKeys - 1 > wave_pos_min;
       if constexpr (!PASS2) {
         float mx = -INFINITY;
@@ -182,7 +176,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
             mloc += e;
           }
       }
-      pv_stage<T, D, St::V_STRIDE, SPLIT>(cur + St::K_BYTES, S, O, lane);
+      St::template pv<SPLIT>(cur, S, O, lane);
     }
     if constexpr (PASS2) {
       if (sub == SUBS - 1 && wave_on && blk <= diag) {
@@ -202,9 +196,7 @@ __global__ __launch_bounds__(kSelThreads) void sel_sweep_kernel(SelectParams p) 
         }
       }
     }
-    if (it + 1 < total) St::store(regs, smem + ((it + 1) & 1) * St::BYTES, tid);
-    __syncthreads();
-  }
+  });
 
   if constexpr (!PASS2) {
     const float l_tot = l_run + wave_xor32(l_run);
