@@ -196,7 +196,7 @@ __device__ __forceinline__ void p_step(const f32x16 (&p)[2], int s, bf16x8& hi, 
 // Chunk c (16 bytes) of row r sits at chunk position c ^ swizzle(r): the K swizzle
 // spreads the 16 rows that 16 lanes read together for QK over all banks; the V
 // swizzle does the same for the 4 rows x 4 chunks one transposing read touches per
-// 32 lanes. Rows past the sequence end re-read its last key (their scores are masked).
+// 32 lanes. Rows past the sequence end read as zeros (their scores are masked).
 // ---------------------------------------------------------------------------
 template <int D, int NT>
 struct StageB16 {
@@ -214,22 +214,34 @@ struct StageB16 {
     return CH >= 16 ? (2 * (r & 3) + 8 * (r & 1)) : (2 * (r & 3));
   }
 
+  // Buffer descriptors start at the stage's first key and cover only the valid keys,
+  // so rows past the sequence end load as zeros; the per-lane offsets do not depend
+  // on the stage and all stage-dependent addressing stays in scalar registers.
   static __device__ __forceinline__ void load(Regs&, const uint16_t* __restrict__ kbase,
                                               const uint16_t* __restrict__ vbase, int64_t row_stride, int key0,
                                               int n_valid, int tid, char* lds) {
-    const int wave = tid >> 6, lane = tid & 63;
-    const char* kb = reinterpret_cast<const char*>(kbase);
-    const char* vb = reinterpret_cast<const char*>(vbase);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int64_t row_bytes = row_stride * 2;
+    const int64_t base = (int64_t)key0 * row_bytes;
+    const int rows = max(0, min(n_valid - key0, kStageKeys));
+    // uniform by construction; readfirstlane keeps the descriptor in scalar registers
+    const int records = __builtin_amdgcn_readfirstlane((int)(rows * row_bytes));
+    const __amdgpu_buffer_rsrc_t kr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(kbase) + base), (short)0, records,
+                                          0x00020000);
+    const __amdgpu_buffer_rsrc_t vr =
+        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(vbase) + base), (short)0, records,
+                                          0x00020000);
 #pragma unroll
     for (int j = 0; j < INSTR / WAVES; ++j) {
       const int blk = j * WAVES + wave;
       const int off = blk * 1024 + lane * 16;
       const int r = off / ROW, pos = (off % ROW) / 16;
-      const int key = min(key0 + r, n_valid - 1);
-      const int64_t g = (int64_t)key * row_stride * 2;
-      __builtin_amdgcn_global_load_lds(kb + g + (pos ^ kswz(r)) * 16, (lds_char*)(lds + blk * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds(vb + g + (pos ^ vswz(r)) * 16, (lds_char*)(lds + TENSOR + blk * 1024), 16,
-                                       0, 0);
+      const int roff = r * (int)row_bytes;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_char*)(lds + blk * 1024), 16, roff + ((pos ^ kswz(r)) << 4),
+                                               0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_char*)(lds + TENSOR + blk * 1024), 16,
+                                               roff + ((pos ^ vswz(r)) << 4), 0, 0, 0);
     }
   }
   static __device__ __forceinline__ void store(const Regs&, char*, int) {}
