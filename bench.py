@@ -61,6 +61,47 @@ def pair_counts(gp, rp, bi):
     return retained, dense
 
 
+WORKLOAD_TAGS = {1: "single_head_2k_fp32", 2: "llama8b_32k", 3: "llama8b_128k", 4: "qwen14b_64k", 5: "chunked_varlen"}
+
+
+def measured_traffic(workload_id):
+    """HBM bytes per launch of the sparse attention kernel from the committed rocprofv3
+    FETCH_SIZE / WRITE_SIZE runs (scaled by a plain copy's readings), or None when the
+    record is missing or the kernel sources changed since the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", f"traffic_{WORKLOAD_TAGS.get(workload_id, '')}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = b"".join(open(os.path.join(ROOT, "block_sparse_attention_poem_amd", "csrc", f), "rb").read()
+                   for f in ("poem_device.hpp", "poem_internal.hpp", "attn_fwd.hip"))
+    if hashlib.sha256(src).hexdigest() != rec.get("attn_source_sha256"):
+        return None
+    k = rec["kernels"].get("void poem::attn_sparse_persistent_kernel<unsigned short, 128, 128>")
+    if k is None:
+        return None
+    return k["read_bytes"] + k["write_bytes"]
+
+
+def unique_bytes(gp, rp, bi, in_bytes, out_bytes):
+    """Minimum HBM bytes of one sparse launch: Q read once, O written once, and every
+    (KV head, sequence, block) that some row retains read once (K and V)."""
+    n_rows, _ = tile_table(gp)
+    T = len(n_rows)
+    G = gp.num_heads_q // gp.num_heads_kv
+    seq_of_tile = np.concatenate([np.full(-(-nq // gp.block_size), s, np.int64)
+                                  for s, nq in enumerate(gp.seqlens_q)]) if T else np.zeros(0, np.int64)
+    counts = np.diff(rp)
+    r = np.repeat(np.arange(len(counts)), counts)
+    g = (r // T) // G
+    sq = seq_of_tile[r % T]
+    key = (g * len(gp.seqlens_q) + sq) * (1 << 20) + bi[:len(r)].astype(np.int64)
+    n_blocks = len(np.unique(key))
+    kv = 2 * n_blocks * gp.block_size * gp.head_dim * in_bytes
+    q_o = gp.total_q * gp.num_heads_q * gp.head_dim * (in_bytes + out_bytes)
+    return int(kv + q_o)
+
+
 def cpu_baseline(w, inp, gp, rp, bi, seconds):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: per
     sampled (head, tile), the selector and the sparse attention over its oracle-kept
@@ -235,9 +276,11 @@ def main():
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
     # dominant kernel of the step: the sparse attention kernel (one launch) or the selector
     attn_tflops = flop_ret / (sp_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_fwd_kernel (sparse)", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
-                "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": None,
-                "algorithmic": f"4 d P_R = {flop_ret:.4e} FLOP per launch"}
+    roofline = {"kernel": "attn_sparse_persistent_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
+                "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": measured_traffic(args.workload),
+                "algorithmic": f"4 d P_R = {flop_ret:.4e} FLOP per launch",
+                "algorithmic_bytes": unique_bytes(gp, rp, bi, q.element_size(),
+                                                  out.element_size())}
     res = {
         "metric": METRIC, "value": value, "unit": "TFLOP/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True, "scaling": "weak",
