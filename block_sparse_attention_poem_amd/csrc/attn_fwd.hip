@@ -27,12 +27,22 @@ struct AttnCfg {
   static constexpr int NT = WAVES * 64;
   using St = Stage<T, D, NT>;
   static constexpr int SUBS = BLK / kStageKeys;
-  static constexpr int STAGE_BYTES = St::BYTES;
+  // bf16: K and V each double-buffered in four separate LDS arrays (a pipelined sweep);
+  // fp32: two stage buffers (K and transposed V together)
+  static constexpr int KBUF = St::ASYNC ? St::BYTES / 2 : St::BYTES;
+  static constexpr int VBUF = St::ASYNC ? St::BYTES / 2 : 16;
 };
+
+#define POEM_ATTN_LDS(T, D, BLK)                                                        \
+  __shared__ __attribute__((aligned(16))) char kb0[AttnCfg<T, D, BLK>::KBUF];           \
+  __shared__ __attribute__((aligned(16))) char kb1[AttnCfg<T, D, BLK>::KBUF];           \
+  __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];           \
+  __shared__ __attribute__((aligned(16))) char vb1[AttnCfg<T, D, BLK>::VBUF];
 
 // One (query head h, tile t of sequence seq): the whole workgroup, B rows.
 template <typename T, int D, int BLK, bool SPARSE>
-__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* buf0, char* buf1) {
+__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* kb0, char* kb1,
+                                          char* vb0, char* vb1) {
   using C = AttnCfg<T, D, BLK>;
   using St = typename C::St;
   constexpr int SUBS = C::SUBS;
@@ -89,28 +99,24 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   float m_run = -INFINITY, l_run = 0.f;
   const float c = p.scale_log2;
 
-  sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
-    const int key0 = stage_key0(it);
-    if (key0 > wave_pos_max) return;  // every key of the stage is above this wave's rows
-    f32x16 S[2];
-    S[0] = St::qk_tile(cur, qf, 0, lane);
-    S[1] = St::qk_tile(cur, qf, 1, lane);
-    float mx = -INFINITY;
+  // causal mask of one stage's scores: only stages that reach past a row need it
+  auto mask = [&](f32x16 (&S)[2], int key0) {
     if (key0 + kStageKeys - 1 > wave_pos_min) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float s = (key0 + acc_key(kt, r, g2) > my_pos) ? -INFINITY : S[kt][r];
-          S[kt][r] = s;
-          mx = fmaxf(mx, s);
-        }
-    } else {
-#pragma unroll
-      for (int kt = 0; kt < 2; ++kt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
+        for (int r = 0; r < 16; ++r)
+          if (key0 + acc_key(kt, r, g2) > my_pos) S[kt][r] = -INFINITY;
     }
+  };
+  // online-softmax step: S becomes 2^(c s - m) for the new running max m; returns the
+  // factor that rescales what was accumulated so far
+  auto weights = [&](f32x16 (&S)[2]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = fmaxf(mx, wave_xor32(mx));
     const float m_new = fmaxf(m_run, mx * c);
     const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
@@ -120,18 +126,83 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        float e = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
-        S[kt][r] = e;
-        rs += e;
+        S[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
+        rs += S[kt][r];
       }
+    // the row sum here keeps the exponentials next to the MFMAs they overlap
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    return alpha;
+  };
+  // rescale, then O += P V for the stage whose weights are in S and V in vbuf
+  auto accumulate = [&](f32x16 (&S)[2], float alpha, const char* vbuf) {
     if (__any(alpha != 1.f)) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
     }
-    St::template pv<false>(cur, S, O, lane);
-  });
+    if constexpr (St::ASYNC) {
+      bf16x8 P[4], unused;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) p_step<false>(S, s4, P[s4], unused);
+      St::pv_packed(vbuf, P, O, lane);
+    } else {
+      St::template pv<false>(vbuf, S, O, lane);
+    }
+  };
+
+  if constexpr (St::ASYNC) {
+    // Software pipeline over stages. K and V have their own double buffers and V lags K
+    // by one stage: step j reads K(j) and V(j-1) while K(j+1) and V(j) load, so the
+    // QK^T MFMAs of stage j are issued next to the softmax of stage j-1.
+    f32x16 Sp[2];
+    auto first = [&]() {
+      St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0);
+      wait_vmem_all();
+      __syncthreads();
+      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1);
+      St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0);
+      Sp[0] = St::qk_tile(kb0, qf, 0, lane);
+      Sp[1] = St::qk_tile(kb0, qf, 1, lane);
+      mask(Sp, stage_key0(0));
+      wait_vmem_all();
+      __syncthreads();
+    };
+    auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
+      const int key0 = stage_key0(it);
+      St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext);
+      St::load_v(vbase, row_stride, key0, n_k, tid, vcur);
+      f32x16 Sn[2];
+      Sn[0] = St::qk_tile(kcur, qf, 0, lane);
+      Sn[1] = St::qk_tile(kcur, qf, 1, lane);
+      const float alpha = weights(Sp);
+      accumulate(Sp, alpha, vprev);
+      mask(Sn, key0);
+      Sp[0] = Sn[0];
+      Sp[1] = Sn[1];
+      wait_vmem_all();
+      __syncthreads();
+    };
+    if (total > 0) {
+      first();
+      for (int it = 1; it < total; it += 2) {
+        step(it, kb1, kb0, vb0, vb1);
+        if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
+      }
+      const float alpha = weights(Sp);
+      accumulate(Sp, alpha, ((total - 1) & 1) ? vb1 : vb0);
+    }
+  } else {
+    sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, kb0, kb1, [&](int it, const char* cur) {
+      const int key0 = stage_key0(it);
+      if (key0 > wave_pos_max) return;  // every key of the stage is above this wave's rows
+      f32x16 S[2];
+      S[0] = St::qk_tile(cur, qf, 0, lane);
+      S[1] = St::qk_tile(cur, qf, 1, lane);
+      mask(S, key0);
+      const float alpha = weights(S);
+      accumulate(S, alpha, cur);
+    });
+  }
 
   const float l_tot = l_run + wave_xor32(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
@@ -160,8 +231,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 template <typename T, int D, int BLK, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_fwd_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char buf0[AttnCfg<T, D, BLK>::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char buf1[AttnCfg<T, D, BLK>::STAGE_BYTES];
+  POEM_ATTN_LDS(T, D, BLK)
   const int bid = blockIdx.x;
   const int gk = bid % p.hkv;
   const int rest = bid / p.hkv;
@@ -170,7 +240,7 @@ void attn_fwd_kernel(AttnParams p) {
   int seq, t;
   rank_to_item(p.seqs, 1, rank, seq, t);
   if (seq < 0) return;
-  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, buf0, buf1);
+  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, kb0, kb1, vb0, vb1);
 }
 
 // Persistent schedule for sparse rows, whose lengths vary from a few blocks to
@@ -180,8 +250,7 @@ void attn_fwd_kernel(AttnParams p) {
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_sparse_persistent_kernel(AttnParams p) {
-  __shared__ __attribute__((aligned(16))) char buf0[AttnCfg<T, D, BLK>::STAGE_BYTES];
-  __shared__ __attribute__((aligned(16))) char buf1[AttnCfg<T, D, BLK>::STAGE_BYTES];
+  POEM_ATTN_LDS(T, D, BLK)
   __shared__ int item_sh;
   const int n_tiles = p.seqs.total_tiles;
   for (;;) {
@@ -193,23 +262,31 @@ void attn_sparse_persistent_kernel(AttnParams p) {
     const int r = p.order[item];
     const int h = r / n_tiles, gtile = r % n_tiles;
     const int seq = find_seq(p.seqs, gtile);
-    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], buf0, buf1);
+    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], kb0, kb1, vb0, vb1);
   }
 }
 
-// Orders the CSR rows by retained count, descending (a counting sort in LDS), and
-// resets the queue head. One workgroup.
+// Orders the CSR rows of each KV head by retained count, descending (a counting sort
+// in LDS; one workgroup per KV head, whose rows h*T .. are contiguous), KV heads one
+// after another, and resets the queue head. Pulling rows in this order keeps the
+// running workgroups on one KV head's K/V at a time (64 MiB at 128K tokens), which
+// the 256 MiB memory-side cache can hold while the rows re-read it.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 4097;  // counts are clamped to 4096 for ordering only
 __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const int32_t* __restrict__ row_ptr,
-                                                                       int rows, int32_t* __restrict__ order,
+                                                                       int rows_per_group,
+                                                                       int32_t* __restrict__ order_all,
                                                                        int32_t* __restrict__ queue) {
   __shared__ int hist[kSchedBins];
   __shared__ int sh[16];
   const int tid = threadIdx.x;
+  const int first = blockIdx.x * rows_per_group;
+  const int rows = rows_per_group;
+  int32_t* order = order_all + first;
   for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
-  auto bin = [&](int r) {
+  auto bin = [&](int i) {
+    const int r = first + i;
     const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), kSchedBins - 1);
     return kSchedBins - 1 - c;  // longest first
   };
@@ -233,8 +310,8 @@ __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const in
     }
   }
   __syncthreads();
-  for (int r = tid; r < rows; r += kSchedThreads) order[atomicAdd(&hist[bin(r)], 1)] = r;
-  if (tid == 0) *queue = 0;
+  for (int r = tid; r < rows; r += kSchedThreads) order[atomicAdd(&hist[bin(r)], 1)] = first + r;
+  if (blockIdx.x == 0 && tid == 0) *queue = 0;
 }
 
 template <typename T, int D, int BLK, bool SPARSE>
@@ -242,8 +319,8 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.seqs.total_tiles * p.hq;
   if (grid == 0) return hipSuccess;
   if (SPARSE && p.queue != nullptr) {
-    hipLaunchKernelGGL(sparse_schedule_kernel, dim3(1), dim3(kSchedThreads), 0, stream, p.row_ptr, p.num_rows,
-                       p.order, p.queue);
+    hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
+                       p.num_rows / p.hkv, p.order, p.queue);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -123,7 +123,7 @@ SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S) {
   L.row_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * CT * 32 * (p->head_dim + 4));
   L.blk_stats = off;
-  off += align256(sizeof(float) * (size_t)p->num_heads_q * g.vis_per_head * S * 2);
+  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.vis_per_head * CT * 32 * 2);
   L.counts = off;
   off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.num_tiles);
   L.slots = off;

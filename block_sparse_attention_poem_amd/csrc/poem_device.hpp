@@ -217,32 +217,50 @@ struct StageB16 {
   // Buffer descriptors start at the stage's first key and cover only the valid keys,
   // so rows past the sequence end load as zeros; the per-lane offsets do not depend
   // on the stage and all stage-dependent addressing stays in scalar registers.
-  static __device__ __forceinline__ void load(Regs&, const uint16_t* __restrict__ kbase,
-                                              const uint16_t* __restrict__ vbase, int64_t row_stride, int key0,
-                                              int n_valid, int tid, char* lds) {
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
-    const int64_t row_bytes = row_stride * 2;
-    const int64_t base = (int64_t)key0 * row_bytes;
+  template <bool IS_V>
+  static __device__ __forceinline__ void load_one(const uint16_t* __restrict__ base_ptr, int64_t row_stride,
+                                                  int key0, int n_valid, int tid, char* dst) {
+    // One wave-wide load covers RPI whole rows: lane l takes chunk l % CH of row
+    // RPI * blk + l / CH. Every swizzle above only sees the low bits of the row, which
+    // the wave's first row (a multiple of RPI) leaves to the lane's own l / CH (plus,
+    // for K with RPI < CH, a uniform part), so the per-lane offset is a few unsigned
+    // operations on values fixed for the whole sweep.
+    constexpr uint32_t RPI = 1024 / ROW;
+    static_assert(RPI % 4 == 0 && RPI <= CH, "row groups must keep the swizzle bits lane-local");
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const uint32_t lane = (uint32_t)tid & 63u;
+    const uint32_t row_bytes = (uint32_t)(row_stride * 2);
     const int rows = max(0, min(n_valid - key0, kStageKeys));
     // uniform by construction; readfirstlane keeps the descriptor in scalar registers
     const int records = __builtin_amdgcn_readfirstlane((int)(rows * row_bytes));
-    const __amdgpu_buffer_rsrc_t kr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(kbase) + base), (short)0, records,
-                                          0x00020000);
-    const __amdgpu_buffer_rsrc_t vr =
-        __builtin_amdgcn_make_buffer_rsrc((void*)(reinterpret_cast<const char*>(vbase) + base), (short)0, records,
-                                          0x00020000);
+    const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(reinterpret_cast<const char*>(base_ptr) + (int64_t)key0 * row_stride * 2), (short)0, records,
+        0x00020000);
+    const uint32_t lr = lane / CH, pos = lane % CH;
+    const uint32_t lane_row = lr * row_bytes;
 #pragma unroll
     for (int j = 0; j < INSTR / WAVES; ++j) {
-      const int blk = j * WAVES + wave;
-      const int off = blk * 1024 + lane * 16;
-      const int r = off / ROW, pos = (off % ROW) / 16;
-      const int roff = r * (int)row_bytes;
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, (lds_char*)(lds + blk * 1024), 16, roff + ((pos ^ kswz(r)) << 4),
-                                               0, 0, 0);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, (lds_char*)(lds + TENSOR + blk * 1024), 16,
-                                               roff + ((pos ^ vswz(r)) << 4), 0, 0, 0);
+      const uint32_t blk = j * WAVES + wave;
+      const uint32_t r0 = RPI * blk;  // uniform
+      const uint32_t sw = IS_V ? (uint32_t)vswz(lr) : ((r0 & (CH - 1)) | lr);
+      const uint32_t voff = r0 * row_bytes + lane_row + ((pos ^ sw) << 4);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_char*)(dst + blk * 1024), 16, (int)voff, 0, 0, 0);
     }
+  }
+  static __device__ __forceinline__ void load_k(const uint16_t* kbase, int64_t row_stride, int key0, int n_valid,
+                                                int tid, char* kbuf) {
+    load_one<false>(kbase, row_stride, key0, n_valid, tid, kbuf);
+  }
+  static __device__ __forceinline__ void load_v(const uint16_t* vbase, int64_t row_stride, int key0, int n_valid,
+                                                int tid, char* vbuf) {
+    load_one<true>(vbase, row_stride, key0, n_valid, tid, vbuf);
+  }
+  // both tensors of a stage into one buffer: K, then V at +TENSOR
+  static __device__ __forceinline__ void load(Regs&, const uint16_t* __restrict__ kbase,
+                                              const uint16_t* __restrict__ vbase, int64_t row_stride, int key0,
+                                              int n_valid, int tid, char* lds) {
+    load_k(kbase, row_stride, key0, n_valid, tid, lds);
+    load_v(vbase, row_stride, key0, n_valid, tid, lds + TENSOR);
   }
   static __device__ __forceinline__ void store(const Regs&, char*, int) {}
   // the direct loads write LDS asynchronously: wait for this wave's before the barrier
@@ -267,12 +285,11 @@ struct StageB16 {
   // group of 16 lanes the transposing read hands lane i element (i & 3) of the 8 bytes
   // addressed by lane 4e + (i >> 2), as its element e; so lane 4e + k addresses key
   // base + e, d = 16-column base + 4k.
-  static __device__ __forceinline__ bf16x8 v_frag(const char* lds, int dt, int s, int lane) {
+  static __device__ __forceinline__ bf16x8 v_frag(const char* vt, int dt, int s, int lane) {
     const int q = lane >> 4, i = lane & 15, g = q >> 1;
     const int d = 32 * dt + 16 * (q & 1) + 4 * (i & 3);
     const int c = d >> 3, half = (d >> 2) & 1;
     const int r0 = 16 * s + 4 * g + (i >> 2), r1 = r0 + 8;
-    const char* vt = lds + TENSOR;
     const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
         (v4i16 __attribute__((address_space(3)))*)(vt + r0 * ROW + (c ^ vswz(r0)) * 16 + half * 8));
     const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
@@ -280,6 +297,15 @@ struct StageB16 {
     typedef short v8i16 __attribute__((ext_vector_type(8)));
     const v8i16 ab = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     return __builtin_bit_cast(bf16x8, ab);
+  }
+
+  // O^T[dt] += V^T . P^T with P already packed to bf16 (one operand per 16-key step).
+  static __device__ __forceinline__ void pv_packed(const char* vbuf, const bf16x8 (&P)[4], f32x16* O, int lane) {
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(v_frag(vbuf, dt, s, lane), P[s], O[dt], 0, 0, 0);
   }
 
   // O^T[dt] += V^T . P^T over the stage's 64 keys, one 16-key step at a time.
@@ -291,7 +317,7 @@ struct StageB16 {
       p_step<SPLIT>(p, s, ph, pl);
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) {
-        const bf16x8 a = v_frag(lds, dt, s, lane);
+        const bf16x8 a = v_frag(lds + TENSOR, dt, s, lane);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, ph, O[dt], 0, 0, 0);
         if constexpr (SPLIT) O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pl, O[dt], 0, 0, 0);
       }

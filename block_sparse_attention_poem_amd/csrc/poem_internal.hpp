@@ -46,7 +46,7 @@ struct SelectParams {
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions
   float* row_stats;          // [hkv][total_tiles][col_tiles*32][D + 4]: M2, l, pad, pad, normalised o
-  float* blk_stats;          // per (h, gtile): [S][n_vis] I then [S][n_vis] m, at slot offsets
+  float* blk_stats;          // per (KV head, gtile, visible block): I[32*col_tiles] then m[32*col_tiles]
   int32_t* counts;           // [hq * total_tiles]
   int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets
   // outputs

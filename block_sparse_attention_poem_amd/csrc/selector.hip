@@ -108,15 +108,13 @@ void sel_sweep_kernel(SelectParams p) {
         for (int e = 0; e < 4; ++e) Od[dt][4 * a + e] = v4[e];
       }
   }
+  // per (KV head, tile, visible block): I of all 32*CT columns, then m of all columns,
+  // so a wave's per-block results are one coalesced 128-byte store each
   float* blk_I = nullptr;
-  float* blk_m = nullptr;
   if constexpr (PASS2) {
-    if (col_on) {
-      const int n_vis = diag + 1;
-      blk_I = p.blk_stats + ((int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * p.S * 2 +
-              (int64_t)jr * n_vis;
-      blk_m = blk_I + (int64_t)p.S * n_vis;
-    }
+    if (wave_on)
+      blk_I = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * (2 * 32 * CT) +
+              32 * ct + jcol;
   }
 
   wait_vmem_all();
@@ -191,8 +189,9 @@ void sel_sweep_kernel(SelectParams p) {
           }
         ss += wave_xor32(ss);
         if (col_on && g2 == 0) {
-          blk_I[blk] = __builtin_sqrtf(ss) * inv_l;
-          blk_m[blk] = mt * inv_l;
+          float* dst = blk_I + (int64_t)blk * (2 * 32 * CT);
+          dst[0] = __builtin_sqrtf(ss) * inv_l;
+          dst[32 * CT] = mt * inv_l;
         }
       }
     }
@@ -225,26 +224,39 @@ constexpr int kThrThreads = 256;
 constexpr int kMaxVis = 4096;
 
 
-// Exclusive prefix over the workgroup of (a, b) in thread order.
-__device__ __forceinline__ void block_excl_scan2(double a, double b, double& ea, double& eb, double* sh) {
+// Exclusive prefix over the workgroup, in thread order, of N pairs of doubles (each
+// thread's A[r], D[r] are replaced by the sums over lower threads). sh: 8 * N doubles.
+constexpr int kRowChunk = 8;
+template <int N>
+__device__ __forceinline__ void block_excl_scan_vec(double (&A)[N], double (&D)[N], double* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  double ia = a, ib = b;
+  double ia[N], id[N];
+#pragma unroll
+  for (int r = 0; r < N; ++r) { ia[r] = A[r]; id[r] = D[r]; }
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    double ta = __shfl_up(ia, o), tb = __shfl_up(ib, o);
-    if (lane >= o) { ia += ta; ib += tb; }
+#pragma unroll
+    for (int r = 0; r < N; ++r) {
+      const double ta = __shfl_up(ia[r], o), td = __shfl_up(id[r], o);
+      if (lane >= o) { ia[r] += ta; id[r] += td; }
+    }
   }
-  double xa = __shfl_up(ia, 1), xb = __shfl_up(ib, 1);
-  if (lane == 0) { xa = 0.0; xb = 0.0; }
-  if (lane == 63) { sh[wave] = ia; sh[4 + wave] = ib; }
+  if (lane == 63) {
+#pragma unroll
+    for (int r = 0; r < N; ++r) { sh[(2 * r) * 4 + wave] = ia[r]; sh[(2 * r + 1) * 4 + wave] = id[r]; }
+  }
   __syncthreads();
-  double oa = 0.0, ob = 0.0;
-  for (int w = 0; w < wave; ++w) { oa += sh[w]; ob += sh[4 + w]; }
+#pragma unroll
+  for (int r = 0; r < N; ++r) {
+    double xa = __shfl_up(ia[r], 1), xd = __shfl_up(id[r], 1);
+    if (lane == 0) { xa = 0.0; xd = 0.0; }
+    double oa = 0.0, od = 0.0;
+    for (int w = 0; w < wave; ++w) { oa += sh[(2 * r) * 4 + w]; od += sh[(2 * r + 1) * 4 + w]; }
+    A[r] = oa + xa;
+    D[r] = od + xd;
+  }
   __syncthreads();
-  ea = oa + xa;
-  eb = ob + xb;
 }
-
 
 __device__ __forceinline__ int block_min_int(int v, int* sh) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -261,12 +273,13 @@ __device__ __forceinline__ int block_min_int(int v, int* sh) {
 __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
   __shared__ uint64_t keys[kMaxVis];
   __shared__ uint8_t keep[kMaxVis];
-  __shared__ double shd[8];
+  __shared__ double shd[8 * kRowChunk];
   __shared__ int shi[8];
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
-  const int R = blockIdx.x;
-  const int h = R / T, gtile = R % T;
+  // heads of one tile are adjacent in the grid: they read the same workspace lines
+  const int gtile = blockIdx.x / p.hq, h = blockIdx.x % p.hq;
+  const int R = h * T + gtile;  // CSR row
   const int seq = find_seq(p.seqs, gtile);
   const int t = gtile - p.seqs.tile_start[seq];
   const int B = p.seqs.block;
@@ -276,8 +289,12 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int s_t = min(p.S, n_rows_t);
   const int S = p.S;
   const int64_t slot = (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
-  const float* Ib = p.blk_stats + slot * S * 2;
-  const float* Mb = Ib + (int64_t)S * n_vis;
+  const int cols = 32 * p.col_tiles;
+  const int64_t bstride = 2 * cols;  // floats per visible block
+  // row i of this head is column (h % G) * S + i of its KV head's tile record
+  const float* Ib = p.blk_stats + ((int64_t)(h / p.group) * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) *
+                                      bstride + (h % p.group) * S;
+  const float* Mb = Ib + cols;
   const float tau = p.tau[h];
   int n_pad = 2;
   while (n_pad < n_vis) n_pad <<= 1;
@@ -285,20 +302,40 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
   const float inv_s = 1.f / (float)s_t;
   const int64_t diag_row = ((int64_t)h * T + gtile) * p.max_vis;
-  for (int b = tid; b < n_pad; b += kThrThreads) {
-    uint64_t key = ~0ull;
-    if (b < n_vis) {
-      float si = 0.f, sm = 0.f;
-      for (int i = 0; i < s_t; ++i) {
-        si += Ib[(int64_t)i * n_vis + b];
-        sm += Mb[(int64_t)i * n_vis + b];
+  // scores: sp lanes per block read its s_t contiguous values and sum them by shuffles
+  int sp = 1;
+  while (sp < s_t) sp <<= 1;
+  const int per_pass = kThrThreads / sp, ri = tid % sp;
+  constexpr int U = 4;  // passes whose loads are issued together
+  for (int b0 = 0; b0 < n_pad; b0 += U * per_pass) {
+    float si[U], sm[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int b = b0 + u * per_pass + tid / sp;
+      si[u] = sm[u] = 0.f;
+      if (b < n_vis && ri < s_t) {
+        si[u] = Ib[(int64_t)b * bstride + ri];
+        sm[u] = Mb[(int64_t)b * bstride + ri];
       }
-      const float score = si * inv_s, mass = sm * inv_s;
-      if (p.tile_scores) p.tile_scores[diag_row + b] = score;
-      if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
-      if (!mandatory(b)) key = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
     }
-    keys[b] = key;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      for (int o = sp >> 1; o > 0; o >>= 1) {
+        si[u] += __shfl_xor(si[u], o);
+        sm[u] += __shfl_xor(sm[u], o);
+      }
+      const int b = b0 + u * per_pass + tid / sp;
+      if (ri == 0 && b < n_pad) {
+        uint64_t key = ~0ull;
+        if (b < n_vis) {
+          const float score = si[u] * inv_s, mass = sm[u] * inv_s;
+          if (p.tile_scores) p.tile_scores[diag_row + b] = score;
+          if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
+          if (!mandatory(b)) key = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
+        }
+        keys[b] = key;
+      }
+    }
   }
   for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
     if (p.tile_scores) p.tile_scores[diag_row + b] = -1.f;
@@ -327,61 +364,60 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int E = n_pad >= kThrThreads ? n_pad / kThrThreads : 1;
   auto id_at = [&](int k) { return (int)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull)); };
 
-  // first prefix length whose bound exceeds tau, over all sampled rows
+  // Prefix sums over the discard order, all sampled rows at once: each thread walks
+  // its E consecutive positions reading the whole row record of each block (rows of a
+  // chunk are contiguous), a vector scan gives each thread its exclusive prefixes, and
+  // the first prefix length whose per-row bound exceeds tau is a block minimum.
+  // With `limit` = the cut, the same walk yields the per-row bound at the cut.
+  auto walk = [&](int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
+    double A[kRowChunk], Dl[kRowChunk];
+#pragma unroll
+    for (int r = 0; r < kRowChunk; ++r) A[r] = Dl[r] = 0.0;
+    for (int e = 0; e < E; ++e) {
+      const int k = tid * E + e;
+      if (k < limit) {
+        const float* ip = Ib + (int64_t)id_at(k) * bstride + i0;
+#pragma unroll
+        for (int r = 0; r < kRowChunk; ++r)
+          if (r < nr) { A[r] += (double)ip[r]; Dl[r] += (double)ip[cols + r]; }
+      }
+    }
+    block_excl_scan_vec<kRowChunk>(A, Dl, shd);
+    for (int e = 0; e < E; ++e) {
+      const int k = tid * E + e;
+      if (k < limit) {
+        const float* ip = Ib + (int64_t)id_at(k) * bstride + i0;
+        bool over = false;
+#pragma unroll
+        for (int r = 0; r < kRowChunk; ++r)
+          if (r < nr) {
+            A[r] += (double)ip[r];
+            Dl[r] += (double)ip[cols + r];
+            const double bound = (1.0 - Dl[r] > 0.0) ? A[r] / (1.0 - Dl[r]) : INFINITY;
+            over |= bound > (double)tau;
+            if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
+          }
+        if (find && over && local_fail == INT_MAX) local_fail = k + 1;
+      }
+    }
+  };
   int k_fail = n_cand + 1;
-  for (int i = 0; i < s_t; ++i) {
-    double a = 0.0, dl = 0.0;
-    for (int e = 0; e < E; ++e) {
-      const int k = tid * E + e;
-      if (k < n_cand) {
-        const int b = id_at(k);
-        a += (double)Ib[(int64_t)i * n_vis + b];
-        dl += (double)Mb[(int64_t)i * n_vis + b];
-      }
-    }
-    double pa, pd;
-    block_excl_scan2(a, dl, pa, pd, shd);
+  for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
     int local_fail = INT_MAX;
-    for (int e = 0; e < E; ++e) {
-      const int k = tid * E + e;
-      if (k < n_cand) {
-        const int b = id_at(k);
-        pa += (double)Ib[(int64_t)i * n_vis + b];
-        pd += (double)Mb[(int64_t)i * n_vis + b];
-        const double bound = (1.0 - pd > 0.0) ? pa / (1.0 - pd) : INFINITY;
-        if (bound > (double)tau && local_fail == INT_MAX) local_fail = k + 1;
-      }
-    }
+    walk(i0, min(kRowChunk, s_t - i0), n_cand, true, local_fail, nullptr);
     k_fail = min(k_fail, block_min_int(local_fail, shi));
   }
   const int k_star = k_fail - 1;
 
   if (p.row_bound) {
     float* rb = p.row_bound + ((int64_t)h * T + gtile) * S;
-    for (int i = 0; i < s_t; ++i) {
-      double a = 0.0, dl = 0.0;
-      for (int e = 0; e < E; ++e) {
-        const int k = tid * E + e;
-        if (k < k_star) {
-          const int b = id_at(k);
-          a += (double)Ib[(int64_t)i * n_vis + b];
-          dl += (double)Mb[(int64_t)i * n_vis + b];
-        }
-      }
-      double pa, pd;
-      block_excl_scan2(a, dl, pa, pd, shd);
-      for (int e = 0; e < E; ++e) {
-        const int k = tid * E + e;
-        if (k < k_star) {
-          const int b = id_at(k);
-          pa += (double)Ib[(int64_t)i * n_vis + b];
-          pd += (double)Mb[(int64_t)i * n_vis + b];
-          if (k == k_star - 1) rb[i] = (float)((1.0 - pd > 0.0) ? pa / (1.0 - pd) : INFINITY);
-        }
-      }
-      if (k_star == 0 && tid == 0) rb[i] = 0.f;
+    for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+      int unused = INT_MAX;
+      walk(i0, min(kRowChunk, s_t - i0), k_star, false, unused, rb);
     }
-    for (int i = s_t + tid; i < S; i += kThrThreads) rb[i] = -1.f;
+    for (int i = tid; i < S; i += kThrThreads)
+      if (i >= s_t) rb[i] = -1.f;
+      else if (k_star == 0) rb[i] = 0.f;
   }
 
   // retained set, compacted in ascending id order
@@ -431,8 +467,9 @@ __global__ __launch_bounds__(1024) void csr_scan_kernel(const int32_t* __restric
 // Copy each row's ids from its slot to its CSR position.
 __global__ __launch_bounds__(64) void csr_scatter_kernel(SelectParams p) {
   const int T = p.seqs.total_tiles;
-  const int R = blockIdx.x;
-  const int h = R / T, gtile = R % T;
+  // heads of one tile are adjacent in the grid: they read the same workspace lines
+  const int gtile = blockIdx.x / p.hq, h = blockIdx.x % p.hq;
+  const int R = h * T + gtile;  // CSR row
   const int seq = find_seq(p.seqs, gtile);
   const int t = gtile - p.seqs.tile_start[seq];
   const int32_t* src = p.slots + (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
