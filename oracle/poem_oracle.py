@@ -29,6 +29,8 @@ Readings where the pages are silent (each listed in the design doc):
     scores the larger id is discarded first. Retained ids are reported ascending.
   * Chunk alignment: the queries of a chunk sit at N_k - N_q .. N_k - 1 and
     (N_k - N_q) is a multiple of the block size.
+  * Mass-only baseline: rank by the tile mass; cut at the last prefix whose
+    largest per-row omitted mass is <= eps (the per-head budget).
 
 Everything is float64; inputs are widened exactly from bf16 / fp32.
 """
@@ -334,14 +336,66 @@ def select_tile(p: Problem, q, k, v, h: int, tile: Tile, tau: float, n_sink: int
                          per_row, ks, retained)
 
 
-def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=None):
+# ---------------------------------------------------------------------------
+# Mass-only selector: the baseline the note measures POEM against (ranking by
+# attention mass alone). Ranking key: the tile mass mean of m over the sampled
+# rows. Stopping rule (a reading; the pages fix no mass threshold): a discard set
+# is acceptable while every sampled row keeps all but at most eps of its dense
+# mass, i.e. max_i Delta_i(k) <= eps. With values of norm <= R that caps each
+# sampled row's error at 2 R eps ([BFLA] Appendix B.1, worst case 2 R delta).
+# ---------------------------------------------------------------------------
+
+
+def mass_curve(m_rows, order):
+    """Delta(k) for k = 0 .. len(order): max over sampled rows of the summed mass
+    of the first k blocks of the discard order; also the per-row values [k, row]."""
+    m_rows = np.asarray(m_rows, dtype=np.float64)
+    per_row = np.zeros((len(order) + 1, m_rows.shape[0]))
+    for k in range(1, len(order) + 1):
+        per_row[k] = per_row[k - 1] + m_rows[:, order[k - 1]]
+    return per_row.max(axis=1), per_row
+
+
+def select_tile_mass(p: Problem, q, k, v, h: int, tile: Tile, eps: float, n_sink: int,
+                     n_local: int, S: int) -> TileSelection:
+    """Mass-only selection for one (query head, tile): the same sampled rows and
+    per-row block masses as select_tile, ranked by the tile mass (discard order:
+    lowest mass first, larger id first among equal masses) and cut at the last
+    prefix whose largest per-row omitted mass is <= eps. `score` holds the ranking
+    key (the tile mass); I and o are reported as in select_tile."""
+    g = h // p.group
+    K = _head_view(k, tile.k_row0, tile.n_k, g)
+    V = _head_view(v, tile.k_row0, tile.n_k, g)
+    n_vis = tile.diag + 1
+    rows = sampled_rows(tile.n_rows, S)
+    stats = [row_block_stats(q[tile.q_row0 + r, h, :], K, V, p.scale, tile.pos0 + r, n_vis, p.block_size)
+             for r in rows]
+    I = np.stack([st["I"] for st in stats])
+    m = np.stack([st["m"] for st in stats])
+    mass = m.mean(axis=0)
+    mand = mandatory_blocks(tile.diag, n_sink, n_local)
+    cand = [b for b in range(n_vis) if b not in set(mand)]
+    order = discard_order(mass, cand)
+    curve, per_row = mass_curve(m, order)
+    ks = cut(curve, float(eps))
+    drop = set(order[:ks])
+    retained = [b for b in range(n_vis) if b not in drop]
+    return TileSelection(h, tile, rows, I, m, np.array([st["lse"] for st in stats]),
+                         np.stack([st["o"] for st in stats]), mass, mass, mand, order, curve,
+                         per_row, ks, retained)
+
+
+def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=None, mode: str = "poem"):
     """Selections for every (head, tile), or for the (h, gtile) pairs in `which`.
+    mode "poem" uses the output-relative selector (tau: error threshold per head),
+    "mass" the mass-only one (tau: omitted-mass budget per head).
 
     Returns {(h, gtile): TileSelection}."""
+    fn = {"poem": select_tile, "mass": select_tile_mass}[mode]
     tl = tiles(p)
     if which is None:
         which = [(h, t.gtile) for h in range(p.num_heads_q) for t in tl]
-    return {(h, gt): select_tile(p, q, k, v, h, tl[gt], float(tau[h]), n_sink, n_local, S)
+    return {(h, gt): fn(p, q, k, v, h, tl[gt], float(tau[h]), n_sink, n_local, S)
             for (h, gt) in which}
 
 

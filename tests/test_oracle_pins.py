@@ -375,6 +375,90 @@ def test_nested_supports():
         prev = sel
 
 
+# --- mass-only selector ---------------------------------------------------------------
+
+
+def pin_mass_cut():
+    """Mass-only cut. One sampled row: keeping the discard order's longest acceptable
+    prefix discards the largest number of blocks whose total mass fits the budget
+    (brute force over every subset). Several rows: every prefix's largest per-row
+    omitted mass recomputed from scratch."""
+    import itertools
+    rng = np.random.default_rng(31)
+    for _ in range(300):
+        n = int(rng.integers(1, 11))
+        S = int(rng.integers(1, 5))
+        m = rng.dirichlet(np.ones(n + 2), size=S)[:, :n]
+        if rng.uniform() < 0.3:  # force ties
+            m = np.round(m, 2)
+        eps = float(rng.uniform(0, 0.3))
+        mass = m.mean(0)
+        order = O.discard_order(mass, list(range(n)))
+        curve, _ = O.mass_curve(m, order)
+        ks = O.cut(curve, eps)
+        best = 0
+        for kk in range(n + 1):
+            if all(max(math.fsum(m[i, b] for b in order[:j]) for i in range(S)) <= eps for j in range(1, kk + 1)):
+                best = kk
+        assert ks == best
+        if S == 1:
+            most = max(len(D) for r in range(n + 1) for D in itertools.combinations(range(n), r)
+                       if math.fsum(m[0, b] for b in D) <= eps)
+            assert ks == most
+
+
+def test_mass_cut():
+    pin_mass_cut()
+
+
+def pin_mass_selection():
+    """Mass-only selection on tiny problems, checked with scipy's softmax: the discard
+    order ascends in the tile mass (mean over sampled rows of the block masses), every
+    sampled row keeps all but at most eps of its mass, and its error obeys the worst
+    case 2 R delta of BFLA Appendix B.1 (R: the largest value norm the row sees)."""
+    for seed in range(3):
+        p, q, k, v = _tiny_problem(40 + seed)
+        for eps in (0.0, 0.001, 0.01, 0.05, 0.5):
+            sel = O.select(p, q, k, v, [eps] * p.num_heads_q, 1, 1, 8, mode="mass")
+            for (h, gt), s in sel.items():
+                t = s.tile
+                assert set(s.mandatory) <= set(s.retained) and s.retained == sorted(s.retained)
+                B = p.block_size
+                bm = []
+                for r in s.rows:
+                    pos = t.pos0 + r
+                    pr = softmax(p.scale * (k[:pos + 1, 0] @ q[t.q_row0 + r, h]))
+                    bm.append([math.fsum(pr[b * B:min((b + 1) * B, pos + 1)]) for b in range(t.diag + 1)])
+                bm = np.array(bm)
+                tm = bm.mean(0)
+                for a, b in zip(s.order, s.order[1:]):
+                    assert tm[a] <= tm[b] + 1e-12
+                od, _ = O.tile_attention(p, q, k, v, h, t)
+                os_, _ = O.tile_attention(p, q, k, v, h, t, s.retained)
+                drop = s.discarded
+                for j, r in enumerate(s.rows):
+                    delta = math.fsum(bm[j, b] for b in drop)
+                    assert delta <= eps + 1e-12
+                    R = np.linalg.norm(v[:t.pos0 + r + 1, 0], axis=1).max()
+                    assert np.linalg.norm(od[r] - os_[r]) <= 2 * R * delta * (1 + 1e-9) + 1e-15
+
+
+def test_mass_selection():
+    pin_mass_selection()
+
+
+def test_mass_nested_supports():
+    """A smaller omitted-mass budget discards a subset (BFLA Appendix B.5)."""
+    p, q, k, v = _tiny_problem(21)
+    prev = None
+    for eps in (0.9, 0.1, 0.02, 0.005, 0.0):
+        sel = O.select(p, q, k, v, [eps] * 2, 1, 1, 8, mode="mass")
+        if prev is not None:
+            for key in sel:
+                assert set(prev[key].retained) <= set(sel[key].retained)
+        prev = sel
+
+
 def test_gpu_toy_geometry_in_oracle():
     """The toy realised at block granularity (B = 64, d = 64, fp32, scale 1): blocks
     0, 1, 2, 3 with masses 1/2, 1/4, 1/4, ~0 and values 2, 0, 4, 0 along e_0; the
@@ -455,7 +539,30 @@ def _stats_transposed_mass(qr, K, V, scale, pos, n_vis, B):
 _orig_stats = O.row_block_stats
 
 
+def _mass_curve_mean_rows(m_rows, order):
+    m_rows = np.asarray(m_rows, dtype=np.float64)
+    c = np.zeros(len(order) + 1)
+    for kk in range(1, len(order) + 1):
+        c[kk] = c[kk - 1] + m_rows[:, order[kk - 1]].mean()
+    return c, np.repeat(c[:, None], m_rows.shape[0], axis=1)
+
+
+def _mass_selector_ranks_by_proxy(p, q, k, v, h, tile, eps, n_sink, n_local, S):
+    s = _orig_select_tile(p, q, k, v, h, tile, 1e9, n_sink, n_local, S)
+    order = O.discard_order(s.score, [b for b in range(tile.diag + 1) if b not in set(s.mandatory)])
+    curve, per_row = O.mass_curve(s.m, order)
+    ks = O.cut(curve, eps)
+    drop = set(order[:ks])
+    return O.TileSelection(h, tile, s.rows, s.I, s.m, s.lse, s.o, s.mass, s.mass, s.mandatory, order, curve,
+                           per_row, ks, [b for b in range(tile.diag + 1) if b not in drop])
+
+
+_orig_select_tile = O.select_tile
+
+
 @pytest.mark.parametrize("name,fn,pins", [
+    ("mass_curve", _mass_curve_mean_rows, ["mass_cut"]),
+    ("select_tile_mass", _mass_selector_ranks_by_proxy, ["mass_selection"]),
     ("deleted_output", _deleted_no_renorm, ["toy_pairs"]),
     ("deletion_error", _identity_wrong_sign, ["toy_pairs", "identity"]),
     ("triangle_bound", _bound_no_denominator, ["toy_pairs", "singleton"]),
@@ -474,6 +581,8 @@ def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
         "threshold": pin_threshold_bruteforce,
         "attention": pin_attention_bruteforce,
         "row_stats": pin_row_stats_invariants,
+        "mass_cut": pin_mass_cut,
+        "mass_selection": pin_mass_selection,
     }
     monkeypatch.setattr(O, name, fn)
     for pin in pins:
