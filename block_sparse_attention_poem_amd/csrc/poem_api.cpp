@@ -185,10 +185,11 @@ int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_pe
   return (int64_t)sel_layout(problem, g, rows_per_tile).total;
 }
 
-poem_status poem_select(const poem_problem* problem, const void* q, const void* k, const void* v,
-                        const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks, int32_t rows_per_tile,
-                        int32_t* row_ptr, int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
-                        float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes, void* stream) {
+static poem_status select_impl(int mode, const poem_problem* problem, const void* q, const void* k, const void* v,
+                               const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                               int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                               int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
+                               void* workspace, size_t workspace_bytes, void* stream) {
   Geometry g;
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
@@ -232,6 +233,7 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
   sp.n_sink = n_sink_blocks;
   sp.n_local = n_local_blocks;
   sp.max_vis = (int32_t)g.max_vis;
+  sp.mode = mode;
   sp.scale_log2 = g.scale * poem::kLog2e;
   for (int h = 0; h < problem->num_heads_q; ++h) sp.tau[h] = tau_host[h];
   char* ws = static_cast<char*>(workspace);
@@ -248,6 +250,25 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
   return hip_status(poem::launch_select(sp, problem->in_dtype, problem->head_dim, problem->block_size,
                                         static_cast<hipStream_t>(stream)),
                     "poem_select launch");
+}
+
+poem_status poem_select(const poem_problem* problem, const void* q, const void* k, const void* v,
+                        const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks, int32_t rows_per_tile,
+                        int32_t* row_ptr, int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
+                        float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(poem::kSelectOutputRelative, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
+                     rows_per_tile, row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound,
+                     workspace, workspace_bytes, stream);
+}
+
+poem_status poem_select_mass(const poem_problem* problem, const void* q, const void* k, const void* v,
+                             const float* eps_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                             int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                             int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(poem::kSelectMass, problem, q, k, v, eps_host, n_sink_blocks, n_local_blocks, rows_per_tile,
+                     row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound, workspace,
+                     workspace_bytes, stream);
 }
 
 static size_t sparse_ws_bytes(const poem_problem* p, const Geometry& g) {

@@ -465,19 +465,24 @@ __device__ __forceinline__ void wait_vmem_all() { __builtin_amdgcn_s_waitcnt(0x0
 // in buf1 for odd it (two distinct LDS objects, so the compiler sees that reading one
 // never waits on the loads filling the other). body(it, lds) computes on stage it
 // while stage it+1 is being fetched; one barrier per stage.
-template <typename St, typename T, typename KeyFn, typename Body>
+// With KONLY (a consumer that never reads V) bf16 stages load K alone.
+template <typename St, bool KONLY = false, typename T, typename KeyFn, typename Body>
 __device__ __forceinline__ void sweep(int total, KeyFn key0_of, const T* kbase, const T* vbase, int64_t row_stride,
                                       int n_valid, int tid, char* buf0, char* buf1, Body&& body) {
   typename St::Regs regs;
+  auto fetch = [&](int it, char* dst) {
+    if constexpr (KONLY && St::ASYNC) St::load_k(kbase, row_stride, key0_of(it), n_valid, tid, dst);
+    else St::load(regs, kbase, vbase, row_stride, key0_of(it), n_valid, tid, dst);
+  };
   if (total > 0) {
-    St::load(regs, kbase, vbase, row_stride, key0_of(0), n_valid, tid, buf0);
+    fetch(0, buf0);
     St::store(regs, buf0, tid);
   }
   wait_vmem_all();
   __syncthreads();
   auto one = [&](int it, char* cur, char* nxt) {
     const bool more = it + 1 < total;
-    if (more) St::load(regs, kbase, vbase, row_stride, key0_of(it + 1), n_valid, tid, nxt);
+    if (more) fetch(it + 1, nxt);
     body(it, static_cast<const char*>(cur));
     if (more) St::store(regs, nxt, tid);
     if constexpr (St::ASYNC) wait_vmem_all();

@@ -33,6 +33,11 @@ struct AttnParams {
 hipError_t launch_attention(const AttnParams& p, int in_dtype, int head_dim, int block, bool sparse,
                             hipStream_t stream);
 
+// Selector modes: the output-relative score (ranking by mean I, cut on the triangle
+// bound) and the mass-only baseline (ranking by mean m, cut on omitted mass).
+constexpr int kSelectOutputRelative = 0;
+constexpr int kSelectMass = 1;
+
 struct SelectParams {
   const void* q;
   const void* k;
@@ -42,6 +47,7 @@ struct SelectParams {
   int32_t col_tiles;         // 32-column tiles per (KV head, tile)
   int32_t n_sink, n_local;
   int32_t max_vis;
+  int32_t mode;              // kSelectOutputRelative or kSelectMass
   float scale_log2;
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions

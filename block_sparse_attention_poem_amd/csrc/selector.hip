@@ -33,7 +33,9 @@ namespace poem {
 constexpr int kSelThreads = 256;
 constexpr int kSelWaves = 4;
 
-template <typename T, int D, int BLK, bool PASS2>
+// MASS: the mass-only selector needs neither o nor U_b, so both passes skip P V and
+// stage K alone.
+template <typename T, int D, int BLK, bool PASS2, bool MASS>
 __global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void sel_sweep_kernel(SelectParams p) {
   using St = Stage<T, D, kSelThreads>;
@@ -98,6 +100,8 @@ void sel_sweep_kernel(SelectParams p) {
       m2 = rs_col[0];
       inv_l = 1.f / rs_col[1];
     }
+  }
+  if constexpr (PASS2 && !MASS) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -120,7 +124,7 @@ void sel_sweep_kernel(SelectParams p) {
   wait_vmem_all();
   const int total = nblk_wg * SUBS;
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
-  sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
+  sweep<St, MASS>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
     const int blk = it / SUBS, sub = it % SUBS;
     const int key0 = stage_key0(it);
     if (PASS2 && sub == 0) {
@@ -158,7 +162,7 @@ void sel_sweep_kernel(SelectParams p) {
           }
         l_run = l_run * alpha + rs;
         m_run = m_new;
-        if (__any(alpha != 1.f)) {
+        if (!MASS && __any(alpha != 1.f)) {
 #pragma unroll
           for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
         }
@@ -174,23 +178,25 @@ void sel_sweep_kernel(SelectParams p) {
             mloc += e;
           }
       }
-      St::template pv<SPLIT>(cur, S, O, lane);
+      if constexpr (!MASS) St::template pv<SPLIT>(cur, S, O, lane);
     }
     if constexpr (PASS2) {
       if (sub == SUBS - 1 && wave_on && blk <= diag) {
         const float mt = mloc + wave_xor32(mloc);
         float ss = 0.f;
+        if constexpr (!MASS) {
 #pragma unroll
-        for (int dt = 0; dt < D / 32; ++dt)
+          for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float dv = __builtin_fmaf(-mt, Od[dt][r], O[dt][r]);
-            ss = __builtin_fmaf(dv, dv, ss);
-          }
-        ss += wave_xor32(ss);
+            for (int r = 0; r < 16; ++r) {
+              const float dv = __builtin_fmaf(-mt, Od[dt][r], O[dt][r]);
+              ss = __builtin_fmaf(dv, dv, ss);
+            }
+          ss += wave_xor32(ss);
+        }
         if (col_on && g2 == 0) {
           float* dst = blk_I + (int64_t)blk * (2 * 32 * CT);
-          dst[0] = __builtin_sqrtf(ss) * inv_l;
+          if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * inv_l;
           dst[32 * CT] = mt * inv_l;
         }
       }
@@ -205,24 +211,35 @@ void sel_sweep_kernel(SelectParams p) {
         rs_col[0] = m_run;
         rs_col[1] = l_tot;
       }
+      if constexpr (!MASS) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int a = 0; a < 4; ++a) {
-          f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv};
-          *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2) = o;
-        }
+          for (int a = 0; a < 4; ++a) {
+            f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv};
+            *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2) = o;
+          }
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Threshold, ranking and compaction: one workgroup per (query head, tile).
+//
+// The G query heads of one (KV head, tile) read disjoint S-float slices of the same
+// per-block records. The grid puts those G workgroups on one XCD (workgroup ids are
+// dealt round-robin over the XCDs) and next to each other in time, so one L2 fetch
+// of a record line serves the whole group. STAGED: a head's per-row values are read
+// once, coalesced, into LDS and both walks of the discard order run on LDS; without
+// it (tiles too long for LDS) the walks gather the rows from the workspace.
 // ---------------------------------------------------------------------------
 
 constexpr int kThrThreads = 256;
 constexpr int kMaxVis = 4096;
-
+constexpr int kStageVis = 1024;   // STAGED: visible blocks per tile
+constexpr int kStageVals = 8192;  // STAGED: visible blocks x sampled rows
+constexpr int kXcds = 8;
 
 // Exclusive prefix over the workgroup, in thread order, of N pairs of doubles (each
 // thread's A[r], D[r] are replaced by the sums over lower threads). sh: 8 * N doubles.
@@ -270,15 +287,27 @@ __device__ __forceinline__ int block_min_int(int v, int* sh) {
   return r;
 }
 
+// MODE kSelectOutputRelative: key = mean_i I_ib, bound = max_i A_i(k) / (1 - Delta_i(k));
+// MODE kSelectMass: key = mean_i m_ib, bound = max_i Delta_i(k).
+template <int MODE, bool STAGED>
 __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
-  __shared__ uint64_t keys[kMaxVis];
-  __shared__ uint8_t keep[kMaxVis];
+  constexpr bool POEM = MODE == kSelectOutputRelative;
+  constexpr int NK = STAGED ? kStageVis : kMaxVis;
+  __shared__ uint64_t keys[NK];
+  __shared__ uint8_t keep[NK];
+  __shared__ float st_I[STAGED && POEM ? kStageVals : 1];
+  __shared__ float st_m[STAGED ? kStageVals : 1];
   __shared__ double shd[8 * kRowChunk];
   __shared__ int shi[8];
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
-  // heads of one tile are adjacent in the grid: they read the same workspace lines
-  const int gtile = blockIdx.x / p.hq, h = blockIdx.x % p.hq;
+  const int G = p.group;
+  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int hg = rest % G;
+  const int unit = (rest / G) * kXcds + xcd;  // gtile * hkv + KV head
+  if (unit >= T * p.hkv) return;
+  const int gtile = unit / p.hkv, gk = unit % p.hkv;
+  const int h = gk * G + hg;
   const int R = h * T + gtile;  // CSR row
   const int seq = find_seq(p.seqs, gtile);
   const int t = gtile - p.seqs.tile_start[seq];
@@ -291,9 +320,8 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int64_t slot = (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
   const int cols = 32 * p.col_tiles;
   const int64_t bstride = 2 * cols;  // floats per visible block
-  // row i of this head is column (h % G) * S + i of its KV head's tile record
-  const float* Ib = p.blk_stats + ((int64_t)(h / p.group) * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) *
-                                      bstride + (h % p.group) * S;
+  // row i of this head is column hg * S + i of its KV head's tile record
+  const float* Ib = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * bstride + hg * S;
   const float* Mb = Ib + cols;
   const float tau = p.tau[h];
   int n_pad = 2;
@@ -314,21 +342,26 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
       const int b = b0 + u * per_pass + tid / sp;
       si[u] = sm[u] = 0.f;
       if (b < n_vis && ri < s_t) {
-        si[u] = Ib[(int64_t)b * bstride + ri];
+        if constexpr (POEM) si[u] = Ib[(int64_t)b * bstride + ri];
         sm[u] = Mb[(int64_t)b * bstride + ri];
+        if constexpr (STAGED) {
+          if constexpr (POEM) st_I[b * S + ri] = si[u];
+          st_m[b * S + ri] = sm[u];
+        }
       }
     }
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       for (int o = sp >> 1; o > 0; o >>= 1) {
-        si[u] += __shfl_xor(si[u], o);
+        if constexpr (POEM) si[u] += __shfl_xor(si[u], o);
         sm[u] += __shfl_xor(sm[u], o);
       }
       const int b = b0 + u * per_pass + tid / sp;
       if (ri == 0 && b < n_pad) {
         uint64_t key = ~0ull;
         if (b < n_vis) {
-          const float score = si[u] * inv_s, mass = sm[u] * inv_s;
+          const float mass = sm[u] * inv_s;
+          const float score = POEM ? si[u] * inv_s : mass;
           if (p.tile_scores) p.tile_scores[diag_row + b] = score;
           if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
           if (!mandatory(b)) key = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
@@ -363,12 +396,24 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int n_cand = n_vis - n_mand;
   const int E = n_pad >= kThrThreads ? n_pad / kThrThreads : 1;
   auto id_at = [&](int k) { return (int)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull)); };
+  // sampled row i of block b
+  auto I_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_I[b * S + i];
+    else return Ib[(int64_t)b * bstride + i];
+  };
+  auto m_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_m[b * S + i];
+    else return Mb[(int64_t)b * bstride + i];
+  };
+  auto bound_of = [&](double a, double dl) -> double {
+    if constexpr (POEM) return (1.0 - dl > 0.0) ? a / (1.0 - dl) : INFINITY;
+    else return dl;
+  };
 
-  // Prefix sums over the discard order, all sampled rows at once: each thread walks
-  // its E consecutive positions reading the whole row record of each block (rows of a
-  // chunk are contiguous), a vector scan gives each thread its exclusive prefixes, and
-  // the first prefix length whose per-row bound exceeds tau is a block minimum.
-  // With `limit` = the cut, the same walk yields the per-row bound at the cut.
+  // Prefix sums over the discard order, kRowChunk sampled rows at a time: each thread
+  // walks its E consecutive positions, a vector scan gives each thread its exclusive
+  // prefixes, and the first prefix length whose per-row bound exceeds tau is a block
+  // minimum. With `limit` = the cut, the same walk yields the per-row bound at the cut.
   auto walk = [&](int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
     double A[kRowChunk], Dl[kRowChunk];
 #pragma unroll
@@ -376,24 +421,27 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
     for (int e = 0; e < E; ++e) {
       const int k = tid * E + e;
       if (k < limit) {
-        const float* ip = Ib + (int64_t)id_at(k) * bstride + i0;
+        const int b = id_at(k);
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
-          if (r < nr) { A[r] += (double)ip[r]; Dl[r] += (double)ip[cols + r]; }
+          if (r < nr) {
+            if constexpr (POEM) A[r] += (double)I_of(b, i0 + r);
+            Dl[r] += (double)m_of(b, i0 + r);
+          }
       }
     }
     block_excl_scan_vec<kRowChunk>(A, Dl, shd);
     for (int e = 0; e < E; ++e) {
       const int k = tid * E + e;
       if (k < limit) {
-        const float* ip = Ib + (int64_t)id_at(k) * bstride + i0;
+        const int b = id_at(k);
         bool over = false;
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
           if (r < nr) {
-            A[r] += (double)ip[r];
-            Dl[r] += (double)ip[cols + r];
-            const double bound = (1.0 - Dl[r] > 0.0) ? A[r] / (1.0 - Dl[r]) : INFINITY;
+            if constexpr (POEM) A[r] += (double)I_of(b, i0 + r);
+            Dl[r] += (double)m_of(b, i0 + r);
+            const double bound = bound_of(A[r], Dl[r]);
             over |= bound > (double)tau;
             if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
           }
@@ -489,9 +537,28 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((int64_t)items * p.hkv);
-  hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
-  hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
-  hipLaunchKernelGGL(sel_threshold_kernel, dim3((unsigned)rows), dim3(kThrThreads), 0, s, p);
+  const bool mass = p.mode == kSelectMass;
+  if (mass) {
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
+  } else {
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+  }
+  // threshold grid: (KV-head unit, head in group) with the unit's XCD kept fixed
+  const int64_t units = (int64_t)p.seqs.total_tiles * p.hkv;
+  const unsigned tgrid = (unsigned)(((units + kXcds - 1) / kXcds) * kXcds * p.group);
+  const bool staged = p.max_vis <= kStageVis && (int64_t)p.max_vis * p.S <= kStageVals;
+  if (mass) {
+    if (staged) hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+    else hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+  } else {
+    if (staged)
+      hipLaunchKernelGGL((sel_threshold_kernel<kSelectOutputRelative, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((sel_threshold_kernel<kSelectOutputRelative, false>), dim3(tgrid), dim3(kThrThreads), 0, s,
+                         p);
+  }
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.row_ptr, (int)rows);
   hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)rows), dim3(64), 0, s, p);
   return hipGetLastError();

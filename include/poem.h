@@ -134,6 +134,32 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
                         float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
 
+/*
+ * poem_select_mass: the mass-only selector, the baseline the POEM note compares the
+ * output-relative score against (its evaluation summary: mass-only baseline at 128K).
+ *
+ * Same sampled rows, per-row block masses m_ib, mandatory set, tie rule and CSR
+ * output as poem_select. The ranking key is the tile mass mbar_b = mean_i m_ib
+ * (discard order: ascending mbar_b, larger id first among equal masses). With
+ * Delta_i(k) the mass of row i over the first k blocks of that order, the cut k*
+ * is the largest k with max_i Delta_i(k') <= eps_host[h] for all k' <= k: every
+ * sampled row keeps all but at most eps of its dense attention mass, which bounds
+ * its output error by 2 R eps for values of norm <= R (BFLA Appendix B.1). The
+ * pages fix no mass threshold; eps is a parameter.
+ *
+ * Arguments as for poem_select, except:
+ *   eps_host     host [H_q]: per-head omitted-mass budget, finite and >= 0.
+ *   tile_scores  nullable: receives the ranking key mbar_b (-1 beyond T_t).
+ *   row_bound    nullable: the per-row omitted mass Delta_i(k*) at the cut.
+ * Neither pass computes P V (no o, u or I), and both stream K only. The workspace
+ * size is poem_select_workspace_bytes(). Errors as for poem_select.
+ */
+poem_status poem_select_mass(const poem_problem* problem, const void* q, const void* k, const void* v,
+                             const float* eps_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                             int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                             int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
+                             float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
+
 /* Bytes of the optional device workspace poem_sparse_prefill uses to schedule its rows
  * (a queue head and one int32 per CSR row); < 0 on error. */
 int64_t poem_sparse_workspace_bytes(const poem_problem* problem);

@@ -248,17 +248,23 @@ SEL = [
 ]
 
 
-def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_sparse=None):
-    """Scores, masks (with exemptions) and the bound theorem on the (h, gtile) pairs in which."""
+def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_sparse=None, mode="poem", taus=None):
+    """Scores, masks (with exemptions) and the bound theorem on the (h, gtile) pairs in which.
+
+    mode "poem": the triangle bound at the cut is <= tau and bounds each sampled row's
+    error. mode "mass" (taus: omitted-mass budgets): each sampled row's omitted mass
+    on the GPU's mask is <= eps, matches the reported row value, and its error is at
+    most 2 R delta (BFLA Appendix B.1)."""
     T = L.num_tiles(gp)
+    taus = inp.tau if taus is None else taus
     rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
     scores = r["tile_scores"].cpu().numpy()
     bounds = r["row_bound"].cpu().numpy()
-    sels = O.select(op, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which)
+    sels = O.select(op, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which, mode=mode)
     n_cand = n_match = 0
     worst_score = 0.0
     for (h, gt), sel in sels.items():
-        tau = float(inp.tau[h])
+        tau = float(taus[h])
         n_vis = sel.tile.diag + 1
         se, sm, info = H.score_errors(sel, scores[h, gt], tau)
         worst_score = max(worst_score, se)
@@ -276,11 +282,19 @@ def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_spars
         t = sel.tile
         od, _ = O.tile_attention(op, q, k, v, h, t)
         osp, _ = O.tile_attention(op, q, k, v, h, t, kept)
+        dropped = [b for b in range(t.diag + 1) if b not in set(kept)]
         for j, row in enumerate(sel.rows):
             err = float(np.linalg.norm(od[row] - osp[row]))
             b = float(bounds[h, gt, j])
             assert b <= tau * (1 + 1e-6), (h, gt, j, b, tau)
-            assert err <= b * (1 + 1e-3) + 1e-6, (h, gt, j, err, b)
+            if mode == "mass":
+                delta = float(sel.m[j, dropped].sum())
+                assert abs(b - delta) <= H.NEAR_REL * max(delta, tau / (t.diag + 1)), (h, gt, j, b, delta)
+                R = float(np.linalg.norm(v[t.k_row0:t.k_row0 + t.pos0 + row + 1, h // op.group], axis=1).max())
+                assert err <= 2 * R * delta * (1 + 1e-9) + 1e-12, (h, gt, j, err, delta, R)
+                b = 2 * R * delta
+            else:
+                assert err <= b * (1 + 1e-3) + 1e-6, (h, gt, j, err, b)
             if gpu_dense is not None:
                 ge = float(np.linalg.norm(gpu_dense[t.q_row0 + row, h].astype(np.float64) -
                                           gpu_sparse[t.q_row0 + row, h].astype(np.float64)))
@@ -304,6 +318,40 @@ def test_selector_matches_oracle(case, sink, n_local):
     which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
     nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy())
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
+MASS = [
+    # case, sink_offset, n_local, eps (omitted-mass budget)
+    ((300, 428, 4, 1, 64, 64, "bf16", 1), 6.0, 1, 0.002),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 6.0, 1, 0.004),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), 5.0, 2, 0.02),
+    ((300, 428, 2, 1, 64, 64, "fp32", 1), 6.0, 1, 0.002),
+    ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1, 0.003),
+    ((64, 4160, 2, 1, 64, 64, "bf16", 1), 7.0, 1, 0.001),
+]
+
+
+@pytest.mark.parametrize("case,sink,n_local,eps", MASS, ids=lambda x: str(x))
+def test_mass_selector_matches_oracle(case, sink, n_local, eps):
+    """poem_select_mass against the oracle's mass-only selector."""
+    w = _small(case, seed=7).with_(sink_offset=sink, n_local_blocks=n_local)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    eps_h = [eps * (1 + 0.5 * (h % 3)) for h in range(w.num_heads_q)]
+    say("mass selector", case, sink, n_local, eps)
+    r = L.select(gp, qd, kd, vd, eps_h, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="mass")
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    # the ranking key the GPU reports is the tile mass, in both score outputs
+    assert np.array_equal(r["tile_scores"].cpu().numpy(), r["tile_mass"].cpu().numpy())
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy(),
+                                 mode="mass", taus=eps_h)
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst mass rel err", ws)
 
 
 # ---------------------------------------------------------------------------
@@ -373,3 +421,33 @@ def test_workload_full_size_sampled(wid):
         assert np.abs(so[r0:r0 + n, h] - Os).max() <= H.OUT_ATOL_BF16
         assert H.lse_close(dl[h, r0:r0 + n], ld, H.LSE_ATOL_BF16)
         assert H.lse_close(sl[h, r0:r0 + n], ls, H.LSE_ATOL_BF16)
+
+
+def test_mass_full_size_sampled():
+    """poem_select_mass at the 128K layer's full size; oracle on stratified tiles."""
+    import torch
+    w = synth.WORKLOADS[3]
+    say("workload 3 mass-only: generate")
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    eps_h = [0.002] * w.num_heads_q
+    say("workload 3 mass-only: select + sparse")
+    r = L.select(gp, qd, kd, vd, eps_h, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="mass")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    say("  keep fraction", len(bi[:rp[-1]]) / L.csr_capacity(gp))
+    so = s_out.cpu().numpy()
+    del s_out
+    torch.cuda.empty_cache()
+    q, k, v = H.f64(inp)
+    which = H.stratified_tiles(op, [0, w.num_heads_q - 1], per_head=3, seed=33)
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, mode="mass", taus=eps_h)
+    say("  sampled candidates", nc, "agreement", nm / max(nc, 1), "worst mass rel err", ws)
+    T = L.num_tiles(gp)
+    for (h, gt) in which[:4]:
+        t = O.tiles(op)[gt]
+        Os, _ = O.tile_attention(op, q, k, v, h, t, H.retained(rp, bi, h * T + gt))
+        assert np.abs(so[t.q_row0:t.q_row0 + t.n_rows, h] - Os).max() <= H.OUT_ATOL_BF16
