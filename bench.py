@@ -149,6 +149,103 @@ def cpu_baseline(w, inp, gp, rp, bi, seconds):
             "seconds": el, "host_cpus": len(os.sched_getaffinity(0))}
 
 
+def sampled_row_index(gp, S):
+    """Packed query-row indices of every tile's sampled rows (even stride ending at the
+    tile's last row) and the tile each belongs to."""
+    rows, tiles = [], []
+    B = gp.block_size
+    g = 0
+    q0 = 0
+    for nq in gp.seqlens_q:
+        for t in range(-(-nq // B)):
+            n = min(B, nq - t * B)
+            st = min(S, n)
+            for j in range(st):
+                rows.append(q0 + t * B + (-(-((j + 1) * n) // st)) - 1)
+                tiles.append(g)
+            g += 1
+        q0 += nq
+    return np.array(rows, np.int64), np.array(tiles, np.int64)
+
+
+def mass_only_leg(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
+    """The mass-only selector beside POEM: its latency at a fixed budget, then POEM and
+    mass-only at matched per-head keep fraction (the mass budget of each head bisected
+    until its kept-block count matches POEM's) and the output errors of both against
+    dense attention, over every query row and over the sampled rows."""
+    import torch
+    H = w.num_heads_q
+    T = L.num_tiles(gp)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
+    eps0 = [args.mass_eps] * H
+    r = None
+    for i in range(steps):
+        ev[i][0].record()
+        r = L.select(gp, q, k, v, eps0, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
+                     mode="mass")
+        ev[i][1].record()
+        L.sparse_prefill(gp, q, k, v, r["row_ptr"], r["block_idx"], out_dtype="bf16", want_lse=False,
+                         workspace=sws)
+        ev[i][2].record()
+    torch.cuda.synchronize()
+    t_sel = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
+    t_sp = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]))
+    cap = L.csr_capacity(gp)
+    kept0 = int(r["row_ptr"][-1].item())
+
+    vis = (np.diff(rp_poem).reshape(H, T).sum(1))  # POEM kept blocks per head
+    lo = np.full(H, -9.0)
+    hi = np.zeros(H)
+    best = [None] * H
+    for _ in range(24):
+        mid = 0.5 * (lo + hi)
+        rr = L.select(gp, q, k, v, list(10.0 ** mid), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
+                      workspace=ws, mode="mass")
+        kept = np.diff(rr["row_ptr"].cpu().numpy().astype(np.int64)).reshape(H, T).sum(1)
+        for h in range(H):
+            gap = abs(int(kept[h]) - int(vis[h]))
+            if best[h] is None or gap < best[h][0]:
+                best[h] = (gap, float(10.0 ** mid[h]))
+        more = kept > vis  # keeps too much: raise the budget
+        lo = np.where(more, mid, lo)
+        hi = np.where(more, hi, mid)
+    eps_m = [b[1] for b in best]
+    rm = L.select(gp, q, k, v, eps_m, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
+                  mode="mass")
+    rpm = rm["row_ptr"].cpu().numpy().astype(np.int64)
+    rp_t = torch.from_numpy(rp_poem.astype(np.int32)).cuda()
+    # POEM's CSR is reproduced by re-running its selector with the bench's thresholds
+    rpo = L.select(gp, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws)
+    assert torch.equal(rpo["row_ptr"], rp_t)
+    od, _ = L.dense_prefill(gp, q, k, v, out_dtype="fp32", want_lse=False)
+    op_, _ = L.sparse_prefill(gp, q, k, v, rpo["row_ptr"], rpo["block_idx"], out_dtype="fp32", want_lse=False,
+                              workspace=sws)
+    om, _ = L.sparse_prefill(gp, q, k, v, rm["row_ptr"], rm["block_idx"], out_dtype="fp32", want_lse=False,
+                             workspace=sws)
+    e_p = torch.linalg.vector_norm(op_ - od, dim=-1)  # [rows, H]
+    e_m = torch.linalg.vector_norm(om - od, dim=-1)
+    del od, op_, om
+    srow, stile = sampled_row_index(gp, w.rows_per_tile)
+    tau = torch.tensor([float(x) for x in inp.tau], device=e_p.device)
+    si = torch.from_numpy(srow).cuda()
+
+    def stats(e):
+        f = e.flatten()
+        return {"mean": float(f.mean()), "rms": float(torch.sqrt((f * f).mean())),
+                "p99": float(torch.quantile(f[torch.randperm(f.numel(), device=f.device)[:1 << 22]], 0.99)),
+                "max": float(f.max()),
+                "sampled_rows_within_tau": float((e[si] <= tau[None, :]).float().mean())}
+
+    res = {"eps": args.mass_eps, "select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": kept0 / cap,
+           "matched_keep": {
+               "keep_fraction_blocks_poem": float(rp_poem[-1]) / cap, "keep_fraction_blocks_mass": float(rpm[-1]) / cap,
+               "eps_per_head": [float("%.4g" % e) for e in eps_m],
+               "err_poem": stats(e_p), "err_mass": stats(e_m),
+               "note": "row error = ||O_sparse - O_dense||_2 over all query rows (fp32 outputs); "
+                       "sampled_rows_within_tau = share of the selector's sampled rows with error <= tau_h"}}
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -159,6 +256,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-mass", action="store_true", help="skip the mass-only selector leg")
+    ap.add_argument("--mass-eps", type=float, default=0.002, help="omitted-mass budget of the mass-only leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -274,10 +373,14 @@ def main():
     sel_ms, sp_ms = float(np.median(t_sel)), float(np.median(t_sp))
     value = flop_ret / ((sel_ms + sp_ms) * 1e-3) / 1e12
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_FP32_TFLOPS
-    # dominant kernel of the step: the sparse attention kernel (one launch) or the selector
+    # dominant kernel of the step: the sparse attention kernel (one launch per step);
+    # its achieved rate uses the average launch duration over the timed steps
     attn_tflops = flop_ret / (sp_ms * 1e-3) / 1e12
-    roofline = {"kernel": "attn_sparse_persistent_kernel", "bound": "mfma", "achieved": attn_tflops, "peak": peak,
-                "unit": "TFLOP/s", "frac": attn_tflops / peak, "traffic": measured_traffic(args.workload),
+    attn_tflops_avg = flop_ret / (float(t_sp.mean()) * 1e-3) / 1e12
+    roofline = {"kernel": "attn_sparse_persistent_kernel", "bound": "mfma", "achieved": attn_tflops_avg,
+                "peak": peak,
+                "unit": "TFLOP/s", "frac": attn_tflops_avg / peak, "avg_launch_ms": float(t_sp.mean()),
+                "traffic": measured_traffic(args.workload),
                 "algorithmic": f"4 d P_R = {flop_ret:.4e} FLOP per launch",
                 "algorithmic_bytes": unique_bytes(gp, rp, bi, q.element_size(),
                                                   out.element_size())}
@@ -303,6 +406,9 @@ def main():
         "keep_fraction_pairs": p_ret / p_dense,
         "roofline": roofline,
     }
+    if not args.no_mass and inp.is_bf16:
+        log("[bench] mass-only selector leg")
+        res["mass_only"] = mass_only_leg(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds)

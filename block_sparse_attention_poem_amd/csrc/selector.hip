@@ -287,162 +287,161 @@ __device__ __forceinline__ int block_min_int(int v, int* sh) {
   return r;
 }
 
-// MODE kSelectOutputRelative: key = mean_i I_ib, bound = max_i A_i(k) / (1 - Delta_i(k));
-// MODE kSelectMass: key = mean_i m_ib, bound = max_i Delta_i(k).
-template <int MODE, bool STAGED>
-__global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
-  constexpr bool POEM = MODE == kSelectOutputRelative;
-  constexpr int NK = STAGED ? kStageVis : kMaxVis;
-  __shared__ uint64_t keys[NK];
-  __shared__ uint8_t keep[NK];
-  __shared__ float st_I[STAGED && POEM ? kStageVals : 1];
-  __shared__ float st_m[STAGED ? kStageVals : 1];
-  __shared__ double shd[8 * kRowChunk];
-  __shared__ int shi[8];
-  const int tid = threadIdx.x;
-  const int T = p.seqs.total_tiles;
-  const int G = p.group;
-  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
-  const int hg = rest % G;
-  const int unit = (rest / G) * kXcds + xcd;  // gtile * hkv + KV head
-  if (unit >= T * p.hkv) return;
-  const int gtile = unit / p.hkv, gk = unit % p.hkv;
-  const int h = gk * G + hg;
-  const int R = h * T + gtile;  // CSR row
-  const int seq = find_seq(p.seqs, gtile);
-  const int t = gtile - p.seqs.tile_start[seq];
-  const int B = p.seqs.block;
-  const int diag = p.seqs.diag0[seq] + t;
-  const int n_vis = diag + 1;
-  const int n_rows_t = min(B, p.seqs.n_q[seq] - t * B);
-  const int s_t = min(p.S, n_rows_t);
-  const int S = p.S;
-  const int64_t slot = (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
-  const int cols = 32 * p.col_tiles;
-  const int64_t bstride = 2 * cols;  // floats per visible block
-  // row i of this head is column hg * S + i of its KV head's tile record
-  const float* Ib = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * bstride + hg * S;
-  const float* Mb = Ib + cols;
-  const float tau = p.tau[h];
-  int n_pad = 2;
-  while (n_pad < n_vis) n_pad <<= 1;
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t x, int m) {
+  const uint32_t lo = __shfl_xor((uint32_t)x, m), hi = __shfl_xor((uint32_t)(x >> 32), m);
+  return ((uint64_t)hi << 32) | lo;
+}
 
-  auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
-  const float inv_s = 1.f / (float)s_t;
-  const int64_t diag_row = ((int64_t)h * T + gtile) * p.max_vis;
-  // scores: sp lanes per block read its s_t contiguous values and sum them by shuffles
-  int sp = 1;
-  while (sp < s_t) sp <<= 1;
-  const int per_pass = kThrThreads / sp, ri = tid % sp;
-  constexpr int U = 4;  // passes whose loads are issued together
-  for (int b0 = 0; b0 < n_pad; b0 += U * per_pass) {
-    float si[U], sm[U];
+// Ascending bitonic sort of 256 * E keys held in blocked order (thread tid holds
+// positions tid * E .. tid * E + E - 1). Partners in the same thread are swapped in
+// registers, partners in the same wave by shuffles, and only the stages whose
+// partners sit in other waves go through LDS (sh: 256 * E keys).
+template <int E>
+__device__ __forceinline__ void sort_blocked(uint64_t (&x)[E], uint64_t* sh) {
+  constexpr int N = kThrThreads * E;
+  const int tid = threadIdx.x, lane = tid & 63;
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      const int b = b0 + u * per_pass + tid / sp;
-      si[u] = sm[u] = 0.f;
-      if (b < n_vis && ri < s_t) {
-        if constexpr (POEM) si[u] = Ib[(int64_t)b * bstride + ri];
-        sm[u] = Mb[(int64_t)b * bstride + ri];
-        if constexpr (STAGED) {
-          if constexpr (POEM) st_I[b * S + ri] = si[u];
-          st_m[b * S + ri] = sm[u];
+  for (int k = 2; k <= N; k <<= 1) {
+#pragma unroll
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      if (j < E) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int ep = e ^ j;
+          if (ep > e) {
+            const bool up = ((tid * E + e) & k) == 0;
+            const uint64_t a = x[e], b = x[ep];
+            if ((a > b) == up) { x[e] = b; x[ep] = a; }
+          }
+        }
+      } else if (j < 64 * E) {
+        const int lj = j / E;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const uint64_t o = shfl_xor_u64(x[e], lj);
+          const bool up = ((tid * E + e) & k) == 0;
+          const bool keep_min = ((lane & lj) == 0) == up;
+          x[e] = keep_min ? (x[e] < o ? x[e] : o) : (x[e] < o ? o : x[e]);
+        }
+      } else {
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) sh[tid * E + e] = x[e];
+        __syncthreads();
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const int i = tid * E + e;
+          const uint64_t o = sh[i ^ j];
+          const bool keep_min = ((i & j) == 0) == ((i & k) == 0);
+          x[e] = keep_min ? (x[e] < o ? x[e] : o) : (x[e] < o ? o : x[e]);
         }
       }
     }
+  }
+}
+
+// One (query head, tile) of the threshold kernel after staging: scores, sort, cut,
+// row bounds and compaction, with E = padded candidates / 256 keys per thread.
+struct ThrTile {
+  int h, gtile, R, S, s_t, n_vis, diag;
+  int64_t slot, bstride;
+  const float* Ib;  // this head's slice of the per-block records (global)
+  const float* Mb;
+  float tau;
+};
+
+// MODE kSelectOutputRelative: key = mean_i I_ib, bound = max_i A_i(k) / (1 - Delta_i(k));
+// MODE kSelectMass: key = mean_i m_ib, bound = max_i Delta_i(k).
+template <int MODE, bool STAGED, int E>
+__device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrTile& w, const float* st_I,
+                                               const float* st_m, uint64_t* sh, uint8_t* keep, double* shd,
+                                               int* shi) {
+  constexpr bool POEM = MODE == kSelectOutputRelative;
+  const int tid = threadIdx.x;
+  const int T = p.seqs.total_tiles;
+  const int S = w.S, s_t = w.s_t, n_vis = w.n_vis, diag = w.diag;
+  auto I_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_I[b * S + i];
+    else return w.Ib[(int64_t)b * w.bstride + i];
+  };
+  auto m_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_m[b * S + i];
+    else return w.Mb[(int64_t)b * w.bstride + i];
+  };
+  auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
+  const float inv_s = 1.f / (float)s_t;
+  const int64_t diag_row = ((int64_t)w.h * T + w.gtile) * p.max_vis;
+
+  // scores of this thread's blocks tid * E + e, as sort keys (score bits, ~id)
+  uint64_t x[E];
 #pragma unroll
-    for (int u = 0; u < U; ++u) {
-      for (int o = sp >> 1; o > 0; o >>= 1) {
-        if constexpr (POEM) si[u] += __shfl_xor(si[u], o);
-        sm[u] += __shfl_xor(sm[u], o);
+  for (int e = 0; e < E; ++e) {
+    const int b = tid * E + e;
+    x[e] = ~0ull;
+    if (b < n_vis) {
+      float si = 0.f, sm = 0.f;
+      for (int i = 0; i < s_t; ++i) {
+        if constexpr (POEM) si += I_of(b, i);
+        sm += m_of(b, i);
       }
-      const int b = b0 + u * per_pass + tid / sp;
-      if (ri == 0 && b < n_pad) {
-        uint64_t key = ~0ull;
-        if (b < n_vis) {
-          const float mass = sm[u] * inv_s;
-          const float score = POEM ? si[u] * inv_s : mass;
-          if (p.tile_scores) p.tile_scores[diag_row + b] = score;
-          if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
-          if (!mandatory(b)) key = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
-        }
-        keys[b] = key;
-      }
+      const float mass = sm * inv_s;
+      const float score = POEM ? si * inv_s : mass;
+      if (p.tile_scores) p.tile_scores[diag_row + b] = score;
+      if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
+      if (!mandatory(b)) x[e] = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
     }
   }
   for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
     if (p.tile_scores) p.tile_scores[diag_row + b] = -1.f;
     if (p.tile_mass) p.tile_mass[diag_row + b] = -1.f;
   }
-  __syncthreads();
-  // bitonic sort, ascending: discard order
-  for (int k = 2; k <= n_pad; k <<= 1) {
-    for (int j = k >> 1; j > 0; j >>= 1) {
-      for (int i = tid; i < n_pad; i += kThrThreads) {
-        const int ixj = i ^ j;
-        if (ixj > i) {
-          const uint64_t a = keys[i], b = keys[ixj];
-          const bool up = (i & k) == 0;
-          if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
-        }
-      }
-      __syncthreads();
-    }
-  }
+  sort_blocked<E>(x, sh);  // ascending: the discard order
+
   // |{b < n_sink} U {diag - n_local < b <= diag}| inside 0 .. diag
   const int sink_hi = min(p.n_sink, n_vis);
   const int loc_lo = max(0, diag - p.n_local + 1);
   const int n_mand = sink_hi + (n_vis - loc_lo) - max(0, sink_hi - loc_lo);
   const int n_cand = n_vis - n_mand;
-  const int E = n_pad >= kThrThreads ? n_pad / kThrThreads : 1;
-  auto id_at = [&](int k) { return (int)(0xffffffffu - (uint32_t)(keys[k] & 0xffffffffull)); };
-  // sampled row i of block b
-  auto I_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_I[b * S + i];
-    else return Ib[(int64_t)b * bstride + i];
-  };
-  auto m_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_m[b * S + i];
-    else return Mb[(int64_t)b * bstride + i];
-  };
+  int ids[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) ids[e] = (int)(0xffffffffu - (uint32_t)(x[e] & 0xffffffffull));
   auto bound_of = [&](double a, double dl) -> double {
     if constexpr (POEM) return (1.0 - dl > 0.0) ? a / (1.0 - dl) : INFINITY;
     else return dl;
   };
 
   // Prefix sums over the discard order, kRowChunk sampled rows at a time: each thread
-  // walks its E consecutive positions, a vector scan gives each thread its exclusive
+  // sums its E consecutive positions, a vector scan gives each thread its exclusive
   // prefixes, and the first prefix length whose per-row bound exceeds tau is a block
   // minimum. With `limit` = the cut, the same walk yields the per-row bound at the cut.
   auto walk = [&](int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
     double A[kRowChunk], Dl[kRowChunk];
 #pragma unroll
     for (int r = 0; r < kRowChunk; ++r) A[r] = Dl[r] = 0.0;
+#pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int k = tid * E + e;
-      if (k < limit) {
-        const int b = id_at(k);
+      if (tid * E + e < limit) {
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
           if (r < nr) {
-            if constexpr (POEM) A[r] += (double)I_of(b, i0 + r);
-            Dl[r] += (double)m_of(b, i0 + r);
+            if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
+            Dl[r] += (double)m_of(ids[e], i0 + r);
           }
       }
     }
     block_excl_scan_vec<kRowChunk>(A, Dl, shd);
+#pragma unroll
     for (int e = 0; e < E; ++e) {
       const int k = tid * E + e;
       if (k < limit) {
-        const int b = id_at(k);
         bool over = false;
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
           if (r < nr) {
-            if constexpr (POEM) A[r] += (double)I_of(b, i0 + r);
-            Dl[r] += (double)m_of(b, i0 + r);
+            if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
+            Dl[r] += (double)m_of(ids[e], i0 + r);
             const double bound = bound_of(A[r], Dl[r]);
-            over |= bound > (double)tau;
+            over |= bound > (double)w.tau;
             if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
           }
         if (find && over && local_fail == INT_MAX) local_fail = k + 1;
@@ -458,7 +457,7 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int k_star = k_fail - 1;
 
   if (p.row_bound) {
-    float* rb = p.row_bound + ((int64_t)h * T + gtile) * S;
+    float* rb = p.row_bound + ((int64_t)w.h * T + w.gtile) * S;
     for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
       int unused = INT_MAX;
       walk(i0, min(kRowChunk, s_t - i0), k_star, false, unused, rb);
@@ -471,7 +470,9 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   // retained set, compacted in ascending id order
   for (int b = tid; b < n_vis; b += kThrThreads) keep[b] = 1;
   __syncthreads();
-  for (int k = tid; k < k_star; k += kThrThreads) keep[id_at(k)] = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (tid * E + e < k_star) keep[ids[e]] = 0;
   __syncthreads();
   const int E2 = (n_vis + kThrThreads - 1) / kThrThreads;
   int cnt = 0;
@@ -481,12 +482,97 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   }
   int total;
   int off = block_excl_scan_int(cnt, total, shi);
-  int32_t* out = p.slots + slot;
+  int32_t* out = p.slots + w.slot;
   for (int e = 0; e < E2; ++e) {
     const int b = tid * E2 + e;
     if (b < n_vis && keep[b]) out[off++] = b;
   }
-  if (tid == 0) p.counts[R] = total;
+  if (tid == 0) p.counts[w.R] = total;
+}
+
+template <int MODE, bool STAGED>
+__global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
+  constexpr bool POEM = MODE == kSelectOutputRelative;
+  constexpr int NK = STAGED ? kStageVis : kMaxVis;
+  __shared__ uint64_t sh[NK];
+  __shared__ uint8_t keep[NK];
+  __shared__ float st_I[STAGED && POEM ? kStageVals : 1];
+  __shared__ float st_m[STAGED ? kStageVals : 1];
+  __shared__ double shd[8 * kRowChunk];
+  __shared__ int shi[8];
+  const int tid = threadIdx.x;
+  const int T = p.seqs.total_tiles;
+  const int G = p.group;
+  const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
+  const int hg = rest % G;
+  const int unit = (rest / G) * kXcds + xcd;  // gtile * hkv + KV head
+  if (unit >= T * p.hkv) return;
+  ThrTile w;
+  w.gtile = unit / p.hkv;
+  const int gk = unit % p.hkv;
+  w.h = gk * G + hg;
+  w.R = w.h * T + w.gtile;  // CSR row
+  const int seq = find_seq(p.seqs, w.gtile);
+  const int t = w.gtile - p.seqs.tile_start[seq];
+  const int B = p.seqs.block;
+  w.diag = p.seqs.diag0[seq] + t;
+  w.n_vis = w.diag + 1;
+  const int n_rows_t = min(B, p.seqs.n_q[seq] - t * B);
+  w.S = p.S;
+  w.s_t = min(p.S, n_rows_t);
+  w.slot = (int64_t)w.h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
+  const int cols = 32 * p.col_tiles;
+  w.bstride = 2 * cols;  // floats per visible block
+  // row i of this head is column hg * S + i of its KV head's tile record
+  w.Ib = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * w.bstride + hg * w.S;
+  w.Mb = w.Ib + cols;
+  w.tau = p.tau[w.h];
+
+  if constexpr (STAGED) {
+    // the head's s_t values of I (POEM only) and m per visible block, read with every
+    // load of a batch in flight before the first LDS store
+    const int per_tensor = w.n_vis * w.s_t;
+    const int total = POEM ? 2 * per_tensor : per_tensor;
+    constexpr int BATCH = 16;
+    for (int base = 0; base < total; base += BATCH * kThrThreads) {
+      float val[BATCH];
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int idx = base + u * kThrThreads + tid;
+        val[u] = 0.f;
+        if (idx < total) {
+          const bool is_m = !POEM || idx >= per_tensor;
+          const int r = is_m && POEM ? idx - per_tensor : idx;
+          const int b = r / w.s_t, i = r % w.s_t;
+          val[u] = (is_m ? w.Mb : w.Ib)[(int64_t)b * w.bstride + i];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < BATCH; ++u) {
+        const int idx = base + u * kThrThreads + tid;
+        if (idx < total) {
+          const bool is_m = !POEM || idx >= per_tensor;
+          const int r = is_m && POEM ? idx - per_tensor : idx;
+          const int b = r / w.s_t, i = r % w.s_t;
+          (is_m ? st_m : st_I)[b * w.S + i] = val[u];
+        }
+      }
+    }
+    __syncthreads();
+  }
+  int n_pad = kThrThreads;
+  while (n_pad < w.n_vis) n_pad <<= 1;
+  switch (n_pad / kThrThreads) {
+    case 1: threshold_tile<MODE, STAGED, 1>(p, w, st_I, st_m, sh, keep, shd, shi); break;
+    case 2: threshold_tile<MODE, STAGED, 2>(p, w, st_I, st_m, sh, keep, shd, shi); break;
+    case 4: threshold_tile<MODE, STAGED, 4>(p, w, st_I, st_m, sh, keep, shd, shi); break;
+    default:
+      if constexpr (!STAGED) {
+        if (n_pad == 8 * kThrThreads) threshold_tile<MODE, STAGED, 8>(p, w, st_I, st_m, sh, keep, shd, shi);
+        else threshold_tile<MODE, STAGED, 16>(p, w, st_I, st_m, sh, keep, shd, shi);
+      }
+      break;
+  }
 }
 
 // Exclusive scan of the per-row counts into row_ptr (one workgroup).
