@@ -109,9 +109,12 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
           if (key0 + acc_key(kt, r, g2) > my_pos) S[kt][r] = -INFINITY;
     }
   };
-  // online-softmax step: S becomes 2^(c s - m) for the new running max m; returns the
-  // factor that rescales what was accumulated so far
-  auto weights = [&](f32x16 (&S)[2]) -> float {
+  // Online softmax in two parts, so that only the running max precedes the rescale
+  // branch. update(): new running max m; when some column's max grew (rare once the
+  // sink is seen) the accumulated O and row sums are rescaled. exps(): the scores
+  // become weights 2^(c s - m) and are added to the row sums.
+  float m_use = 0.f;
+  auto update = [&](const f32x16 (&S)[2]) {
     float mx = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -119,8 +122,16 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
     mx = fmaxf(mx, wave_xor32(mx));
     const float m_new = fmaxf(m_run, mx * c);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
+    m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+    m_run = m_new;
+    if (__any(alpha != 1.f)) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
+      l_run *= alpha;
+    }
+  };
+  auto exps = [&](f32x16 (&S)[2]) {
     float rs = 0.f;
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -129,32 +140,44 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         S[kt][r] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[kt][r], c, -m_use));
         rs += S[kt][r];
       }
-    // the row sum here keeps the exponentials next to the MFMAs they overlap
-    l_run = l_run * alpha + rs;
-    m_run = m_new;
-    return alpha;
-  };
-  // rescale, then O += P V for the stage whose weights are in S and V in vbuf
-  auto accumulate = [&](f32x16 (&S)[2], float alpha, const char* vbuf) {
-    if (__any(alpha != 1.f)) {
-#pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) O[dt] *= alpha;
-    }
-    if constexpr (St::ASYNC) {
-      bf16x8 P[4], unused;
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) p_step<false>(S, s4, P[s4], unused);
-      St::pv_packed(vbuf, P, O, lane);
-    } else {
-      St::template pv<false>(vbuf, S, O, lane);
-    }
+    l_run += rs;
   };
 
   if constexpr (St::ASYNC) {
     // Software pipeline over stages. K and V have their own double buffers and V lags K
-    // by one stage: step j reads K(j) and V(j-1) while K(j+1) and V(j) load, so the
-    // QK^T MFMAs of stage j are issued next to the softmax of stage j-1.
+    // by one stage: step j reads K(j) and V(j-1) while K(j+1) and V(j) load. The step is
+    // laid out by hand in short chunks fenced off from the scheduler:
+    //   QK phase : each QK^T MFMA of stage j with the next-but-one K fragment read and
+    //              the exponentials (and bf16 packs) of stage j-1;
+    //   mask     : only on stages that reach past a row;
+    //   PV phase : each P V MFMA of stage j-1 with the next-but-one V fragment read and
+    //              part of stage j's running max;
+    //   rescale  : only when some column's max grew.
+    constexpr int NQK = 2 * (D / 16);  // QK^T MFMAs per stage (2 key tiles x d steps)
+    constexpr int NDT = D / 32;        // d tiles of O
+    constexpr int NPV = 4 * NDT;       // P V MFMAs per stage (4 key steps x d tiles)
+    constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
+    constexpr int XPM = 32 / NPV;      // max candidates per P V MFMA
     f32x16 Sp[2];
+    auto kfrag = [&](const char* kbuf, int i) {  // K operand of QK MFMA i
+      const int kt = i & 1, st = i >> 1;
+      const int r = 32 * kt + (lane & 31);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + r * St::ROW +
+                                                                          ((2 * st + g2) ^ St::kswz(r)) * 16));
+    };
+    auto finish_max = [&](float mx) {  // running max of the stage, rare rescale
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_next);
+      m_run = m_new;
+      m_use = m_next;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+        l_run *= alpha;
+      }
+    };
     auto first = [&]() {
       St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0);
       wait_vmem_all();
@@ -164,19 +187,67 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       Sp[0] = St::qk_tile(kb0, qf, 0, lane);
       Sp[1] = St::qk_tile(kb0, qf, 1, lane);
       mask(Sp, stage_key0(0));
+      float mx = -INFINITY;
+#pragma unroll
+      for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sp[e >> 4][e & 15]);
+      finish_max(mx);
       wait_vmem_all();
       __syncthreads();
     };
+    const typename St::LaneOffsets lo = St::lane_offsets(row_stride, tid);
     auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
       const int key0 = stage_key0(it);
-      St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext);
-      St::load_v(vbase, row_stride, key0, n_k, tid, vcur);
-      f32x16 Sn[2];
-      Sn[0] = St::qk_tile(kcur, qf, 0, lane);
-      Sn[1] = St::qk_tile(kcur, qf, 1, lane);
-      const float alpha = weights(Sp);
-      accumulate(Sp, alpha, vprev);
-      mask(Sn, key0);
+      St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext, lo);
+      St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lo);
+      // QK phase
+      f32x16 Sn[2] = {f32x16{}, f32x16{}};
+      bf16x8 P[4];
+      bf16x8 ka[3];
+      ka[0] = kfrag(kcur, 0);
+      ka[1] = kfrag(kcur, 1);
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        Sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf.q[i >> 1], Sn[i & 1], 0, 0, 0);
+        if (i + 2 < NQK) ka[(i + 2) % 3] = kfrag(kcur, i + 2);
+#pragma unroll
+        for (int u = 0; u < EPM; ++u) {
+          const int e = i * EPM + u;
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
+          Sp[e >> 4][e & 15] = x;
+          rs += x;
+          if ((e & 7) == 7) {
+            bf16x8 unused;
+            p_step<false>(Sp, e >> 3, P[e >> 3], unused);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      l_run += rs;
+      // PV phase (the max is taken over the raw scores; masked stages redo it below)
+      bf16x8 va[3];
+      va[0] = St::v_frag(vprev, 0, 0, lane);
+      va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int dt = i % NDT, st = i / NDT;
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], P[st], O[dt], 0, 0, 0);
+        if (i + 2 < NPV) va[(i + 2) % 3] = St::v_frag(vprev, (i + 2) % NDT, (i + 2) / NDT, lane);
+#pragma unroll
+        for (int u = 0; u < XPM; ++u) {
+          const int e = i * XPM + u;
+          mx = fmaxf(mx, Sn[e >> 4][e & 15]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if (key0 + kStageKeys - 1 > wave_pos_min) {
+        mask(Sn, key0);
+        mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
+      }
+      finish_max(mx);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
       wait_vmem_all();
@@ -188,8 +259,11 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         step(it, kb1, kb0, vb0, vb1);
         if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
       }
-      const float alpha = weights(Sp);
-      accumulate(Sp, alpha, ((total - 1) & 1) ? vb1 : vb0);
+      exps(Sp);
+      bf16x8 P[4], unused;
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) p_step<false>(Sp, s4, P[s4], unused);
+      St::pv_packed(((total - 1) & 1) ? vb1 : vb0, P, O, lane);
     }
   } else {
     sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, kb0, kb1, [&](int it, const char* cur) {
@@ -199,8 +273,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       S[0] = St::qk_tile(cur, qf, 0, lane);
       S[1] = St::qk_tile(cur, qf, 1, lane);
       mask(S, key0);
-      const float alpha = weights(S);
-      accumulate(S, alpha, cur);
+      update(S);
+      exps(S);
+      St::template pv<false>(cur, S, O, lane);
     });
   }
 

@@ -217,16 +217,33 @@ struct StageB16 {
   // Buffer descriptors start at the stage's first key and cover only the valid keys,
   // so rows past the sequence end load as zeros; the per-lane offsets do not depend
   // on the stage and all stage-dependent addressing stays in scalar registers.
+  // Per-lane byte offsets of the direct loads. One wave-wide load covers RPI whole
+  // rows: lane l takes chunk l % CH of row RPI * blk + l / CH. Every swizzle above only
+  // sees the low bits of the row, which the wave's first row (a multiple of RPI) leaves
+  // to the lane's own l / CH, plus, for K when RPI < CH, a part that depends on blk.
+  // When that part is the same for all of a wave's loads (RPI * WAVES a multiple of CH)
+  // the whole per-lane offset is fixed for the sweep and each load adds only a scalar.
+  static constexpr uint32_t RPI = 1024 / ROW;
+  static_assert(RPI % 4 == 0 && RPI <= CH, "row groups must keep the swizzle bits lane-local");
+  static constexpr bool K_FIXED = (RPI * WAVES) % CH == 0;
+  struct LaneOffsets {
+    uint32_t k, v;
+  };
+  static __device__ __forceinline__ uint32_t lane_off(uint32_t row_bytes, uint32_t lane, uint32_t r0, bool is_v) {
+    const uint32_t lr = lane / CH, pos = lane % CH;
+    const uint32_t sw = is_v ? (uint32_t)vswz(lr) : ((r0 & (CH - 1)) | lr);
+    return lr * row_bytes + ((pos ^ sw) << 4);
+  }
+  static __device__ __forceinline__ LaneOffsets lane_offsets(int64_t row_stride, int tid) {
+    const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = (uint32_t)tid & 63u;
+    const uint32_t row_bytes = (uint32_t)(row_stride * 2);
+    return {lane_off(row_bytes, lane, RPI * wave, false), lane_off(row_bytes, lane, 0, true)};
+  }
+
   template <bool IS_V>
   static __device__ __forceinline__ void load_one(const uint16_t* __restrict__ base_ptr, int64_t row_stride,
-                                                  int key0, int n_valid, int tid, char* dst) {
-    // One wave-wide load covers RPI whole rows: lane l takes chunk l % CH of row
-    // RPI * blk + l / CH. Every swizzle above only sees the low bits of the row, which
-    // the wave's first row (a multiple of RPI) leaves to the lane's own l / CH (plus,
-    // for K with RPI < CH, a uniform part), so the per-lane offset is a few unsigned
-    // operations on values fixed for the whole sweep.
-    constexpr uint32_t RPI = 1024 / ROW;
-    static_assert(RPI % 4 == 0 && RPI <= CH, "row groups must keep the swizzle bits lane-local");
+                                                  int key0, int n_valid, int tid, char* dst,
+                                                  const LaneOffsets& lo) {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lane = (uint32_t)tid & 63u;
     const uint32_t row_bytes = (uint32_t)(row_stride * 2);
@@ -236,24 +253,33 @@ struct StageB16 {
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(base_ptr) + (int64_t)key0 * row_stride * 2), (short)0, records,
         0x00020000);
-    const uint32_t lr = lane / CH, pos = lane % CH;
-    const uint32_t lane_row = lr * row_bytes;
 #pragma unroll
     for (int j = 0; j < INSTR / WAVES; ++j) {
       const uint32_t blk = j * WAVES + wave;
       const uint32_t r0 = RPI * blk;  // uniform
-      const uint32_t sw = IS_V ? (uint32_t)vswz(lr) : ((r0 & (CH - 1)) | lr);
-      const uint32_t voff = r0 * row_bytes + lane_row + ((pos ^ sw) << 4);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_char*)(dst + blk * 1024), 16, (int)voff, 0, 0, 0);
+      uint32_t off;
+      if constexpr (IS_V) off = lo.v;
+      else if constexpr (K_FIXED) off = lo.k;
+      else off = lane_off(row_bytes, lane, r0, false);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_char*)(dst + blk * 1024), 16, (int)(r0 * row_bytes + off),
+                                               0, 0, 0);
     }
   }
   static __device__ __forceinline__ void load_k(const uint16_t* kbase, int64_t row_stride, int key0, int n_valid,
+                                                int tid, char* kbuf, const LaneOffsets& lo) {
+    load_one<false>(kbase, row_stride, key0, n_valid, tid, kbuf, lo);
+  }
+  static __device__ __forceinline__ void load_v(const uint16_t* vbase, int64_t row_stride, int key0, int n_valid,
+                                                int tid, char* vbuf, const LaneOffsets& lo) {
+    load_one<true>(vbase, row_stride, key0, n_valid, tid, vbuf, lo);
+  }
+  static __device__ __forceinline__ void load_k(const uint16_t* kbase, int64_t row_stride, int key0, int n_valid,
                                                 int tid, char* kbuf) {
-    load_one<false>(kbase, row_stride, key0, n_valid, tid, kbuf);
+    load_k(kbase, row_stride, key0, n_valid, tid, kbuf, lane_offsets(row_stride, tid));
   }
   static __device__ __forceinline__ void load_v(const uint16_t* vbase, int64_t row_stride, int key0, int n_valid,
                                                 int tid, char* vbuf) {
-    load_one<true>(vbase, row_stride, key0, n_valid, tid, vbuf);
+    load_v(vbase, row_stride, key0, n_valid, tid, vbuf, lane_offsets(row_stride, tid));
   }
   // both tensors of a stage into one buffer: K, then V at +TENSOR
   static __device__ __forceinline__ void load(Regs&, const uint16_t* __restrict__ kbase,
@@ -455,6 +481,34 @@ template <int D, int NT> struct StageSel<float, D, NT> { using type = StageF32<D
 template <typename T, int D, int NT> using Stage = typename StageSel<T, D, NT>::type;
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+
+// Scheduling hints (instruction groups the compiler fills in order within the current
+// basic block; results do not depend on them). Masks: MFMA, VALU, LDS read, VMEM read.
+constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgVmemRead = 0x020;
+// One pipelined attention stage: 16 QK^T MFMAs (16 K reads) next to the previous
+// stage's exponentials and bf16 packs, then its 16 P V MFMAs (32 transposing V
+// reads). LDS reads run ahead of the MFMAs that consume them.
+__device__ __forceinline__ void sched_stage() {
+  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+#pragma unroll
+  for (int i = 0; i < 14; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
+    __builtin_amdgcn_sched_group_barrier(kSgValu, 1, 0);
+  }
+}
 
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued once after the
 // per-column loads that precede a sweep: otherwise those loads stay "pending" at the
