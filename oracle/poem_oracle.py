@@ -31,6 +31,9 @@ Readings where the pages are silent (each listed in the design doc):
     (N_k - N_q) is a multiple of the block size.
   * Mass-only baseline: rank by the tile mass; cut at the last prefix whose
     largest per-row omitted mass is <= eps (the per-head budget).
+  * Group-shared lists: the S sampled rows of a (KV head, tile) are spread over
+    its G query heads (row j from head g G + j mod G); every sampled row's bound
+    must stay within its own head's tau.
 
 Everything is float64; inputs are widened exactly from bf16 / fp32.
 """
@@ -297,6 +300,7 @@ class TileSelection:
     per_row: np.ndarray  # [|cand|+1, S_t]
     k_star: int
     retained: list  # ascending
+    heads: list = None  # group selection: query head of each sampled row
 
     @property
     def discarded(self):
@@ -385,16 +389,77 @@ def select_tile_mass(p: Problem, q, k, v, h: int, tile: Tile, eps: float, n_sink
                          per_row, ks, retained)
 
 
+# ---------------------------------------------------------------------------
+# GQA-group-shared selection: one list per (KV head, tile) for the G query heads
+# that share the KV head ([BFLA] Section 3.3 shares K/V across a head group).
+# Reading: the S sampled rows of the tile (the positions of sampled_rows) are spread
+# over the group: row j is taken from query head g G + (j mod G). The score of a
+# block is the mean of I over those rows and the discard order is as in
+# select_tile. A discard set is acceptable iff every sampled row's bound
+# A_i / (1 - Delta_i) is <= the threshold of that row's head, so each sampled row
+# keeps the triangle-bound guarantee of its own head.
+# ---------------------------------------------------------------------------
+
+
+def group_excess_curve(I_rows, m_rows, order, row_tau):
+    """E(k) = max over sampled rows of (A_i(k) / (1 - Delta_i(k)) - tau_i) for
+    k = 0 .. len(order): a prefix is acceptable iff E(k) <= 0. Also the per-row
+    bounds [k, row]."""
+    _, per_row = bound_curve(I_rows, m_rows, order)
+    excess = per_row - np.asarray(row_tau, dtype=np.float64)[None, :]
+    return excess.max(axis=1), per_row
+
+
+def select_tile_group(p: Problem, q, k, v, g: int, tile: Tile, tau, n_sink: int, n_local: int,
+                      S: int) -> TileSelection:
+    """Group-shared selection for KV head g and one tile; tau: thresholds of all
+    query heads. The returned selection (h = g G) holds the sampled rows, their
+    heads, the group score and the shared retained list."""
+    G = p.group
+    K = _head_view(k, tile.k_row0, tile.n_k, g)
+    V = _head_view(v, tile.k_row0, tile.n_k, g)
+    n_vis = tile.diag + 1
+    rows = sampled_rows(tile.n_rows, S)
+    heads = [g * G + (j % G) for j in range(len(rows))]
+    stats = [row_block_stats(q[tile.q_row0 + r, h, :], K, V, p.scale, tile.pos0 + r, n_vis, p.block_size)
+             for r, h in zip(rows, heads)]
+    I = np.stack([st["I"] for st in stats])
+    m = np.stack([st["m"] for st in stats])
+    score = I.mean(axis=0)
+    mass = m.mean(axis=0)
+    mand = mandatory_blocks(tile.diag, n_sink, n_local)
+    cand = [b for b in range(n_vis) if b not in set(mand)]
+    order = discard_order(score, cand)
+    curve, per_row = group_excess_curve(I, m, order, [float(tau[h]) for h in heads])
+    ks = cut(curve, 0.0)
+    drop = set(order[:ks])
+    retained = [b for b in range(n_vis) if b not in drop]
+    return TileSelection(g * G, tile, rows, I, m, np.array([st["lse"] for st in stats]),
+                         np.stack([st["o"] for st in stats]), score, mass, mand, order, curve,
+                         per_row, ks, retained, heads)
+
+
 def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=None, mode: str = "poem"):
     """Selections for every (head, tile), or for the (h, gtile) pairs in `which`.
     mode "poem" uses the output-relative selector (tau: error threshold per head),
-    "mass" the mass-only one (tau: omitted-mass budget per head).
+    "mass" the mass-only one (tau: omitted-mass budget per head), "group" the
+    group-shared output-relative selector (one list per KV head and tile).
 
     Returns {(h, gtile): TileSelection}."""
-    fn = {"poem": select_tile, "mass": select_tile_mass}[mode]
     tl = tiles(p)
     if which is None:
         which = [(h, t.gtile) for h in range(p.num_heads_q) for t in tl]
+    if mode == "group":
+        # one selection per (KV head, tile), shared by the heads of the group
+        shared = {}
+        out = {}
+        for (h, gt) in which:
+            key = (h // p.group, gt)
+            if key not in shared:
+                shared[key] = select_tile_group(p, q, k, v, key[0], tl[gt], tau, n_sink, n_local, S)
+            out[(h, gt)] = shared[key]
+        return out
+    fn = {"poem": select_tile, "mass": select_tile_mass}[mode]
     return {(h, gt): fn(p, q, k, v, h, tl[gt], float(tau[h]), n_sink, n_local, S)
             for (h, gt) in which}
 

@@ -249,14 +249,14 @@ def test_mandatory_and_tiles():
 # --- selector ----------------------------------------------------------------------
 
 
-def _tiny_problem(seed, nq=200, nk=328, hq=2, hkv=1, d=8, B=64):
+def _tiny_problem(seed, nq=200, nk=328, hq=2, hkv=1, d=8, B=64, sink=6.0):
     rng = np.random.default_rng(seed)
     p = O.Problem((nq,), (nk,), hq, hkv, d, B)
     q = rng.standard_normal((nq, hq, d)) * 1.5
     k = rng.standard_normal((nk, hkv, d)) * 1.5
     v = rng.standard_normal((nk, hkv, d)) + rng.standard_normal(d)
     k[0, :, :] = 0
-    k[0, :, -1] = 6.0 * math.sqrt(d)
+    k[0, :, -1] = sink * math.sqrt(d)
     q[:, :, -1] = 1.0
     return p, q, k, v
 
@@ -459,6 +459,79 @@ def test_mass_nested_supports():
         prev = sel
 
 
+# --- group-shared selector -------------------------------------------------------------
+
+
+def pin_group_cut():
+    """Group cut: every prefix recomputed from scratch, each sampled row against its
+    own head's threshold (rows of different heads carry different taus)."""
+    rng = np.random.default_rng(41)
+    for _ in range(300):
+        n = int(rng.integers(1, 11))
+        S = int(rng.integers(1, 9))
+        I = rng.uniform(0, 0.02, (S, n)) * (rng.uniform(0, 1, (S, n)) < 0.8)
+        m = rng.dirichlet(np.ones(n + 2), size=S)[:, :n]
+        taus = rng.uniform(0, 0.1, S)
+        order = O.discard_order(I.mean(0), list(range(n)))
+        curve, _ = O.group_excess_curve(I, m, order, taus)
+        best = 0
+        for kk in range(n + 1):
+            ok = True
+            for j in range(1, kk + 1):
+                D = order[:j]
+                for i in range(S):
+                    if math.fsum(I[i, b] for b in D) / (1 - math.fsum(m[i, b] for b in D)) > taus[i]:
+                        ok = False
+            if ok:
+                best = kk
+        assert O.cut(curve, 0.0) == best
+
+
+def test_group_cut():
+    pin_group_cut()
+
+
+def pin_group_selection():
+    """Group-shared lists on tiny GQA problems: row j of a tile comes from head
+    g G + (j mod G); each sampled row's error (its own head's dense vs sparse output)
+    is within its bound, which is within that head's tau; the list is shared."""
+    cuts = []
+    for seed in range(3):
+        p, q, k, v = _tiny_problem(60 + seed, hq=4, hkv=2, sink=11.0)
+        taus = [0.03, 1.0, 0.1, 3.0]
+        sel = O.select(p, q, k, v, taus, 1, 1, 8, mode="group")
+        for (h, gt), s in sel.items():
+            g = h // p.group
+            t = s.tile
+            assert s.heads == [g * p.group + (j % p.group) for j in range(len(s.rows))]
+            assert sel[(g * p.group, gt)].retained == s.retained
+            assert set(s.mandatory) <= set(s.retained)
+            cuts.append(s.k_star)
+            for j, (r, hh) in enumerate(zip(s.rows, s.heads)):
+                od, _ = O.tile_attention(p, q, k, v, hh, t)
+                os_, _ = O.tile_attention(p, q, k, v, hh, t, s.retained)
+                err = np.linalg.norm(od[r] - os_[r])
+                b = s.per_row[s.k_star][j]
+                assert b <= taus[hh] + 1e-15
+                assert err <= b * (1 + 1e-9) + 1e-15
+    assert max(cuts) > 0  # some tiles discard blocks
+
+
+def test_group_selection():
+    pin_group_selection()
+
+
+def test_group_of_one_is_the_per_head_selector():
+    """With one query head per KV head the group selector is the per-head selector."""
+    p, q, k, v = _tiny_problem(70, hq=2, hkv=2)
+    for tau in (0.005, 0.03, 0.2):
+        a = O.select(p, q, k, v, [tau, tau * 2], 1, 1, 8)
+        b = O.select(p, q, k, v, [tau, tau * 2], 1, 1, 8, mode="group")
+        for key in a:
+            assert a[key].retained == b[key].retained and a[key].k_star == b[key].k_star
+            assert np.array_equal(a[key].score, b[key].score)
+
+
 def test_gpu_toy_geometry_in_oracle():
     """The toy realised at block granularity (B = 64, d = 64, fp32, scale 1): blocks
     0, 1, 2, 3 with masses 1/2, 1/4, 1/4, ~0 and values 2, 0, 4, 0 along e_0; the
@@ -560,7 +633,13 @@ def _mass_selector_ranks_by_proxy(p, q, k, v, h, tile, eps, n_sink, n_local, S):
 _orig_select_tile = O.select_tile
 
 
+def _group_curve_loosest_tau(I_rows, m_rows, order, row_tau):
+    _, per_row = O.bound_curve(I_rows, m_rows, order)
+    return per_row.max(axis=1) - max(row_tau), per_row
+
+
 @pytest.mark.parametrize("name,fn,pins", [
+    ("group_excess_curve", _group_curve_loosest_tau, ["group_cut", "group_selection"]),
     ("mass_curve", _mass_curve_mean_rows, ["mass_cut"]),
     ("select_tile_mass", _mass_selector_ranks_by_proxy, ["mass_selection"]),
     ("deleted_output", _deleted_no_renorm, ["toy_pairs"]),
@@ -583,6 +662,8 @@ def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
         "row_stats": pin_row_stats_invariants,
         "mass_cut": pin_mass_cut,
         "mass_selection": pin_mass_selection,
+        "group_cut": pin_group_cut,
+        "group_selection": pin_group_selection,
     }
     monkeypatch.setattr(O, name, fn)
     for pin in pins:
