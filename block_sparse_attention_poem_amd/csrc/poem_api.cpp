@@ -1,6 +1,7 @@
 // libpoem C ABI: argument validation, geometry, workspace layout and launches.
 // Every check runs on the host before anything is enqueued; nothing here allocates
 // device memory, copies host data to the device or synchronises the host.
+#include <algorithm>
 #include <math.h>
 #include <stdarg.h>
 #include <stdio.h>
@@ -115,15 +116,20 @@ struct SelLayout {
   size_t row_stats = 0, blk_stats = 0, counts = 0, slots = 0, total = 0;
 };
 
-SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S) {
+// Record columns per (KV head, tile): per-head lists pack the G heads' S rows into
+// 32-column tiles; a group-shared list has S columns.
+int record_columns(const poem_problem* p, int S, bool group_mode) {
   const int G = p->num_heads_q / p->num_heads_kv;
-  const int CT = (G * S + 31) / 32;
+  return group_mode ? S : 32 * ((G * S + 31) / 32);
+}
+
+SelLayout sel_layout(const poem_problem* p, const Geometry& g, int cols) {
   SelLayout L;
   size_t off = 0;
   L.row_stats = off;
-  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * CT * 32 * (p->head_dim + 4));
+  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (p->head_dim + 4));
   L.blk_stats = off;
-  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.vis_per_head * CT * 32 * 2);
+  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.vis_per_head * cols * 2);
   L.counts = off;
   off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.num_tiles);
   L.slots = off;
@@ -132,12 +138,12 @@ SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S) {
   return L;
 }
 
-poem_status check_rows(const poem_problem* p, int32_t S) {
+poem_status check_rows(const poem_problem* p, int32_t S, bool group_mode) {
   if (S < 1) return fail(POEM_ERR_INVALID_ARG, "rows_per_tile must be >= 1 (got %d)", S);
   if (S > POEM_MAX_ROWS_PER_TILE)
     return fail(POEM_ERR_UNSUPPORTED, "rows_per_tile %d exceeds POEM_MAX_ROWS_PER_TILE (%d)", S, POEM_MAX_ROWS_PER_TILE);
   const int G = p->num_heads_q / p->num_heads_kv;
-  if ((int64_t)G * S > 128)
+  if (!group_mode && (int64_t)G * S > 128)
     return fail(POEM_ERR_UNSUPPORTED, "group size x rows_per_tile = %d exceeds 128 selector columns", G * S);
   return POEM_OK;
 }
@@ -179,13 +185,18 @@ int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_pe
   Geometry g;
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
-  s = check_rows(problem, rows_per_tile);
+  s = check_rows(problem, rows_per_tile, true);
   if (s != POEM_OK) return s;
   ok();
-  return (int64_t)sel_layout(problem, g, rows_per_tile).total;
+  // enough for every selector entry point the problem allows
+  const int G = problem->num_heads_q / problem->num_heads_kv;
+  size_t bytes = sel_layout(problem, g, record_columns(problem, rows_per_tile, true)).total;
+  if ((int64_t)G * rows_per_tile <= 128)
+    bytes = std::max(bytes, sel_layout(problem, g, record_columns(problem, rows_per_tile, false)).total);
+  return (int64_t)bytes;
 }
 
-static poem_status select_impl(int mode, const poem_problem* problem, const void* q, const void* k, const void* v,
+static poem_status select_impl(int mode, bool group_mode, const poem_problem* problem, const void* q, const void* k, const void* v,
                                const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
                                int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                                int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
@@ -193,7 +204,7 @@ static poem_status select_impl(int mode, const poem_problem* problem, const void
   Geometry g;
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
-  s = check_rows(problem, rows_per_tile);
+  s = check_rows(problem, rows_per_tile, group_mode);
   if (s != POEM_OK) return s;
   if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
   if (row_ptr == nullptr || block_idx == nullptr) return fail(POEM_ERR_INVALID_ARG, "row_ptr or block_idx is NULL");
@@ -214,7 +225,8 @@ static poem_status select_impl(int mode, const poem_problem* problem, const void
   if (block_idx_capacity < g.capacity)
     return fail(POEM_ERR_CAPACITY, "block_idx capacity %lld < required %lld", (long long)block_idx_capacity,
                 (long long)g.capacity);
-  const SelLayout L = sel_layout(problem, g, rows_per_tile);
+  const int cols = record_columns(problem, rows_per_tile, group_mode);
+  const SelLayout L = sel_layout(problem, g, cols);
   if (workspace == nullptr) return fail(POEM_ERR_WORKSPACE, "workspace is NULL");
   if (workspace_bytes < L.total)
     return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -230,6 +242,9 @@ static poem_status select_impl(int mode, const poem_problem* problem, const void
   sp.group = problem->num_heads_q / problem->num_heads_kv;
   sp.S = rows_per_tile;
   sp.col_tiles = (sp.group * rows_per_tile + 31) / 32;
+  sp.group_mode = group_mode ? 1 : 0;
+  sp.cols_rec = cols;
+  sp.tiles_per_wave = group_mode ? 32 / rows_per_tile : 1;
   sp.n_sink = n_sink_blocks;
   sp.n_local = n_local_blocks;
   sp.max_vis = (int32_t)g.max_vis;
@@ -256,7 +271,17 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks, int32_t rows_per_tile,
                         int32_t* row_ptr, int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
                         float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(poem::kSelectOutputRelative, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
+  return select_impl(poem::kSelectOutputRelative, false, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
+                     rows_per_tile, row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound,
+                     workspace, workspace_bytes, stream);
+}
+
+poem_status poem_select_group(const poem_problem* problem, const void* q, const void* k, const void* v,
+                              const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                              int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                              int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
+                              void* workspace, size_t workspace_bytes, void* stream) {
+  return select_impl(poem::kSelectOutputRelative, true, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
                      rows_per_tile, row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound,
                      workspace, workspace_bytes, stream);
 }
@@ -266,7 +291,7 @@ poem_status poem_select_mass(const poem_problem* problem, const void* q, const v
                              int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                              int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(poem::kSelectMass, problem, q, k, v, eps_host, n_sink_blocks, n_local_blocks, rows_per_tile,
+  return select_impl(poem::kSelectMass, false, problem, q, k, v, eps_host, n_sink_blocks, n_local_blocks, rows_per_tile,
                      row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound, workspace,
                      workspace_bytes, stream);
 }

@@ -48,11 +48,18 @@ struct SelectParams {
   int32_t n_sink, n_local;
   int32_t max_vis;
   int32_t mode;              // kSelectOutputRelative or kSelectMass
+  // column layout of the per-(KV head, tile) records. Per-head lists: column
+  // f = hg * S + j (row j of head g G + hg), cols_rec = 32 * col_tiles, one tile per
+  // wave. Group-shared lists (group_mode): column j is row j of head g G + j mod G,
+  // cols_rec = S and a wave holds tiles_per_wave = 32 / S tiles.
+  int32_t group_mode;
+  int32_t cols_rec;
+  int32_t tiles_per_wave;
   float scale_log2;
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions
-  float* row_stats;          // [hkv][total_tiles][col_tiles*32][D + 4]: M2, l, pad, pad, normalised o
-  float* blk_stats;          // per (KV head, gtile, visible block): I[32*col_tiles] then m[32*col_tiles]
+  float* row_stats;          // [hkv][total_tiles][cols_rec][D + 4]: M2, l, pad, pad, normalised o
+  float* blk_stats;          // per (KV head, gtile, visible block): I[cols_rec] then m[cols_rec]
   int32_t* counts;           // [hq * total_tiles]
   int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets
   // outputs

@@ -47,7 +47,8 @@ void sel_sweep_kernel(SelectParams p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
   const int CT = p.col_tiles;
-  const int TG = max(1, kSelWaves / CT);
+  const int TPW = p.tiles_per_wave;
+  const int TG = p.group_mode ? kSelWaves * TPW : max(1, kSelWaves / CT);
 
   const int gk = blockIdx.x % p.hkv;
   const int rank = blockIdx.x / p.hkv;
@@ -59,22 +60,37 @@ void sel_sweep_kernel(SelectParams p) {
   const int t_last = min(tile0 + TG - 1, n_tiles - 1);
   const int nblk_wg = diag0 + t_last + 1;
 
-  // this wave's unit: tile t, column tile ct
-  const int t = tile0 + wave / CT, ct = wave % CT;
-  const bool wave_on = wave < TG * CT && t < n_tiles;
+  // this lane's column: tile t, record column col, row jr of the tile's sample taken
+  // from query head gk * G + hg
+  int t, col, jr, hg, tw0, tw1;
+  bool in_range;
+  if (p.group_mode) {
+    tw0 = tile0 + wave * TPW;
+    tw1 = min(tw0 + TPW - 1, n_tiles - 1);
+    t = tw0 + jcol / p.S;
+    jr = col = jcol % p.S;
+    hg = jr % p.group;
+    in_range = jcol < TPW * p.S && t < n_tiles;
+  } else {
+    tw0 = tw1 = t = tile0 + wave / CT;
+    col = 32 * (wave % CT) + jcol;
+    hg = col / p.S;
+    jr = col % p.S;
+    in_range = wave < TG * CT && t < n_tiles && hg < p.group;
+  }
+  const bool wave_on = tw0 < n_tiles && (p.group_mode || wave < TG * CT);
   const int diag = diag0 + t;
-  const int n_rows_t = wave_on ? min(BLK, n_q - t * BLK) : 1;
+  const int n_rows_t = in_range ? min(BLK, n_q - t * BLK) : 1;
   const int s_t = min(p.S, n_rows_t);
-  const int f = 32 * ct + jcol;
-  const int hg = f / p.S, jr = f % p.S;
-  const bool col_on = wave_on && hg < p.group && jr < s_t;
+  const bool col_on = in_range && jr < s_t;
   const int h = gk * p.group + (col_on ? hg : 0);
   const int r_local = col_on ? ((jr + 1) * n_rows_t + s_t - 1) / s_t - 1 : 0;
   const int tile_pos0 = (n_k - n_q) + t * BLK;
   const int my_pos = tile_pos0 + r_local;
-  const int wave_pos_min = wave_on ? tile_pos0 : 0;
-  const int wave_pos_max = wave_on ? tile_pos0 + n_rows_t - 1 : -1;
-  const int gtile = p.seqs.tile_start[seq] + t;
+  // key range the wave's rows see: its first tile's first row .. its last tile's last row
+  const int wave_pos_min = wave_on ? (n_k - n_q) + tw0 * BLK : 0;
+  const int wave_pos_max = wave_on ? (n_k - n_q) + min((tw1 + 1) * BLK, n_q) - 1 : -1;
+  const int gtile = p.seqs.tile_start[seq] + (in_range ? t : 0);
 
   const int64_t qrow = (int64_t)p.seqs.q_start[seq] + t * BLK + r_local;
   QFrag<T, D> qf;
@@ -84,8 +100,7 @@ void sel_sweep_kernel(SelectParams p) {
   const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
   const T* vbase = reinterpret_cast<const T*>(p.v) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
   // per column: M2, l, two pad words, then o (16-byte aligned)
-  float* rs_col = p.row_stats +
-                  ((((int64_t)gk * p.seqs.total_tiles + (wave_on ? gtile : 0)) * CT + ct) * 32 + jcol) * (D + 4);
+  float* rs_col = p.row_stats + (((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + (in_range ? col : 0)) * (D + 4);
   const float c = p.scale_log2;
 
   f32x16 O[D / 32];
@@ -112,13 +127,13 @@ void sel_sweep_kernel(SelectParams p) {
         for (int e = 0; e < 4; ++e) Od[dt][4 * a + e] = v4[e];
       }
   }
-  // per (KV head, tile, visible block): I of all 32*CT columns, then m of all columns,
-  // so a wave's per-block results are one coalesced 128-byte store each
+  // per (KV head, tile, visible block): I of the record's columns, then m of them, so
+  // a wave's per-block results are one coalesced store each per tile
   float* blk_I = nullptr;
+  const int64_t bstride = 2 * (int64_t)p.cols_rec;
   if constexpr (PASS2) {
-    if (wave_on)
-      blk_I = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * (2 * 32 * CT) +
-              32 * ct + jcol;
+    if (in_range)
+      blk_I = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * bstride + col;
   }
 
   wait_vmem_all();
@@ -181,7 +196,8 @@ void sel_sweep_kernel(SelectParams p) {
       if constexpr (!MASS) St::template pv<SPLIT>(cur, S, O, lane);
     }
     if constexpr (PASS2) {
-      if (sub == SUBS - 1 && wave_on && blk <= diag) {
+      // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
+      if (sub == SUBS - 1 && in_range && blk <= diag) {
         const float mt = mloc + wave_xor32(mloc);
         float ss = 0.f;
         if constexpr (!MASS) {
@@ -195,9 +211,9 @@ void sel_sweep_kernel(SelectParams p) {
           ss += wave_xor32(ss);
         }
         if (col_on && g2 == 0) {
-          float* dst = blk_I + (int64_t)blk * (2 * 32 * CT);
+          float* dst = blk_I + (int64_t)blk * bstride;
           if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * inv_l;
-          dst[32 * CT] = mt * inv_l;
+          dst[p.cols_rec] = mt * inv_l;
         }
       }
     }
@@ -343,11 +359,12 @@ __device__ __forceinline__ void sort_blocked(uint64_t (&x)[E], uint64_t* sh) {
 // One (query head, tile) of the threshold kernel after staging: scores, sort, cut,
 // row bounds and compaction, with E = padded candidates / 256 keys per thread.
 struct ThrTile {
-  int h, gtile, R, S, s_t, n_vis, diag;
+  int h0, nh;  // the list is written for query heads h0 .. h0 + nh - 1 (nh = G when shared)
+  int gtile, S, s_t, n_vis, diag;
   int64_t slot, bstride;
-  const float* Ib;  // this head's slice of the per-block records (global)
+  const float* Ib;  // the rows' slice of the per-block records (global)
   const float* Mb;
-  float tau;
+  int tau_group;    // 0: every row uses tau[h0]; G: row i uses tau[h0 + i % G]
 };
 
 // MODE kSelectOutputRelative: key = mean_i I_ib, bound = max_i A_i(k) / (1 - Delta_i(k));
@@ -370,7 +387,9 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   };
   auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
   const float inv_s = 1.f / (float)s_t;
-  const int64_t diag_row = ((int64_t)w.h * T + w.gtile) * p.max_vis;
+  const int64_t head_stride = (int64_t)T * p.max_vis;  // score rows of consecutive heads
+  const int64_t diag_row = ((int64_t)w.h0 * T + w.gtile) * p.max_vis;
+  auto tau_of = [&](int i) { return p.tau[w.h0 + (w.tau_group ? i % w.tau_group : 0)]; };
 
   // scores of this thread's blocks tid * E + e, as sort keys (score bits, ~id)
   uint64_t x[E];
@@ -386,15 +405,18 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
       }
       const float mass = sm * inv_s;
       const float score = POEM ? si * inv_s : mass;
-      if (p.tile_scores) p.tile_scores[diag_row + b] = score;
-      if (p.tile_mass) p.tile_mass[diag_row + b] = mass;
+      for (int hh = 0; hh < w.nh; ++hh) {
+        if (p.tile_scores) p.tile_scores[diag_row + hh * head_stride + b] = score;
+        if (p.tile_mass) p.tile_mass[diag_row + hh * head_stride + b] = mass;
+      }
       if (!mandatory(b)) x[e] = ((uint64_t)__float_as_uint(score) << 32) | (uint64_t)(0xffffffffu - (uint32_t)b);
     }
   }
-  for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
-    if (p.tile_scores) p.tile_scores[diag_row + b] = -1.f;
-    if (p.tile_mass) p.tile_mass[diag_row + b] = -1.f;
-  }
+  for (int hh = 0; hh < w.nh; ++hh)
+    for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
+      if (p.tile_scores) p.tile_scores[diag_row + hh * head_stride + b] = -1.f;
+      if (p.tile_mass) p.tile_mass[diag_row + hh * head_stride + b] = -1.f;
+    }
   sort_blocked<E>(x, sh);  // ascending: the discard order
 
   // |{b < n_sink} U {diag - n_local < b <= diag}| inside 0 .. diag
@@ -441,7 +463,7 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
             if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
             Dl[r] += (double)m_of(ids[e], i0 + r);
             const double bound = bound_of(A[r], Dl[r]);
-            over |= bound > (double)w.tau;
+            over |= bound > (double)tau_of(i0 + r);
             if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
           }
         if (find && over && local_fail == INT_MAX) local_fail = k + 1;
@@ -457,7 +479,7 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   const int k_star = k_fail - 1;
 
   if (p.row_bound) {
-    float* rb = p.row_bound + ((int64_t)w.h * T + w.gtile) * S;
+    float* rb = p.row_bound + ((int64_t)w.h0 * T + w.gtile) * S;
     for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
       int unused = INT_MAX;
       walk(i0, min(kRowChunk, s_t - i0), k_star, false, unused, rb);
@@ -465,6 +487,11 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
     for (int i = tid; i < S; i += kThrThreads)
       if (i >= s_t) rb[i] = -1.f;
       else if (k_star == 0) rb[i] = 0.f;
+    if (w.nh > 1) {  // the same rows' bounds under every head of the group
+      __syncthreads();
+      for (int hh = 1; hh < w.nh; ++hh)
+        for (int i = tid; i < S; i += kThrThreads) rb[(int64_t)hh * T * S + i] = rb[i];
+    }
   }
 
   // retained set, compacted in ascending id order
@@ -487,7 +514,7 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
     const int b = tid * E2 + e;
     if (b < n_vis && keep[b]) out[off++] = b;
   }
-  if (tid == 0) p.counts[w.R] = total;
+  if (tid < w.nh) p.counts[(w.h0 + tid) * T + w.gtile] = total;
 }
 
 template <int MODE, bool STAGED>
@@ -502,7 +529,7 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   __shared__ int shi[8];
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
-  const int G = p.group;
+  const int G = p.group_mode ? 1 : p.group;  // workgroups per (KV head, tile)
   const int xcd = blockIdx.x % kXcds, rest = blockIdx.x / kXcds;
   const int hg = rest % G;
   const int unit = (rest / G) * kXcds + xcd;  // gtile * hkv + KV head
@@ -510,8 +537,9 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   ThrTile w;
   w.gtile = unit / p.hkv;
   const int gk = unit % p.hkv;
-  w.h = gk * G + hg;
-  w.R = w.h * T + w.gtile;  // CSR row
+  w.h0 = gk * p.group + hg;
+  w.nh = p.group_mode ? p.group : 1;
+  w.tau_group = p.group_mode ? p.group : 0;
   const int seq = find_seq(p.seqs, w.gtile);
   const int t = w.gtile - p.seqs.tile_start[seq];
   const int B = p.seqs.block;
@@ -520,13 +548,14 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int n_rows_t = min(B, p.seqs.n_q[seq] - t * B);
   w.S = p.S;
   w.s_t = min(p.S, n_rows_t);
-  w.slot = (int64_t)w.h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
-  const int cols = 32 * p.col_tiles;
+  w.slot = (int64_t)w.h0 * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
+  const int cols = p.cols_rec;
   w.bstride = 2 * cols;  // floats per visible block
-  // row i of this head is column hg * S + i of its KV head's tile record
-  w.Ib = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * w.bstride + hg * w.S;
+  // per-head lists: row i of head hg is column hg * S + i of the KV head's tile
+  // record; shared lists: row i is column i
+  w.Ib = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * w.bstride +
+         (p.group_mode ? 0 : hg * w.S);
   w.Mb = w.Ib + cols;
-  w.tau = p.tau[w.h];
 
   if constexpr (STAGED) {
     // the head's s_t values of I (POEM only) and m per visible block, read with every
@@ -606,7 +635,8 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(SelectParams p) {
   const int R = h * T + gtile;  // CSR row
   const int seq = find_seq(p.seqs, gtile);
   const int t = gtile - p.seqs.tile_start[seq];
-  const int32_t* src = p.slots + (int64_t)h * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
+  const int hs = p.group_mode ? (h / p.group) * p.group : h;  // a shared list lives in its first head's slot
+  const int32_t* src = p.slots + (int64_t)hs * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t);
   const int n = p.counts[R];
   int32_t* dst = p.block_idx + p.row_ptr[R];
   for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
@@ -614,7 +644,7 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(SelectParams p) {
 
 template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
-  const int TG = max(1, kSelWaves / p.col_tiles);
+  const int TG = p.group_mode ? kSelWaves * p.tiles_per_wave : max(1, kSelWaves / p.col_tiles);
   int items = 0;
   for (int i = 0; i < p.seqs.num_seqs; ++i) items += (p.seqs.n_tiles[i] + TG - 1) / TG;
   const int64_t rows = (int64_t)p.hq * p.seqs.total_tiles;
@@ -633,7 +663,7 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   }
   // threshold grid: (KV-head unit, head in group) with the unit's XCD kept fixed
   const int64_t units = (int64_t)p.seqs.total_tiles * p.hkv;
-  const unsigned tgrid = (unsigned)(((units + kXcds - 1) / kXcds) * kXcds * p.group);
+  const unsigned tgrid = (unsigned)(((units + kXcds - 1) / kXcds) * kXcds * (p.group_mode ? 1 : p.group));
   const bool staged = p.max_vis <= kStageVis && (int64_t)p.max_vis * p.S <= kStageVals;
   if (mass) {
     if (staged) hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);

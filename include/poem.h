@@ -88,7 +88,8 @@ int64_t poem_csr_capacity(const poem_problem* problem);
 /* Largest T_t + 1 over all tiles (the row length of the selector's score outputs). */
 int64_t poem_max_visible_blocks(const poem_problem* problem);
 
-/* Bytes of device workspace poem_select needs (256-byte aligned start); < 0 on error. */
+/* Bytes of device workspace the selectors need (256-byte aligned start): enough for
+ * poem_select, poem_select_mass and poem_select_group at this rows_per_tile; < 0 on error. */
 int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile);
 
 /*
@@ -133,6 +134,36 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                         int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
                         float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * poem_select_group: the output-relative selector with one list per (KV head, tile),
+ * shared by the G = H_q / H_kv query heads that read that KV head (BFLA Section 3.3
+ * groups query heads by KV head).
+ *
+ * The tile's S_t = min(rows_per_tile, n_t) sampled rows sit at the positions
+ * poem_select uses, but are spread over the group: row j is taken from query head
+ * g G + (j mod G), so each head contributes about S / G rows and the selector does
+ * about 1 / G of poem_select's work. Per row: m_ib, u_ib, o_i and I_ib as in
+ * poem_select; block score Ibar_b = mean over the S_t rows; discard order as in
+ * poem_select. A prefix of the discard order is acceptable iff every sampled row's
+ * bound A_i / (1 - Delta_i) is <= tau_host of that row's head; the cut is the longest
+ * prefix all of whose sub-prefixes are acceptable. Each sampled row thus keeps its own
+ * head's guarantee. The CSR holds the shared list under every head of the group
+ * (rows h * num_tiles + tile), so poem_sparse_prefill consumes it unchanged.
+ *
+ * Arguments as for poem_select, except:
+ *   rows_per_tile  S per (KV head, tile), 1 .. POEM_MAX_ROWS_PER_TILE (no limit on G S).
+ *   tile_scores, tile_mass  nullable: the group's Ibar_b and mbar_b, repeated under each
+ *                  head of the group.
+ *   row_bound      nullable: the group's per-row bounds at the cut, row j of the group
+ *                  sample at index j, repeated under each head of the group.
+ * The workspace size is poem_select_workspace_bytes(). Errors as for poem_select.
+ */
+poem_status poem_select_group(const poem_problem* problem, const void* q, const void* k, const void* v,
+                              const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                              int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
+                              int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
+                              float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * poem_select_mass: the mass-only selector, the baseline the POEM note compares the

@@ -48,14 +48,16 @@ def retained(rp, bi, r):
     return bi[rp[r]:rp[r + 1]].tolist()
 
 
-def mask_agreement(sel, gpu_retained, tau, floor):
+def mask_agreement(sel, gpu_retained, tau, floor, target=None):
     """Compare one tile's GPU retained set with the oracle's selection.
 
     Returns (n_candidates, n_matching_decisions, non_exempt_mismatches). A mismatch on
     block b is exempt when b's oracle score is within NEAR_REL of the oracle score at
     the last discarded or first retained position of the oracle's discard order, or
     when the oracle bound B(j) is within NEAR_REL * tau of tau at b's own position j
-    or the one before it."""
+    or the one before it (target: the curve value at the cut, tau unless given; the
+    group selector's excess curve cuts at 0)."""
+    target = tau if target is None else target
     order = sel.order
     ks = sel.k_star
     pos = {b: j + 1 for j, b in enumerate(order)}  # 1-based position in the discard order
@@ -76,7 +78,7 @@ def mask_agreement(sel, gpu_retained, tau, floor):
         ex = any(abs(s - ns) <= NEAR_REL * max(ns, floor) for ns in near_scores)
         j = pos[b]
         for jj in (j, j - 1):
-            if 0 <= jj < len(sel.curve) and abs(sel.curve[jj] - tau) <= NEAR_REL * tau:
+            if 0 <= jj < len(sel.curve) and abs(sel.curve[jj] - target) <= NEAR_REL * tau:
                 ex = True
         if not ex:
             bad.append(b)

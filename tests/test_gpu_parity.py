@@ -354,6 +354,85 @@ def test_mass_selector_matches_oracle(case, sink, n_local, eps):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst mass rel err", ws)
 
 
+def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=None, gpu_sparse=None):
+    """poem_select_group against the oracle's group selection on (KV head, gtile) units:
+    group scores, the shared list under every head, masks with exemptions, and for
+    every sampled row (of its own head) error <= bound <= that head's tau."""
+    T = L.num_tiles(gp)
+    G = op.group
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    scores = r["tile_scores"].cpu().numpy()
+    bounds = r["row_bound"].cpu().numpy()
+    which = [(g * G, gt) for (g, gt) in which_units]
+    sels = O.select(op, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which,
+                    mode="group")
+    n_cand = n_match = 0
+    worst = 0.0
+    for (h0, gt), sel in sels.items():
+        t = sel.tile
+        n_vis = t.diag + 1
+        tmin = min(float(taus[h]) for h in range(h0, h0 + G))
+        kept = H.retained(rp, bi, h0 * T + gt)
+        for h in range(h0, h0 + G):  # one list, the same scores and bounds under every head
+            assert H.retained(rp, bi, h * T + gt) == kept
+            assert np.array_equal(scores[h, gt], scores[h0, gt])
+            assert np.array_equal(bounds[h, gt], bounds[h0, gt])
+        se, sm, info = H.score_errors(sel, scores[h0, gt], tmin)
+        worst = max(worst, se)
+        assert se <= H.SCORE_RTOL, (h0, gt, se, info)
+        assert sm <= H.MANDATORY_SCORE_RTOL, (h0, gt, sm)
+        assert np.all(scores[h0, gt, n_vis:] == -1.0)
+        assert kept == sorted(kept) and len(set(kept)) == len(kept)
+        assert set(sel.mandatory) <= set(kept)
+        nc, nm, bad = H.mask_agreement(sel, kept, tmin, tmin / n_vis, target=0.0)
+        n_cand += nc
+        n_match += nm
+        assert not bad, (h0, gt, bad)
+        for j, (row, hh) in enumerate(zip(sel.rows, sel.heads)):
+            od, _ = O.tile_attention(op, q, k, v, hh, t)
+            osp, _ = O.tile_attention(op, q, k, v, hh, t, kept)
+            err = float(np.linalg.norm(od[row] - osp[row]))
+            b = float(bounds[h0, gt, j])
+            assert b <= float(taus[hh]) * (1 + 1e-6), (h0, gt, j, b, taus[hh])
+            assert err <= b * (1 + 1e-3) + 1e-6, (h0, gt, j, err, b)
+            if gpu_dense is not None:
+                ge = float(np.linalg.norm(gpu_dense[t.q_row0 + row, hh].astype(np.float64) -
+                                          gpu_sparse[t.q_row0 + row, hh].astype(np.float64)))
+                assert ge <= b * (1 + 1e-3) + 2e-4, (h0, gt, j, ge, b)
+        assert np.all(bounds[h0, gt, len(sel.rows):] == -1.0)
+    return n_cand, n_match, worst
+
+
+GROUP = [
+    # case, sink_offset, n_local, rows_per_tile (per KV head and tile)
+    ((300, 428, 4, 1, 64, 64, "bf16", 1), 6.0, 1, 8),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 6.0, 1, 8),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), 5.0, 2, 8),
+    ((300, 428, 4, 2, 64, 64, "fp32", 1), 6.0, 1, 4),
+    ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1, 5),
+    ((64, 4160, 4, 1, 64, 64, "bf16", 1), 7.0, 1, 16),
+]
+
+
+@pytest.mark.parametrize("case,sink,n_local,S", GROUP, ids=lambda x: str(x))
+def test_group_selector_matches_oracle(case, sink, n_local, S):
+    w = _small(case, seed=9).with_(sink_offset=sink, n_local_blocks=n_local, rows_per_tile=S)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("group selector", case, sink, n_local, S)
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="group")
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    q, k, v = H.f64(inp)
+    units = [(g, t.gtile) for g in range(op.num_heads_kv) for t in O.tiles(op)]
+    nc, nm, ws = check_group_selection(w, inp.tau, gp, op, r, units, q, k, v, d_out.cpu().numpy(),
+                                       s_out.cpu().numpy())
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
 # ---------------------------------------------------------------------------
 # the workloads at full size
 # ---------------------------------------------------------------------------
@@ -449,5 +528,36 @@ def test_mass_full_size_sampled():
     T = L.num_tiles(gp)
     for (h, gt) in which[:4]:
         t = O.tiles(op)[gt]
+        Os, _ = O.tile_attention(op, q, k, v, h, t, H.retained(rp, bi, h * T + gt))
+        assert np.abs(so[t.q_row0:t.q_row0 + t.n_rows, h] - Os).max() <= H.OUT_ATOL_BF16
+
+
+def test_group_full_size_sampled():
+    """poem_select_group at the 128K layer's full size; oracle on stratified units."""
+    import torch
+    w = synth.WORKLOADS[3]
+    say("workload 3 group-shared: generate")
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("workload 3 group-shared: select + sparse")
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="group")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    say("  keep fraction", len(bi[:rp[-1]]) / L.csr_capacity(gp))
+    so = s_out.cpu().numpy()
+    del s_out
+    torch.cuda.empty_cache()
+    q, k, v = H.f64(inp)
+    which = H.stratified_tiles(op, [0, w.num_heads_q - 1], per_head=3, seed=44)
+    units = sorted({(h // op.group, gt) for (h, gt) in which})
+    nc, nm, ws = check_group_selection(w, inp.tau, gp, op, r, units, q, k, v)
+    say("  sampled candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+    T = L.num_tiles(gp)
+    for (g, gt) in units[:3]:
+        t = O.tiles(op)[gt]
+        h = g * op.group + 1
         Os, _ = O.tile_attention(op, q, k, v, h, t, H.retained(rp, bi, h * T + gt))
         assert np.abs(so[t.q_row0:t.q_row0 + t.n_rows, h] - Os).max() <= H.OUT_ATOL_BF16

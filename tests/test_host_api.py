@@ -95,7 +95,8 @@ def _select(lib, p, **over):
                 row_ptr=FAKE, block_idx=FAKE, cap=L.csr_capacity(p), ts=None, tm=None, rb=None,
                 ws=ctypes.c_void_p(0x200000), ws_bytes=L.select_workspace_bytes(p, 8))
     args.update(over)
-    return lib.poem_select(ctypes.byref(cp), args["q"], args["k"], args["v"], args["tau"], args["sink"],
+    fn = getattr(lib, args.pop("fn", "poem_select"))
+    return fn(ctypes.byref(cp), args["q"], args["k"], args["v"], args["tau"], args["sink"],
                            args["local"], args["S"], args["row_ptr"], args["block_idx"], args["cap"], args["ts"],
                            args["tm"], args["rb"], args["ws"], args["ws_bytes"], None)
 
@@ -116,12 +117,15 @@ def test_select_validation(lib):
         (dict(S=33), L.POEM_ERR_UNSUPPORTED),
         (dict(cap=L.csr_capacity(p) - 1), L.POEM_ERR_CAPACITY),
         (dict(ws=None), L.POEM_ERR_WORKSPACE),
-        (dict(ws_bytes=L.select_workspace_bytes(p, 8) - 1), L.POEM_ERR_WORKSPACE),
+        (dict(ws_bytes=4096), L.POEM_ERR_WORKSPACE),
         (dict(ws=ctypes.c_void_p(0x200010)), L.POEM_ERR_WORKSPACE),
     ]
-    for over, status in cases:
-        assert _select(lib, p, **over) == status, over
-        assert lib.poem_last_error().decode() != ""
+    for fn in ("poem_select", "poem_select_mass", "poem_select_group"):
+        for over, status in cases:
+            assert _select(lib, p, fn=fn, **over) == status, (fn, over)
+            assert lib.poem_last_error().decode() != ""
+    # per-head lists use the largest layout, which the reported size covers exactly
+    assert _select(lib, p, ws_bytes=L.select_workspace_bytes(p, 8) - 1) == L.POEM_ERR_WORKSPACE
 
 
 def test_select_limits(lib):
@@ -129,7 +133,12 @@ def test_select_limits(lib):
     p = prob(num_heads_q=16, num_heads_kv=1)
     assert L.select_workspace_bytes(p, 8) > 0
     cp = p.c()
-    assert lib.poem_select_workspace_bytes(ctypes.byref(cp), 16) == L.POEM_ERR_UNSUPPORTED
+    # per-head lists are not built for 256 columns; a group-shared list has S columns
+    ws16 = lib.poem_select_workspace_bytes(ctypes.byref(cp), 16)
+    assert ws16 > 0
+    assert _select(lib, p, S=16, ws_bytes=ws16) == L.POEM_ERR_UNSUPPORTED
+    assert _select(lib, p, S=16, ws_bytes=ws16 - 256, fn="poem_select_group") == L.POEM_ERR_WORKSPACE
+    assert _select(lib, p, S=16, ws_bytes=ws16 - 256, fn="poem_select_mass") == L.POEM_ERR_UNSUPPORTED
     # more than POEM_MAX_VISIBLE_BLOCKS blocks visible to a tile
     big = prob(seqlens_q=[64], seqlens_k=[64 * 5000])
     assert _select(lib, big) == L.POEM_ERR_UNSUPPORTED
