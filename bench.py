@@ -168,21 +168,24 @@ def sampled_row_index(gp, S):
     return np.array(rows, np.int64), np.array(tiles, np.int64)
 
 
-def mass_only_leg(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
-    """The mass-only selector beside POEM: its latency at a fixed budget, then POEM and
-    mass-only at matched per-head keep fraction (the mass budget of each head bisected
-    until its kept-block count matches POEM's) and the output errors of both against
-    dense attention, over every query row and over the sampled rows."""
+def _err_stats(e, si, tau):
+    """Row errors e [rows, H]: mean, rms, p99 (on up to 4M rows), max, and the share of
+    the selector's sampled rows si whose error is within their head's tau."""
     import torch
-    H = w.num_heads_q
-    T = L.num_tiles(gp)
+    f = e.flatten()
+    sub = f[torch.randperm(f.numel(), device=f.device)[:1 << 22]]
+    return {"mean": float(f.mean()), "rms": float(torch.sqrt((f * f).mean())),
+            "p99": float(torch.quantile(sub, 0.99)), "max": float(f.max()),
+            "sampled_rows_within_tau": float((e[si] <= tau[None, :]).float().mean())}
+
+
+def _time_select_sparse(gp, L, w, q, k, v, ws, sws, taus, mode, steps):
+    import torch
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
-    eps0 = [args.mass_eps] * H
     r = None
     for i in range(steps):
         ev[i][0].record()
-        r = L.select(gp, q, k, v, eps0, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
-                     mode="mass")
+        r = L.select(gp, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws, mode=mode)
         ev[i][1].record()
         L.sparse_prefill(gp, q, k, v, r["row_ptr"], r["block_idx"], out_dtype="bf16", want_lse=False,
                          workspace=sws)
@@ -190,60 +193,79 @@ def mass_only_leg(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
     torch.cuda.synchronize()
     t_sel = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
     t_sp = float(np.median([ev[i][1].elapsed_time(ev[i][2]) for i in range(steps)]))
+    return r, t_sel, t_sp
+
+
+def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
+    """The other selectors beside POEM's per-head one, on the same inputs:
+    - mass-only: latency at a fixed budget, then POEM and mass-only at matched per-head
+      keep fraction (each head's mass budget bisected until its kept-block count
+      matches POEM's), with the output errors of both against dense attention;
+    - group-shared lists: latency at the same thresholds, keep fraction and errors.
+    Errors are ||O_sparse - O_dense|| per query row with fp32 outputs."""
+    import torch
+    H = w.num_heads_q
+    T = L.num_tiles(gp)
     cap = L.csr_capacity(gp)
-    kept0 = int(r["row_ptr"][-1].item())
-
-    vis = (np.diff(rp_poem).reshape(H, T).sum(1))  # POEM kept blocks per head
-    lo = np.full(H, -9.0)
-    hi = np.zeros(H)
-    best = [None] * H
-    for _ in range(24):
-        mid = 0.5 * (lo + hi)
-        rr = L.select(gp, q, k, v, list(10.0 ** mid), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
-                      workspace=ws, mode="mass")
-        kept = np.diff(rr["row_ptr"].cpu().numpy().astype(np.int64)).reshape(H, T).sum(1)
-        for h in range(H):
-            gap = abs(int(kept[h]) - int(vis[h]))
-            if best[h] is None or gap < best[h][0]:
-                best[h] = (gap, float(10.0 ** mid[h]))
-        more = kept > vis  # keeps too much: raise the budget
-        lo = np.where(more, mid, lo)
-        hi = np.where(more, hi, mid)
-    eps_m = [b[1] for b in best]
-    rm = L.select(gp, q, k, v, eps_m, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
-                  mode="mass")
-    rpm = rm["row_ptr"].cpu().numpy().astype(np.int64)
-    rp_t = torch.from_numpy(rp_poem.astype(np.int32)).cuda()
-    # POEM's CSR is reproduced by re-running its selector with the bench's thresholds
-    rpo = L.select(gp, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws)
-    assert torch.equal(rpo["row_ptr"], rp_t)
-    od, _ = L.dense_prefill(gp, q, k, v, out_dtype="fp32", want_lse=False)
-    op_, _ = L.sparse_prefill(gp, q, k, v, rpo["row_ptr"], rpo["block_idx"], out_dtype="fp32", want_lse=False,
-                              workspace=sws)
-    om, _ = L.sparse_prefill(gp, q, k, v, rm["row_ptr"], rm["block_idx"], out_dtype="fp32", want_lse=False,
-                             workspace=sws)
-    e_p = torch.linalg.vector_norm(op_ - od, dim=-1)  # [rows, H]
-    e_m = torch.linalg.vector_norm(om - od, dim=-1)
-    del od, op_, om
-    srow, stile = sampled_row_index(gp, w.rows_per_tile)
-    tau = torch.tensor([float(x) for x in inp.tau], device=e_p.device)
+    srow, _ = sampled_row_index(gp, w.rows_per_tile)
     si = torch.from_numpy(srow).cuda()
+    tau = torch.tensor([float(x) for x in inp.tau], device="cuda")
+    od, _ = L.dense_prefill(gp, q, k, v, out_dtype="fp32", want_lse=False)
 
-    def stats(e):
-        f = e.flatten()
-        return {"mean": float(f.mean()), "rms": float(torch.sqrt((f * f).mean())),
-                "p99": float(torch.quantile(f[torch.randperm(f.numel(), device=f.device)[:1 << 22]], 0.99)),
-                "max": float(f.max()),
-                "sampled_rows_within_tau": float((e[si] <= tau[None, :]).float().mean())}
+    def errors(rr):
+        o, _ = L.sparse_prefill(gp, q, k, v, rr["row_ptr"], rr["block_idx"], out_dtype="fp32", want_lse=False,
+                                workspace=sws)
+        e = torch.linalg.vector_norm(o - od, dim=-1)
+        del o
+        return e
 
-    res = {"eps": args.mass_eps, "select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": kept0 / cap,
-           "matched_keep": {
-               "keep_fraction_blocks_poem": float(rp_poem[-1]) / cap, "keep_fraction_blocks_mass": float(rpm[-1]) / cap,
-               "eps_per_head": [float("%.4g" % e) for e in eps_m],
-               "err_poem": stats(e_p), "err_mass": stats(e_m),
-               "note": "row error = ||O_sparse - O_dense||_2 over all query rows (fp32 outputs); "
-                       "sampled_rows_within_tau = share of the selector's sampled rows with error <= tau_h"}}
-    return res
+    # POEM's CSR again (the same thresholds reproduce it exactly)
+    rpo = L.select(gp, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws)
+    assert torch.equal(rpo["row_ptr"], torch.from_numpy(rp_poem.astype(np.int32)).cuda())
+    e_p = errors(rpo)
+    out = {"err_poem": _err_stats(e_p, si, tau)}
+    del e_p
+
+    res_m = {}
+    if not args.no_mass:
+        r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "mass", steps)
+        res_m = {"eps": args.mass_eps, "select_ms": t_sel, "sparse_ms": t_sp,
+                 "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
+        vis = np.diff(rp_poem).reshape(H, T).sum(1)  # POEM's kept blocks per head
+        lo, hi = np.full(H, -9.0), np.zeros(H)
+        best = [None] * H
+        for _ in range(24):
+            mid = 0.5 * (lo + hi)
+            rr = L.select(gp, q, k, v, list(10.0 ** mid), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
+                          workspace=ws, mode="mass")
+            kept = np.diff(rr["row_ptr"].cpu().numpy().astype(np.int64)).reshape(H, T).sum(1)
+            for h in range(H):
+                gap = abs(int(kept[h]) - int(vis[h]))
+                if best[h] is None or gap < best[h][0]:
+                    best[h] = (gap, float(10.0 ** mid[h]))
+            more = kept > vis  # keeps too much: raise the budget
+            lo = np.where(more, mid, lo)
+            hi = np.where(more, hi, mid)
+        eps_m = [b[1] for b in best]
+        rm = L.select(gp, q, k, v, eps_m, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
+                      mode="mass")
+        e_m = errors(rm)
+        res_m["matched_keep"] = {
+            "keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
+            "keep_fraction_blocks_mass": float(rm["row_ptr"][-1].item()) / cap,
+            "eps_per_head": [float("%.4g" % e) for e in eps_m],
+            "err_poem": out["err_poem"], "err_mass": _err_stats(e_m, si, tau)}
+        del e_m
+
+    r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, inp.tau, "group", steps)
+    e_g = errors(r)
+    res_g = {"select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap,
+             "err_group": _err_stats(e_g, si, tau), "err_poem": out["err_poem"],
+             "note": "same per-head thresholds as the headline step; one list per (KV head, tile) from the "
+                     "group's 8 sampled rows; sampled_rows_within_tau is taken on the per-head selector's rows"}
+    del od, e_g
+    torch.cuda.empty_cache()
+    return res_m, res_g
 
 
 def main():
@@ -256,6 +278,7 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-legs", action="store_true", help="skip the mass-only and group-shared selector legs")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-only selector leg")
     ap.add_argument("--mass-eps", type=float, default=0.002, help="omitted-mass budget of the mass-only leg")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -406,9 +429,12 @@ def main():
         "keep_fraction_pairs": p_ret / p_dense,
         "roofline": roofline,
     }
-    if not args.no_mass and inp.is_bf16:
-        log("[bench] mass-only selector leg")
-        res["mass_only"] = mass_only_leg(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
+    if not args.no_legs and inp.is_bf16:
+        log("[bench] mass-only and group-shared selector legs")
+        res_m, res_g = selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
+        if res_m:
+            res["mass_only"] = res_m
+        res["group_shared"] = res_g
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds)
