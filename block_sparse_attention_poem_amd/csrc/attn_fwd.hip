@@ -158,6 +158,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     constexpr int NPV = 4 * NDT;       // P V MFMAs per stage (4 key steps x d tiles)
     constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
     constexpr int XPM = 32 / NPV;      // max candidates per P V MFMA
+    // The row sums add the bf16 weights the P V MFMAs use (two per dot instruction), so
+    // numerator and denominator see the same rounding.
     f32x16 Sp[2];
     auto kfrag = [&](const char* kbuf, int i) {  // K operand of QK MFMA i
       const int kt = i & 1, st = i >> 1;
@@ -213,12 +215,15 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 #pragma unroll
         for (int u = 0; u < EPM; ++u) {
           const int e = i * EPM + u;
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
-          Sp[e >> 4][e & 15] = x;
-          rs += x;
+          Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
           if ((e & 7) == 7) {
             bf16x8 unused;
             p_step<false>(Sp, e >> 3, P[e >> 3], unused);
+            rs = row_sum_bf16(P[e >> 3], rs);
+            // Sparse rows: keep the sum in this chunk (an empty statement, no code); left
+            // free, the compiler sinks it past the mask branch. Measured either way at
+            // 128K: pinned is faster for the sparse kernel and slower for the dense one.
+            if constexpr (SPARSE) __asm__ volatile("" : "+v"(rs));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
@@ -259,10 +264,16 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         step(it, kb1, kb0, vb0, vb1);
         if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
       }
-      exps(Sp);
       bf16x8 P[4], unused;
+      float rs = 0.f;
 #pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4) p_step<false>(Sp, s4, P[s4], unused);
+      for (int e = 0; e < 32; ++e) Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
+#pragma unroll
+      for (int s4 = 0; s4 < 4; ++s4) {
+        p_step<false>(Sp, s4, P[s4], unused);
+        rs = row_sum_bf16(P[s4], rs);
+      }
+      l_run += rs;
       St::pv_packed(((total - 1) & 1) ? vb1 : vb0, P, O, lane);
     }
   } else {
