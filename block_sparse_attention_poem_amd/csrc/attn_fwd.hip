@@ -229,7 +229,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += rs;
-      // PV phase (the max is taken over the raw scores; masked stages redo it below)
+      // PV phase (the max is taken over the raw scores; masked stages redo it below). The
+      // wave issues at raised priority here, so the MFMA-heavy phase of one wave gets the
+      // issue slots ahead of the VALU-heavy phase of the other wave on its SIMD.
+      __builtin_amdgcn_s_setprio(1);
       bf16x8 va[3];
       va[0] = St::v_frag(vprev, 0, 0, lane);
       va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
@@ -252,6 +255,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 #pragma unroll
         for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
       }
+      __builtin_amdgcn_s_setprio(0);
       finish_max(mx);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
