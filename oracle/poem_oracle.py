@@ -31,6 +31,10 @@ Readings where the pages are silent (each listed in the design doc):
     (N_k - N_q) is a multiple of the block size.
   * Mass-only baseline: rank by the tile mass; cut at the last prefix whose
     largest per-row omitted mass is <= eps (the per-head budget).
+  * Practical POEM: pooled estimates mbar and Ibar / mbar, preselection of the
+    shortest top-mass prefix covering rho of the candidates' mass, rerank by
+    log mbar + w log(Ibar / mbar), keep in that order until the pooled retained
+    mass reaches (1 - eps) of the total.
   * Group-shared lists: the S sampled rows of a (KV head, tile) are spread over
     its G query heads (row j from head g G + j mod G); every sampled row's bound
     must stay within its own head's tau.
@@ -439,11 +443,102 @@ def select_tile_group(p: Problem, q, k, v, g: int, tile: Tile, tau, n_sink: int,
                          per_row, ks, retained, heads)
 
 
-def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=None, mode: str = "poem"):
+# ---------------------------------------------------------------------------
+# Practical POEM ([note] Equation (6) and its selection procedure, Appendix B):
+# estimates of block mass and output deviation, a mass preselection, a rerank by
+# log mass plus a weighted log deviation, and a retention threshold on pooled mass
+# accumulated in the reranked order.
+# Readings (the pages leave these open):
+#   estimates   pooled over the sampled rows: mbar_b (mean mass) and the deviation
+#               dhat_b = Ibar_b / mbar_b, the mass-weighted mean of ||v_ib - o_i||;
+#   preselect   the shortest prefix of the candidates in (mbar descending, id
+#               ascending) order whose mass reaches rho times the candidates' mass;
+#   rerank      the preselected blocks by log mbar_b + w log dhat_b, descending (a
+#               block with zero mass, or with zero deviation when w != 0, scores
+#               -inf; with w = 0 the deviation term is absent), smaller id first
+#               among equal scores;
+#   threshold   blocks are kept in that order until the pooled retained mass
+#               (mandatory blocks included) reaches (1 - eps) of the pooled total.
+# w, rho and the per-head eps are parameters.
+# ---------------------------------------------------------------------------
+
+
+def practical_keys(mbar, Ibar, w: float):
+    """Rerank score log mbar + w log(Ibar / mbar) per block: -inf for a block with no
+    mass, or (when w != 0) with no deviation; with w = 0 the deviation term is absent."""
+    mbar = np.asarray(mbar, dtype=np.float64)
+    Ibar = np.asarray(Ibar, dtype=np.float64)
+    out = np.full(len(mbar), -np.inf)
+    okm = mbar > 0
+    out[okm] = np.log(mbar[okm])
+    if w != 0.0:
+        okI = okm & (Ibar > 0)
+        out[okm & ~okI] = -np.inf
+        out[okI] += w * np.log(Ibar[okI] / mbar[okI])
+    return out
+
+
+def practical_retain(mbar, Ibar, mandatory, candidates, eps: float, w: float, rho: float):
+    """The practical selection from pooled estimates. Returns (preselected, reranked
+    order, kept candidates)."""
+    mbar = np.asarray(mbar, dtype=np.float64)
+    by_mass = sorted(candidates, key=lambda b: (-float(mbar[b]), int(b)))
+    cum = np.cumsum([mbar[b] for b in by_mass]) if by_mass else np.zeros(0)
+    need = rho * (cum[-1] if len(cum) else 0.0)
+    n_pre = 0
+    while n_pre < len(by_mass) and (n_pre == 0 or cum[n_pre - 1] < need):
+        n_pre += 1
+    if len(cum) and need <= 0.0:
+        n_pre = 0
+    pre = by_mass[:n_pre]
+    key = practical_keys(mbar, Ibar, w)
+    order = sorted(pre, key=lambda b: (-float(key[b]), int(b)))
+    target = (1.0 - eps) * float(mbar.sum())
+    acc = float(sum(mbar[b] for b in mandatory))
+    kept = []
+    for b in order:
+        if acc >= target:
+            break
+        kept.append(b)
+        acc += float(mbar[b])
+    return pre, order, kept
+
+
+def select_tile_practical(p: Problem, q, k, v, h: int, tile: Tile, eps: float, n_sink: int, n_local: int,
+                          S: int, w: float = 0.5, rho: float = 0.95) -> TileSelection:
+    """Practical POEM for one (query head, tile). `order` holds the reranked
+    preselected blocks, `score` the rerank score, `per_row` the per-row omitted mass of
+    the final discard set (one row), k_star the number of discarded candidates."""
+    g = h // p.group
+    K = _head_view(k, tile.k_row0, tile.n_k, g)
+    V = _head_view(v, tile.k_row0, tile.n_k, g)
+    n_vis = tile.diag + 1
+    rows = sampled_rows(tile.n_rows, S)
+    stats = [row_block_stats(q[tile.q_row0 + r, h, :], K, V, p.scale, tile.pos0 + r, n_vis, p.block_size)
+             for r in rows]
+    I = np.stack([st["I"] for st in stats])
+    m = np.stack([st["m"] for st in stats])
+    Ibar = I.mean(axis=0)
+    mbar = m.mean(axis=0)
+    mand = mandatory_blocks(tile.diag, n_sink, n_local)
+    cand = [b for b in range(n_vis) if b not in set(mand)]
+    pre, order, kept = practical_retain(mbar, Ibar, mand, cand, float(eps), float(w), float(rho))
+    retained = sorted(set(mand) | set(kept))
+    drop = [b for b in range(n_vis) if b not in set(retained)]
+    omitted = m[:, drop].sum(axis=1) if drop else np.zeros(len(rows))
+    return TileSelection(h, tile, rows, I, m, np.array([st["lse"] for st in stats]),
+                         np.stack([st["o"] for st in stats]), practical_keys(mbar, Ibar, w), mbar, mand, order,
+                         np.zeros(0), omitted[None, :], len(drop), retained)
+
+
+def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=None, mode: str = "poem",
+           practical=None):
     """Selections for every (head, tile), or for the (h, gtile) pairs in `which`.
     mode "poem" uses the output-relative selector (tau: error threshold per head),
     "mass" the mass-only one (tau: omitted-mass budget per head), "group" the
-    group-shared output-relative selector (one list per KV head and tile).
+    group-shared output-relative selector (one list per KV head and tile),
+    "practical" practical POEM (tau: pooled omitted-mass budget per head;
+    practical = dict(w=..., rho=...)).
 
     Returns {(h, gtile): TileSelection}."""
     tl = tiles(p)
@@ -459,6 +554,10 @@ def select(p: Problem, q, k, v, tau, n_sink: int, n_local: int, S: int, which=No
                 shared[key] = select_tile_group(p, q, k, v, key[0], tl[gt], tau, n_sink, n_local, S)
             out[(h, gt)] = shared[key]
         return out
+    if mode == "practical":
+        return {(h, gt): select_tile_practical(p, q, k, v, h, tl[gt], float(tau[h]), n_sink, n_local, S,
+                                               **(practical or {}))
+                for (h, gt) in which}
     fn = {"poem": select_tile, "mass": select_tile_mass}[mode]
     return {(h, gt): fn(p, q, k, v, h, tl[gt], float(tau[h]), n_sink, n_local, S)
             for (h, gt) in which}

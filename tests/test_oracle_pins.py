@@ -532,6 +532,80 @@ def test_group_of_one_is_the_per_head_selector():
             assert np.array_equal(a[key].score, b[key].score)
 
 
+# --- practical POEM ---------------------------------------------------------------------
+
+
+def _random_pooled(rng, n):
+    mbar = rng.dirichlet(np.ones(n + 2))  # the last two entries play the mandatory blocks
+    Ibar = mbar * rng.uniform(0.5, 20.0, n + 2) * (rng.uniform(0, 1, n + 2) < 0.9)
+    if rng.uniform() < 0.3:
+        mbar = np.round(mbar, 2)
+        mbar = mbar / mbar.sum()
+    return mbar, Ibar
+
+
+def pin_practical_selection():
+    """Practical POEM from pooled estimates, against brute force on <= 10 candidates:
+    the preselection is the fewest candidates whose mass reaches rho of theirs (a
+    largest-mass prefix); the rerank is non-increasing in log m + w log(I / m) with
+    math.log; the kept prefix is the shortest one whose pooled mass, with the
+    mandatory blocks, reaches (1 - eps) of the total; with w = 0 and rho = 1 the
+    kept set is the fewest candidates that do so (subset brute force)."""
+    import itertools
+    rng = np.random.default_rng(51)
+    for _ in range(300):
+        n = int(rng.integers(1, 11))
+        mbar, Ibar = _random_pooled(rng, n)
+        mand = [n, n + 1]
+        cand = list(range(n))
+        eps = float(rng.uniform(0, 0.3))
+        w = float(rng.choice([0.0, 0.5, 1.0, 2.0]))
+        rho = float(rng.choice([1.0, 0.9, 0.6]))
+        pre, order, kept = O.practical_retain(mbar, Ibar, mand, cand, eps, w, rho)
+        tot_c = math.fsum(mbar[b] for b in cand)
+        fewest = min(len(D) for r in range(n + 1) for D in itertools.combinations(cand, r)
+                     if math.fsum(mbar[b] for b in D) >= rho * tot_c - 1e-15)
+        assert len(pre) == fewest or tot_c == 0.0
+        assert math.fsum(mbar[b] for b in pre) >= rho * tot_c - 1e-12
+        assert sorted(order) == sorted(pre)
+
+        def key(b):
+            if mbar[b] <= 0 or (w != 0.0 and Ibar[b] <= 0):
+                return -math.inf
+            return math.log(mbar[b]) + (w * math.log(Ibar[b] / mbar[b]) if w != 0.0 else 0.0)
+        for a, b in zip(order, order[1:]):
+            assert key(a) > key(b) or (key(a) == key(b) and a < b)
+        target = (1 - eps) * math.fsum(mbar)
+        base = math.fsum(mbar[b] for b in mand)
+        assert kept == order[:len(kept)]
+        if len(kept) < len(order):
+            assert base + math.fsum(mbar[b] for b in kept) >= target - 1e-12
+        if kept:
+            assert base + math.fsum(mbar[b] for b in kept[:-1]) < target + 1e-12
+        if w == 0.0 and rho == 1.0:
+            need = min((len(D) for r in range(n + 1) for D in itertools.combinations(cand, r)
+                        if base + math.fsum(mbar[b] for b in D) >= target - 1e-15), default=n)
+            assert len(kept) == need
+
+
+def test_practical_selection():
+    pin_practical_selection()
+
+
+def test_practical_on_tiny_problems():
+    """End to end on tiny problems: the mandatory blocks are kept, the list is
+    ascending, and the pooled omitted mass is within eps whenever some preselected
+    block was dropped."""
+    p, q, k, v = _tiny_problem(82, sink=9.0)
+    for eps in (0.001, 0.02, 0.2):
+        sel = O.select(p, q, k, v, [eps] * 2, 1, 1, 8, mode="practical", practical=dict(w=0.5, rho=0.95))
+        for (h, gt), s in sel.items():
+            assert set(s.mandatory) <= set(s.retained) and s.retained == sorted(s.retained)
+            dropped_pre = [b for b in s.order if b not in set(s.retained)]
+            if dropped_pre:
+                assert s.per_row[0].mean() <= eps + 1e-12
+
+
 def test_gpu_toy_geometry_in_oracle():
     """The toy realised at block granularity (B = 64, d = 64, fp32, scale 1): blocks
     0, 1, 2, 3 with masses 1/2, 1/4, 1/4, ~0 and values 2, 0, 4, 0 along e_0; the
@@ -638,7 +712,25 @@ def _group_curve_loosest_tau(I_rows, m_rows, order, row_tau):
     return per_row.max(axis=1) - max(row_tau), per_row
 
 
+def _practical_rerank_ascending(mbar, Ibar, mandatory, candidates, eps, w, rho):
+    pre, order, kept = _orig_practical(mbar, Ibar, mandatory, candidates, eps, w, rho)
+    order = order[::-1]
+    target = (1.0 - eps) * float(np.sum(mbar))
+    acc = float(sum(mbar[b] for b in mandatory))
+    kept = []
+    for b in order:
+        if acc >= target:
+            break
+        kept.append(b)
+        acc += float(mbar[b])
+    return pre, order, kept
+
+
+_orig_practical = O.practical_retain
+
+
 @pytest.mark.parametrize("name,fn,pins", [
+    ("practical_retain", _practical_rerank_ascending, ["practical"]),
     ("group_excess_curve", _group_curve_loosest_tau, ["group_cut", "group_selection"]),
     ("mass_curve", _mass_curve_mean_rows, ["mass_cut"]),
     ("select_tile_mass", _mass_selector_ranks_by_proxy, ["mass_selection"]),
@@ -663,6 +755,7 @@ def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
         "mass_cut": pin_mass_cut,
         "mass_selection": pin_mass_selection,
         "group_cut": pin_group_cut,
+        "practical": pin_practical_selection,
         "group_selection": pin_group_selection,
     }
     monkeypatch.setattr(O, name, fn)
