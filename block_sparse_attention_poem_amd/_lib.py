@@ -21,7 +21,7 @@ POEM_BF16, POEM_FP32 = 0, 1
 STATUS_NAMES = {0: "POEM_OK", -1: "POEM_ERR_INVALID_ARG", -2: "POEM_ERR_UNSUPPORTED", -3: "POEM_ERR_WORKSPACE",
                 -4: "POEM_ERR_CAPACITY", -5: "POEM_ERR_HIP"}
 SYMBOLS = ["poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_select_workspace_bytes",
-           "poem_sparse_workspace_bytes", "poem_select", "poem_select_mass", "poem_select_group",
+           "poem_sparse_workspace_bytes", "poem_select", "poem_select_mass", "poem_select_group", "poem_select_practical",
            "poem_sparse_prefill", "poem_dense_prefill",
            "poem_last_error", "poem_version"]
 
@@ -74,6 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.poem_select_mass.restype = ctypes.c_int
     lib.poem_select_group.argtypes = lib.poem_select.argtypes
     lib.poem_select_group.restype = ctypes.c_int
+    lib.poem_select_practical.argtypes = [P, vp, vp, vp, f32p, i32, i32, i32, ctypes.c_float, ctypes.c_float, vp,
+                                          vp, i64, vp, vp, vp, vp, ctypes.c_size_t, vp]
+    lib.poem_select_practical.restype = ctypes.c_int
     lib.poem_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.poem_sparse_prefill.restype = ctypes.c_int
     lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp]
@@ -214,10 +217,12 @@ class SparseWorkspace(Workspace):
 
 def select(problem: Problem, q, k, v, tau, n_sink_blocks: int = 1, n_local_blocks: int = 1,
            rows_per_tile: int = 8, diagnostics: bool = False, workspace: Optional[SelectWorkspace] = None,
-           stream=None, mode: str = "poem"):
+           stream=None, mode: str = "poem", weight: float = 0.5, presel_fraction: float = 0.95):
     """Run poem_select (mode "poem", tau: error threshold per head), poem_select_mass
     (mode "mass", tau: omitted-mass budget per head) or poem_select_group (mode "group":
-    one list per KV head and tile; rows_per_tile counts the group's sampled rows).
+    one list per KV head and tile; rows_per_tile counts the group's sampled rows) or
+    poem_select_practical (mode "practical", tau: pooled omitted-mass budget per head,
+    with weight and presel_fraction).
     Returns dict(row_ptr, block_idx[, tile_scores, tile_mass, row_bound])."""
     torch = _torch()
     _check_qkv(problem, q, k, v)
@@ -238,10 +243,15 @@ def select(problem: Problem, q, k, v, tau, n_sink_blocks: int = 1, n_local_block
         rb = torch.empty((problem.num_heads_q, T, rows_per_tile), dtype=torch.float32, device=dev)
         out.update(tile_scores=sc, tile_mass=ms, row_bound=rb)
     ws = workspace if workspace is not None else SelectWorkspace(problem, rows_per_tile, dev)
-    fn = {"poem": lib.poem_select, "mass": lib.poem_select_mass, "group": lib.poem_select_group}[mode]
-    _check(fn(ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), tau_arr, int(n_sink_blocks), int(n_local_blocks),
-              int(rows_per_tile), _ptr(row_ptr), _ptr(block_idx), cap, _ptr(sc), _ptr(ms), _ptr(rb),
-              ctypes.c_void_p(ws.ptr), ws.nbytes, _stream_ptr(stream)))
+    tail = (_ptr(row_ptr), _ptr(block_idx), cap, _ptr(sc), _ptr(ms), _ptr(rb), ctypes.c_void_p(ws.ptr), ws.nbytes,
+            _stream_ptr(stream))
+    head = (ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), tau_arr, int(n_sink_blocks), int(n_local_blocks),
+            int(rows_per_tile))
+    if mode == "practical":
+        _check(lib.poem_select_practical(*head, float(weight), float(presel_fraction), *tail))
+    else:
+        fn = {"poem": lib.poem_select, "mass": lib.poem_select_mass, "group": lib.poem_select_group}[mode]
+        _check(fn(*head, *tail))
     out["_workspace"] = ws
     return out
 

@@ -196,7 +196,7 @@ int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_pe
   return (int64_t)bytes;
 }
 
-static poem_status select_impl(int mode, bool group_mode, const poem_problem* problem, const void* q, const void* k, const void* v,
+static poem_status select_impl(int mode, bool group_mode, float prac_w, float prac_rho, const poem_problem* problem, const void* q, const void* k, const void* v,
                                const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks,
                                int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                                int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
@@ -249,6 +249,8 @@ static poem_status select_impl(int mode, bool group_mode, const poem_problem* pr
   sp.n_local = n_local_blocks;
   sp.max_vis = (int32_t)g.max_vis;
   sp.mode = mode;
+  sp.prac_w = prac_w;
+  sp.prac_rho = prac_rho;
   sp.scale_log2 = g.scale * poem::kLog2e;
   for (int h = 0; h < problem->num_heads_q; ++h) sp.tau[h] = tau_host[h];
   char* ws = static_cast<char*>(workspace);
@@ -271,7 +273,7 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         const float* tau_host, int32_t n_sink_blocks, int32_t n_local_blocks, int32_t rows_per_tile,
                         int32_t* row_ptr, int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
                         float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(poem::kSelectOutputRelative, false, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
+  return select_impl(poem::kSelectOutputRelative, false, 0.f, 1.f, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
                      rows_per_tile, row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound,
                      workspace, workspace_bytes, stream);
 }
@@ -281,9 +283,23 @@ poem_status poem_select_group(const poem_problem* problem, const void* q, const 
                               int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                               int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
                               void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(poem::kSelectOutputRelative, true, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
+  return select_impl(poem::kSelectOutputRelative, true, 0.f, 1.f, problem, q, k, v, tau_host, n_sink_blocks, n_local_blocks,
                      rows_per_tile, row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound,
                      workspace, workspace_bytes, stream);
+}
+
+poem_status poem_select_practical(const poem_problem* problem, const void* q, const void* k, const void* v,
+                                  const float* eps_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                                  int32_t rows_per_tile, float weight, float presel_fraction, int32_t* row_ptr,
+                                  int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
+                                  float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes,
+                                  void* stream) {
+  if (!isfinite(weight)) return fail(POEM_ERR_INVALID_ARG, "weight must be finite");
+  if (!(presel_fraction > 0.f && presel_fraction <= 1.f))
+    return fail(POEM_ERR_INVALID_ARG, "presel_fraction must be in (0, 1] (got %g)", (double)presel_fraction);
+  return select_impl(poem::kSelectPractical, false, weight, presel_fraction, problem, q, k, v, eps_host,
+                     n_sink_blocks, n_local_blocks, rows_per_tile, row_ptr, block_idx, block_idx_capacity,
+                     tile_scores, tile_mass, row_bound, workspace, workspace_bytes, stream);
 }
 
 poem_status poem_select_mass(const poem_problem* problem, const void* q, const void* k, const void* v,
@@ -291,7 +307,7 @@ poem_status poem_select_mass(const poem_problem* problem, const void* q, const v
                              int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                              int64_t block_idx_capacity, float* tile_scores, float* tile_mass, float* row_bound,
                              void* workspace, size_t workspace_bytes, void* stream) {
-  return select_impl(poem::kSelectMass, false, problem, q, k, v, eps_host, n_sink_blocks, n_local_blocks, rows_per_tile,
+  return select_impl(poem::kSelectMass, false, 0.f, 1.f, problem, q, k, v, eps_host, n_sink_blocks, n_local_blocks, rows_per_tile,
                      row_ptr, block_idx, block_idx_capacity, tile_scores, tile_mass, row_bound, workspace,
                      workspace_bytes, stream);
 }

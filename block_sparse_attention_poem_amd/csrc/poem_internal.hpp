@@ -37,6 +37,7 @@ hipError_t launch_attention(const AttnParams& p, int in_dtype, int head_dim, int
 // bound) and the mass-only baseline (ranking by mean m, cut on omitted mass).
 constexpr int kSelectOutputRelative = 0;
 constexpr int kSelectMass = 1;
+constexpr int kSelectPractical = 2;  // practical POEM: mass preselection, log rerank, pooled mass
 
 struct SelectParams {
   const void* q;
@@ -47,7 +48,8 @@ struct SelectParams {
   int32_t col_tiles;         // 32-column tiles per (KV head, tile)
   int32_t n_sink, n_local;
   int32_t max_vis;
-  int32_t mode;              // kSelectOutputRelative or kSelectMass
+  int32_t mode;              // kSelectOutputRelative, kSelectMass or kSelectPractical
+  float prac_w, prac_rho;    // practical POEM: deviation weight, preselected mass fraction
   // column layout of the per-(KV head, tile) records. Per-head lists: column
   // f = hg * S + j (row j of head g G + hg), cols_rec = 32 * col_tiles, one tile per
   // wave. Group-shared lists (group_mode): column j is row j of head g G + j mod G,

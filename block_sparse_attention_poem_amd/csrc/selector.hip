@@ -517,13 +517,198 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   if (tid < w.nh) p.counts[(w.h0 + tid) * T + w.gtile] = total;
 }
 
+template <int V> struct IntTag { static constexpr int value = V; };
+
+// float -> uint32 whose unsigned order is the float order (-inf lowest)
+__device__ __forceinline__ uint32_t ordered_bits(float f) {
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Inclusive prefix over the workgroup of one double per position, positions held in
+// blocked order (E per thread): x[e] becomes the sum over positions <= tid * E + e.
+// Returns the total.
+template <int E>
+__device__ __forceinline__ double blocked_inclusive_scan(double (&x)[E], double* shd, double* total_sh) {
+  double run = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) { run += x[e]; x[e] = run; }
+  double a[1] = {run}, d[1] = {0.0};
+  block_excl_scan_vec<1>(a, d, shd);  // a: this thread's exclusive offset
+#pragma unroll
+  for (int e = 0; e < E; ++e) x[e] += a[0];
+  if (threadIdx.x == kThrThreads - 1) *total_sh = x[E - 1];  // the last position holds the total
+  __syncthreads();
+  const double total = *total_sh;
+  __syncthreads();
+  return total;
+}
+
+// Practical POEM for one (query head, tile): pooled estimates, a mass preselection,
+// a rerank by log mbar + w log(Ibar / mbar), and blocks kept in that order until the
+// pooled retained mass reaches (1 - eps) of the pooled total (POEM note Equation (6)
+// and its selection procedure). Two register sorts and two fp64 prefix scans.
+template <bool STAGED, int E>
+__device__ __forceinline__ void practical_tile(const SelectParams& p, const ThrTile& w, const float* st_I,
+                                               const float* st_m, float* bar_I, float* bar_m, uint64_t* sh,
+                                               uint8_t* keep, double* shd, int* shi) {
+  __shared__ double sums[2];
+  const int tid = threadIdx.x;
+  const int T = p.seqs.total_tiles;
+  const int S = w.S, s_t = w.s_t, n_vis = w.n_vis, diag = w.diag;
+  auto I_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_I[b * S + i];
+    else return w.Ib[(int64_t)b * w.bstride + i];
+  };
+  auto m_of = [&](int b, int i) -> float {
+    if constexpr (STAGED) return st_m[b * S + i];
+    else return w.Mb[(int64_t)b * w.bstride + i];
+  };
+  auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
+  const float inv_s = 1.f / (float)s_t;
+  const float wt = p.prac_w;
+  const int64_t diag_row = ((int64_t)w.h0 * T + w.gtile) * p.max_vis;
+  // natural-log rerank key of a block (-inf without mass, or without deviation if w != 0)
+  auto rerank_key = [&](float mb, float ib) {
+    constexpr float kLn2f = 0.6931471805599453f;
+    float key = -INFINITY;
+    if (mb > 0.f) {
+      key = __builtin_amdgcn_logf(mb) * kLn2f;
+      if (wt != 0.f) key = ib > 0.f ? key + wt * (__builtin_amdgcn_logf(ib / mb) * kLn2f) : -INFINITY;
+    }
+    return key;
+  };
+
+  // pooled estimates and keys by mass (descending, ids ascending among equal masses)
+  uint64_t x[E];
+  double tot_all = 0.0, tot_mand = 0.0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int b = tid * E + e;
+    x[e] = ~0ull;
+    if (b < n_vis) {
+      float si = 0.f, sm = 0.f;
+      for (int i = 0; i < s_t; ++i) {
+        si += I_of(b, i);
+        sm += m_of(b, i);
+      }
+      const float mb = sm * inv_s, ib = si * inv_s;
+      bar_I[b] = ib;
+      bar_m[b] = mb;
+      if (p.tile_scores) p.tile_scores[diag_row + b] = rerank_key(mb, ib);
+      if (p.tile_mass) p.tile_mass[diag_row + b] = mb;
+      tot_all += (double)mb;
+      if (mandatory(b)) tot_mand += (double)mb;
+      else x[e] = ((uint64_t)(0xffffffffu - __float_as_uint(mb)) << 32) | (uint64_t)(uint32_t)b;
+    }
+  }
+  for (int b = n_vis + tid; b < p.max_vis; b += kThrThreads) {
+    if (p.tile_scores) p.tile_scores[diag_row + b] = -1.f;
+    if (p.tile_mass) p.tile_mass[diag_row + b] = -1.f;
+  }
+  {
+    double a[1] = {tot_all}, d[1] = {tot_mand};
+    block_excl_scan_vec<1>(a, d, shd);
+    if (tid == kThrThreads - 1) {
+      sums[0] = a[0] + tot_all;
+      sums[1] = d[0] + tot_mand;
+    }
+    __syncthreads();
+    tot_all = sums[0];
+    tot_mand = sums[1];
+    __syncthreads();
+  }
+  sort_blocked<E>(x, sh);
+
+  // preselection: the shortest prefix of the mass order reaching rho of the candidates' mass
+  auto id_of = [](uint64_t key) { return (int)(uint32_t)(key & 0xffffffffull); };
+  double c[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) c[e] = x[e] == ~0ull ? 0.0 : (double)bar_m[id_of(x[e])];
+  const double cand_mass = blocked_inclusive_scan<E>(c, shd, &sums[0]);
+  const double need = (double)p.prac_rho * cand_mass;
+  int first_reach = INT_MAX;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (x[e] != ~0ull && c[e] >= need && first_reach == INT_MAX) first_reach = tid * E + e;
+  const int reach = block_min_int(first_reach, shi);
+  const int n_pre = need <= 0.0 ? 0 : (reach == INT_MAX ? INT_MAX : reach + 1);
+
+  // rerank the preselected blocks: key descending, ids ascending among equal keys
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    if (x[e] != ~0ull && tid * E + e < n_pre) {
+      const int b = id_of(x[e]);
+      x[e] = ((uint64_t)(~ordered_bits(rerank_key(bar_m[b], bar_I[b]))) << 32) | (uint64_t)(uint32_t)b;
+    } else {
+      x[e] = ~0ull;
+    }
+  }
+  sort_blocked<E>(x, sh);
+
+  // keep in that order while the pooled retained mass is below (1 - eps) of the total
+  const double target = (1.0 - (double)p.tau[w.h0]) * tot_all;
+  double incl[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) c[e] = incl[e] = x[e] == ~0ull ? 0.0 : (double)bar_m[id_of(x[e])];
+  blocked_inclusive_scan<E>(incl, shd, &sums[0]);
+  for (int b = tid; b < n_vis; b += kThrThreads) keep[b] = mandatory(b) ? 1 : 0;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const double before = tot_mand + (incl[e] - c[e]);  // retained mass ahead of this position
+    if (x[e] != ~0ull && before < target) keep[id_of(x[e])] = 1;
+  }
+  __syncthreads();
+
+  if (p.row_bound) {  // per-row omitted mass of the final discard set
+    float* rb = p.row_bound + ((int64_t)w.h0 * T + w.gtile) * S;
+    for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+      double a[kRowChunk], d[kRowChunk], mine[kRowChunk];
+#pragma unroll
+      for (int r = 0; r < kRowChunk; ++r) a[r] = d[r] = 0.0;
+      for (int b = tid; b < n_vis; b += kThrThreads)
+        if (!keep[b]) {
+#pragma unroll
+          for (int r = 0; r < kRowChunk; ++r)
+            if (i0 + r < s_t) a[r] += (double)m_of(b, i0 + r);
+        }
+#pragma unroll
+      for (int r = 0; r < kRowChunk; ++r) mine[r] = a[r];
+      block_excl_scan_vec<kRowChunk>(a, d, shd);
+      if (tid == kThrThreads - 1)
+        for (int r = 0; r < kRowChunk && i0 + r < s_t; ++r) rb[i0 + r] = (float)(a[r] + mine[r]);
+      __syncthreads();
+    }
+    for (int i = s_t + tid; i < S; i += kThrThreads) rb[i] = -1.f;
+  }
+
+  // retained set, compacted in ascending id order
+  const int E2 = (n_vis + kThrThreads - 1) / kThrThreads;
+  int cnt = 0;
+  for (int e = 0; e < E2; ++e) {
+    const int b = tid * E2 + e;
+    if (b < n_vis) cnt += keep[b];
+  }
+  int total;
+  int off = block_excl_scan_int(cnt, total, shi);
+  int32_t* out = p.slots + w.slot;
+  for (int e = 0; e < E2; ++e) {
+    const int b = tid * E2 + e;
+    if (b < n_vis && keep[b]) out[off++] = b;
+  }
+  if (tid == 0) p.counts[w.h0 * T + w.gtile] = total;
+}
+
 template <int MODE, bool STAGED>
 __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
-  constexpr bool POEM = MODE == kSelectOutputRelative;
+  constexpr bool NEED_I = MODE != kSelectMass;  // the mass-only ranking reads m alone
+  constexpr bool PRAC = MODE == kSelectPractical;
   constexpr int NK = STAGED ? kStageVis : kMaxVis;
   __shared__ uint64_t sh[NK];
   __shared__ uint8_t keep[NK];
-  __shared__ float st_I[STAGED && POEM ? kStageVals : 1];
+  __shared__ float st_I[STAGED && NEED_I ? kStageVals : 1];
+  __shared__ float bar_I[PRAC ? NK : 1], bar_m[PRAC ? NK : 1];  // practical: pooled estimates
   __shared__ float st_m[STAGED ? kStageVals : 1];
   __shared__ double shd[8 * kRowChunk];
   __shared__ int shi[8];
@@ -558,10 +743,10 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   w.Mb = w.Ib + cols;
 
   if constexpr (STAGED) {
-    // the head's s_t values of I (POEM only) and m per visible block, read with every
+    // the head's s_t values of I (not for the mass-only ranking) and m per visible block, read with every
     // load of a batch in flight before the first LDS store
     const int per_tensor = w.n_vis * w.s_t;
-    const int total = POEM ? 2 * per_tensor : per_tensor;
+    const int total = NEED_I ? 2 * per_tensor : per_tensor;
     constexpr int BATCH = 16;
     for (int base = 0; base < total; base += BATCH * kThrThreads) {
       float val[BATCH];
@@ -570,8 +755,8 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
         const int idx = base + u * kThrThreads + tid;
         val[u] = 0.f;
         if (idx < total) {
-          const bool is_m = !POEM || idx >= per_tensor;
-          const int r = is_m && POEM ? idx - per_tensor : idx;
+          const bool is_m = !NEED_I || idx >= per_tensor;
+          const int r = is_m && NEED_I ? idx - per_tensor : idx;
           const int b = r / w.s_t, i = r % w.s_t;
           val[u] = (is_m ? w.Mb : w.Ib)[(int64_t)b * w.bstride + i];
         }
@@ -580,8 +765,8 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
       for (int u = 0; u < BATCH; ++u) {
         const int idx = base + u * kThrThreads + tid;
         if (idx < total) {
-          const bool is_m = !POEM || idx >= per_tensor;
-          const int r = is_m && POEM ? idx - per_tensor : idx;
+          const bool is_m = !NEED_I || idx >= per_tensor;
+          const int r = is_m && NEED_I ? idx - per_tensor : idx;
           const int b = r / w.s_t, i = r % w.s_t;
           (is_m ? st_m : st_I)[b * w.S + i] = val[u];
         }
@@ -591,14 +776,19 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   }
   int n_pad = kThrThreads;
   while (n_pad < w.n_vis) n_pad <<= 1;
+  auto run = [&](auto e_tag) {
+    constexpr int E = decltype(e_tag)::value;
+    if constexpr (PRAC) practical_tile<STAGED, E>(p, w, st_I, st_m, bar_I, bar_m, sh, keep, shd, shi);
+    else threshold_tile<MODE, STAGED, E>(p, w, st_I, st_m, sh, keep, shd, shi);
+  };
   switch (n_pad / kThrThreads) {
-    case 1: threshold_tile<MODE, STAGED, 1>(p, w, st_I, st_m, sh, keep, shd, shi); break;
-    case 2: threshold_tile<MODE, STAGED, 2>(p, w, st_I, st_m, sh, keep, shd, shi); break;
-    case 4: threshold_tile<MODE, STAGED, 4>(p, w, st_I, st_m, sh, keep, shd, shi); break;
+    case 1: run(IntTag<1>{}); break;
+    case 2: run(IntTag<2>{}); break;
+    case 4: run(IntTag<4>{}); break;
     default:
       if constexpr (!STAGED) {
-        if (n_pad == 8 * kThrThreads) threshold_tile<MODE, STAGED, 8>(p, w, st_I, st_m, sh, keep, shd, shi);
-        else threshold_tile<MODE, STAGED, 16>(p, w, st_I, st_m, sh, keep, shd, shi);
+        if (n_pad == 8 * kThrThreads) run(IntTag<8>{});
+        else run(IntTag<16>{});
       }
       break;
   }
@@ -668,6 +858,11 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   if (mass) {
     if (staged) hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
     else hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+  } else if (p.mode == kSelectPractical) {
+    if (staged)
+      hipLaunchKernelGGL((sel_threshold_kernel<kSelectPractical, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+    else
+      hipLaunchKernelGGL((sel_threshold_kernel<kSelectPractical, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
   } else {
     if (staged)
       hipLaunchKernelGGL((sel_threshold_kernel<kSelectOutputRelative, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);

@@ -89,7 +89,8 @@ int64_t poem_csr_capacity(const poem_problem* problem);
 int64_t poem_max_visible_blocks(const poem_problem* problem);
 
 /* Bytes of device workspace the selectors need (256-byte aligned start): enough for
- * poem_select, poem_select_mass and poem_select_group at this rows_per_tile; < 0 on error. */
+ * poem_select, poem_select_mass, poem_select_practical and poem_select_group at this
+ * rows_per_tile; < 0 on error. */
 int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile);
 
 /*
@@ -134,6 +135,41 @@ poem_status poem_select(const poem_problem* problem, const void* q, const void* 
                         int32_t rows_per_tile, int32_t* row_ptr, int32_t* block_idx,
                         int64_t block_idx_capacity, float* tile_scores, float* tile_mass,
                         float* row_bound, void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * poem_select_practical: practical POEM, the deployed form of the output-relative
+ * selector (POEM note Equation (6) and its selection procedure, Appendix B).
+ *
+ * The same sampled rows and passes as poem_select give per visible block the pooled
+ * estimates mbar_b = mean_i m_ib and Ibar_b = mean_i I_ib (Ibar_b / mbar_b is the
+ * mass-weighted mean deviation ||v_ib - o_i||). Then:
+ *   preselection  the shortest prefix of the candidates in (mbar descending, id
+ *                 ascending) order whose mass reaches presel_fraction of the
+ *                 candidates' mass; the other candidates are discarded;
+ *   rerank        the preselected blocks by log mbar_b + weight * log(Ibar_b / mbar_b)
+ *                 (natural logs), descending, smaller id first among equal keys; a
+ *                 block with no mass, or (weight != 0) no deviation, ranks last;
+ *   threshold     blocks are kept in that order while the pooled retained mass (the
+ *                 mandatory blocks' included) is below (1 - eps_host[h]) of the pooled
+ *                 total over the visible blocks.
+ * The pages leave the estimates, the preselection rule, the weight and the threshold
+ * open; these are the parameters. The CSR is as for poem_select.
+ *
+ * Arguments as for poem_select, except:
+ *   eps_host        host [H_q]: pooled omitted-mass budget per head, finite, >= 0.
+ *   weight          finite: the deviation weight w.
+ *   presel_fraction (0, 1]: the preselected share of the candidates' mass.
+ *   tile_scores     nullable: the rerank key of every visible block (-1 beyond T_t).
+ *   row_bound       nullable: the per-row omitted mass of the final discard set.
+ * Errors as for poem_select; a non-finite weight or a fraction outside (0, 1] is
+ * POEM_ERR_INVALID_ARG.
+ */
+poem_status poem_select_practical(const poem_problem* problem, const void* q, const void* k, const void* v,
+                                  const float* eps_host, int32_t n_sink_blocks, int32_t n_local_blocks,
+                                  int32_t rows_per_tile, float weight, float presel_fraction, int32_t* row_ptr,
+                                  int32_t* block_idx, int64_t block_idx_capacity, float* tile_scores,
+                                  float* tile_mass, float* row_bound, void* workspace, size_t workspace_bytes,
+                                  void* stream);
 
 /*
  * poem_select_group: the output-relative selector with one list per (KV head, tile),

@@ -433,6 +433,94 @@ def test_group_selector_matches_oracle(case, sink, n_local, S):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
+def check_practical(w, eps_h, wt, rho, gp, op, r, which, q, k, v):
+    """poem_select_practical against the oracle: pooled masses (1e-3 gate), rerank keys
+    where defined, the retained set with exemptions at the preselection boundary (mass
+    order) and at the kept boundary (rerank order), and the per-row omitted masses of
+    the GPU's mask."""
+    T = L.num_tiles(gp)
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    keys = r["tile_scores"].cpu().numpy()
+    mass = r["tile_mass"].cpu().numpy()
+    bounds = r["row_bound"].cpu().numpy()
+    sels = O.select(op, q, k, v, eps_h, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which,
+                    mode="practical", practical=dict(w=wt, rho=rho))
+    n_cand = n_match = 0
+    for (h, gt), sel in sels.items():
+        t = sel.tile
+        n_vis = t.diag + 1
+        eps = float(eps_h[h])
+        floor = max(eps, 1e-3) / n_vis
+        mbar, Ibar = sel.mass, sel.I.mean(axis=0)
+        g_m = mass[h, gt, :n_vis].astype(np.float64)
+        assert np.all(np.abs(g_m - mbar) <= H.NEAR_REL * np.maximum(mbar, floor)), (h, gt)
+        assert np.all(mass[h, gt, n_vis:] == -1.0) and np.all(keys[h, gt, n_vis:] == -1.0)
+        cand = [b for b in range(n_vis) if b not in set(sel.mandatory)]
+        ok = [b for b in cand if mbar[b] > floor and Ibar[b] > floor]
+        g_k = keys[h, gt, :n_vis].astype(np.float64)
+        assert np.all(np.abs(g_k[ok] - sel.score[ok]) <= 4e-3 * (1 + abs(wt))), (h, gt)
+        pre, order, kept = O.practical_retain(mbar, Ibar, sel.mandatory, cand, eps, wt, rho)
+        by_mass = sorted(cand, key=lambda b: (-float(mbar[b]), int(b)))
+        cum_m = np.cumsum([mbar[b] for b in by_mass]) if by_mass else np.zeros(0)
+        need = rho * (cum_m[-1] if len(cum_m) else 0.0)
+        pos_m = {b: j for j, b in enumerate(by_mass)}
+        pos_r = {b: j for j, b in enumerate(order)}
+        before = {b: float(sum(mbar[x] for x in sel.mandatory) + sum(mbar[x] for x in order[:j]))
+                  for j, b in enumerate(order)}
+        target = (1 - eps) * float(mbar.sum())
+        nb_m = [by_mass[j] for j in (len(pre) - 1, len(pre)) if 0 <= j < len(by_mass)]
+        nb_r = [order[j] for j in (len(kept) - 1, len(kept)) if 0 <= j < len(order)]
+        got = H.retained(rp, bi, h * T + gt)
+        assert got == sorted(got) and set(sel.mandatory) <= set(got)
+        for b in cand:
+            n_cand += 1
+            if (b in got) == (b in sel.retained):
+                n_match += 1
+                continue
+            ex = any(abs(mbar[b] - mbar[x]) <= H.NEAR_REL * max(mbar[x], floor) for x in nb_m)
+            j = pos_m[b]
+            ex |= any(abs(cum_m[jj] - need) <= H.NEAR_REL * max(need, floor) for jj in (j - 1, j) if jj >= 0)
+            if b in pos_r:
+                ex |= any(abs(sel.score[b] - sel.score[x]) <= 4e-3 * (1 + abs(wt)) for x in nb_r)
+                ex |= abs(before[b] - target) <= H.NEAR_REL * max(eps, floor)
+            assert ex, (h, gt, b, b in got, b in sel.retained)
+        dropped = [b for b in range(n_vis) if b not in set(got)]
+        for j in range(len(sel.rows)):
+            delta = float(sel.m[j, dropped].sum())
+            assert abs(float(bounds[h, gt, j]) - delta) <= H.NEAR_REL * max(delta, floor), (h, gt, j)
+        if [b for b in order if b not in set(got)]:
+            assert float(sel.m[:, dropped].sum(axis=1).mean()) <= eps * (1 + H.NEAR_REL) + floor
+    return n_cand, n_match
+
+
+PRACTICAL = [
+    # case, sink_offset, n_local, eps, weight, presel_fraction
+    ((300, 428, 4, 1, 64, 64, "bf16", 1), 6.0, 1, 0.002, 0.5, 0.95),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 6.0, 1, 0.004, 1.0, 0.99),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), 5.0, 2, 0.02, 0.0, 1.0),
+    ((300, 428, 2, 1, 64, 64, "fp32", 1), 6.0, 1, 0.002, 2.0, 0.9),
+    ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1, 0.003, 0.5, 0.95),
+    ((64, 4160, 2, 1, 64, 64, "bf16", 1), 7.0, 1, 0.001, 0.5, 0.95),
+]
+
+
+@pytest.mark.parametrize("case,sink,n_local,eps,wt,rho", PRACTICAL, ids=lambda x: str(x))
+def test_practical_selector_matches_oracle(case, sink, n_local, eps, wt, rho):
+    w = _small(case, seed=11).with_(sink_offset=sink, n_local_blocks=n_local)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    eps_h = [eps * (1 + 0.5 * (h % 3)) for h in range(w.num_heads_q)]
+    say("practical selector", case, sink, n_local, eps, wt, rho)
+    r = L.select(gp, qd, kd, vd, eps_h, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="practical", weight=wt, presel_fraction=rho)
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    nc, nm = check_practical(w, eps_h, wt, rho, gp, op, r, which, q, k, v)
+    say("  candidates", nc, "agreement", nm / max(nc, 1))
+
+
 # ---------------------------------------------------------------------------
 # the workloads at full size
 # ---------------------------------------------------------------------------
@@ -561,3 +649,23 @@ def test_group_full_size_sampled():
         h = g * op.group + 1
         Os, _ = O.tile_attention(op, q, k, v, h, t, H.retained(rp, bi, h * T + gt))
         assert np.abs(so[t.q_row0:t.q_row0 + t.n_rows, h] - Os).max() <= H.OUT_ATOL_BF16
+
+
+def test_practical_full_size_sampled():
+    """poem_select_practical at the 128K layer's full size; oracle on stratified tiles."""
+    w = synth.WORKLOADS[3]
+    say("workload 3 practical: generate")
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    eps_h = [0.002] * w.num_heads_q
+    say("workload 3 practical: select")
+    r = L.select(gp, qd, kd, vd, eps_h, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                 mode="practical", weight=0.5, presel_fraction=0.95)
+    _sync()
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    say("  keep fraction", len(bi[:rp[-1]]) / L.csr_capacity(gp))
+    q, k, v = H.f64(inp)
+    which = H.stratified_tiles(op, [0, w.num_heads_q - 1], per_head=3, seed=55)
+    nc, nm = check_practical(w, eps_h, 0.5, 0.95, gp, op, r, which, q, k, v)
+    say("  sampled candidates", nc, "agreement", nm / max(nc, 1))

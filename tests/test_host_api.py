@@ -95,7 +95,13 @@ def _select(lib, p, **over):
                 row_ptr=FAKE, block_idx=FAKE, cap=L.csr_capacity(p), ts=None, tm=None, rb=None,
                 ws=ctypes.c_void_p(0x200000), ws_bytes=L.select_workspace_bytes(p, 8))
     args.update(over)
-    fn = getattr(lib, args.pop("fn", "poem_select"))
+    fn = args.pop("fn", "poem_select")
+    if fn == "poem_select_practical":
+        return lib.poem_select_practical(ctypes.byref(cp), args["q"], args["k"], args["v"], args["tau"], args["sink"],
+                                         args["local"], args["S"], args.get("weight", 0.5), args.get("presel", 0.95),
+                                         args["row_ptr"], args["block_idx"], args["cap"], args["ts"], args["tm"],
+                                         args["rb"], args["ws"], args["ws_bytes"], None)
+    fn = getattr(lib, fn)
     return fn(ctypes.byref(cp), args["q"], args["k"], args["v"], args["tau"], args["sink"],
                            args["local"], args["S"], args["row_ptr"], args["block_idx"], args["cap"], args["ts"],
                            args["tm"], args["rb"], args["ws"], args["ws_bytes"], None)
@@ -120,10 +126,13 @@ def test_select_validation(lib):
         (dict(ws_bytes=4096), L.POEM_ERR_WORKSPACE),
         (dict(ws=ctypes.c_void_p(0x200010)), L.POEM_ERR_WORKSPACE),
     ]
-    for fn in ("poem_select", "poem_select_mass", "poem_select_group"):
+    for fn in ("poem_select", "poem_select_mass", "poem_select_group", "poem_select_practical"):
         for over, status in cases:
             assert _select(lib, p, fn=fn, **over) == status, (fn, over)
             assert lib.poem_last_error().decode() != ""
+    for over in (dict(weight=float("nan")), dict(weight=float("inf")), dict(presel=0.0), dict(presel=1.5),
+                 dict(presel=float("nan"))):
+        assert _select(lib, p, fn="poem_select_practical", **over) == L.POEM_ERR_INVALID_ARG, over
     # per-head lists use the largest layout, which the reported size covers exactly
     assert _select(lib, p, ws_bytes=L.select_workspace_bytes(p, 8) - 1) == L.POEM_ERR_WORKSPACE
 
