@@ -179,13 +179,14 @@ def _err_stats(e, si, tau):
             "sampled_rows_within_tau": float((e[si] <= tau[None, :]).float().mean())}
 
 
-def _time_select_sparse(gp, L, w, q, k, v, ws, sws, taus, mode, steps):
+def _time_select_sparse(gp, L, w, q, k, v, ws, sws, taus, mode, steps, **kw):
     import torch
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(steps)]
     r = None
     for i in range(steps):
         ev[i][0].record()
-        r = L.select(gp, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws, mode=mode)
+        r = L.select(gp, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws, mode=mode,
+                     **kw)
         ev[i][1].record()
         L.sparse_prefill(gp, q, k, v, r["row_ptr"], r["block_idx"], out_dtype="bf16", want_lse=False,
                          workspace=sws)
@@ -198,9 +199,9 @@ def _time_select_sparse(gp, L, w, q, k, v, ws, sws, taus, mode, steps):
 
 def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
     """The other selectors beside POEM's per-head one, on the same inputs:
-    - mass-only: latency at a fixed budget, then POEM and mass-only at matched per-head
-      keep fraction (each head's mass budget bisected until its kept-block count
-      matches POEM's), with the output errors of both against dense attention;
+    - mass-only and practical POEM: latency at a fixed budget, then each at POEM's
+      per-head keep counts (each head's budget bisected until its kept-block count
+      matches POEM's), with the output errors against dense attention;
     - group-shared lists: latency at the same thresholds, keep fraction and errors.
     Errors are ||O_sparse - O_dense|| per query row with fp32 outputs."""
     import torch
@@ -226,18 +227,17 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
     out = {"err_poem": _err_stats(e_p, si, tau)}
     del e_p
 
-    res_m = {}
-    if not args.no_mass:
-        r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "mass", steps)
-        res_m = {"eps": args.mass_eps, "select_ms": t_sel, "sparse_ms": t_sp,
-                 "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
-        vis = np.diff(rp_poem).reshape(H, T).sum(1)  # POEM's kept blocks per head
+    vis = np.diff(rp_poem).reshape(H, T).sum(1)  # POEM's kept blocks per head
+
+    def matched(mode, **kw):
+        """Per-head budgets bisected (in log10) until each head keeps as many blocks as
+        POEM; returns the budgets and the selection at them."""
         lo, hi = np.full(H, -9.0), np.zeros(H)
         best = [None] * H
         for _ in range(24):
             mid = 0.5 * (lo + hi)
             rr = L.select(gp, q, k, v, list(10.0 ** mid), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
-                          workspace=ws, mode="mass")
+                          workspace=ws, mode=mode, **kw)
             kept = np.diff(rr["row_ptr"].cpu().numpy().astype(np.int64)).reshape(H, T).sum(1)
             for h in range(H):
                 gap = abs(int(kept[h]) - int(vis[h]))
@@ -246,9 +246,16 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
             more = kept > vis  # keeps too much: raise the budget
             lo = np.where(more, mid, lo)
             hi = np.where(more, hi, mid)
-        eps_m = [b[1] for b in best]
-        rm = L.select(gp, q, k, v, eps_m, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
-                      mode="mass")
+        eps = [b[1] for b in best]
+        return eps, L.select(gp, q, k, v, eps, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws,
+                             mode=mode, **kw)
+
+    res_m = {}
+    if not args.no_mass:
+        r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "mass", steps)
+        res_m = {"eps": args.mass_eps, "select_ms": t_sel, "sparse_ms": t_sp,
+                 "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
+        eps_m, rm = matched("mass")
         e_m = errors(rm)
         res_m["matched_keep"] = {
             "keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
@@ -256,6 +263,18 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
             "eps_per_head": [float("%.4g" % e) for e in eps_m],
             "err_poem": out["err_poem"], "err_mass": _err_stats(e_m, si, tau)}
         del e_m
+
+    # practical POEM: latency at a fixed budget, then errors at POEM's per-head keep counts
+    pk = dict(weight=args.practical_weight, presel_fraction=args.practical_presel)
+    r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "practical", steps, **pk)
+    res_p = {"eps": args.mass_eps, "weight": pk["weight"], "presel_fraction": pk["presel_fraction"],
+             "select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
+    eps_p, rpr = matched("practical", **pk)
+    e_pr = errors(rpr)
+    res_p["matched_keep"] = {"keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
+                             "keep_fraction_blocks_practical": float(rpr["row_ptr"][-1].item()) / cap,
+                             "err_poem": out["err_poem"], "err_practical": _err_stats(e_pr, si, tau)}
+    del e_pr
 
     r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, inp.tau, "group", steps)
     e_g = errors(r)
@@ -265,7 +284,7 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
                      "group's 8 sampled rows; sampled_rows_within_tau is taken on the per-head selector's rows"}
     del od, e_g
     torch.cuda.empty_cache()
-    return res_m, res_g
+    return res_m, res_g, res_p
 
 
 def main():
@@ -280,7 +299,10 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-legs", action="store_true", help="skip the mass-only and group-shared selector legs")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-only selector leg")
-    ap.add_argument("--mass-eps", type=float, default=0.002, help="omitted-mass budget of the mass-only leg")
+    ap.add_argument("--mass-eps", type=float, default=0.002,
+                    help="omitted-mass budget of the mass-only and practical legs")
+    ap.add_argument("--practical-weight", type=float, default=0.5, help="deviation weight of the practical leg")
+    ap.add_argument("--practical-presel", type=float, default=0.95, help="preselected mass share (practical leg)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="only run one device-to-device copy of this many MiB (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -431,10 +453,11 @@ def main():
     }
     if not args.no_legs and inp.is_bf16:
         log("[bench] mass-only and group-shared selector legs")
-        res_m, res_g = selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
+        res_m, res_g, res_p = selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
         if res_m:
             res["mass_only"] = res_m
         res["group_shared"] = res_g
+        res["practical"] = res_p
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
         res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds)
