@@ -31,6 +31,7 @@
 namespace poem {
 
 constexpr int kSelThreads = 256;
+template <bool B> struct BoolTag { static constexpr bool value = B; };
 constexpr int kSelWaves = 4;
 
 // MASS: the mass-only selector needs neither o nor U_b, so both passes skip P V and
@@ -41,8 +42,10 @@ void sel_sweep_kernel(SelectParams p) {
   using St = Stage<T, D, kSelThreads>;
   constexpr int SUBS = BLK / kStageKeys;
   constexpr bool SPLIT = sizeof(T) == 2;
-  __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
-  __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
+  // bf16 pass 1 of the output-relative selectors runs the pipelined sweep below; pass 2
+  // (which also holds o for its per-block norms), the mass-only passes and fp32 run
+  // the plain double-buffered sweep
+  constexpr bool PIPE = St::ASYNC && !MASS && !PASS2;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
@@ -116,7 +119,8 @@ void sel_sweep_kernel(SelectParams p) {
       inv_l = 1.f / rs_col[1];
     }
   }
-  if constexpr (PASS2 && !MASS) {
+  // the column's dense output o in the accumulator layout (pass 2)
+  auto load_o = [&](f32x16 (&o)[D / 32]) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
@@ -124,9 +128,10 @@ void sel_sweep_kernel(SelectParams p) {
         f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
         if (col_on) v4 = *reinterpret_cast<const f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) Od[dt][4 * a + e] = v4[e];
+        for (int e = 0; e < 4; ++e) o[dt][4 * a + e] = v4[e];
       }
-  }
+  };
+  if constexpr (PASS2 && !MASS && !PIPE) load_o(Od);
   // per (KV head, tile, visible block): I of the record's columns, then m of them, so
   // a wave's per-block results are one coalesced store each per tile
   float* blk_I = nullptr;
@@ -139,6 +144,270 @@ void sel_sweep_kernel(SelectParams p) {
   wait_vmem_all();
   const int total = nblk_wg * SUBS;
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
+  // pass 2: I and m of one block from its weight sum and U (O), for the pair's column
+  auto finalize_block = [&](int blk, const f32x16 (&o)[D / 32]) {
+    const float mt = mloc + wave_xor32(mloc);
+    float ss = 0.f;
+    if constexpr (!MASS) {
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float dv = __builtin_fmaf(-mt, o[dt][r], O[dt][r]);
+          ss = __builtin_fmaf(dv, dv, ss);
+        }
+      ss += wave_xor32(ss);
+    }
+    if (col_on && g2 == 0) {
+      float* dst = blk_I + (int64_t)blk * bstride;
+      if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * inv_l;
+      dst[p.cols_rec] = mt * inv_l;
+    }
+  };
+  if constexpr (PIPE) {
+    // Software pipeline over stages, as in the attention kernel: K and V in separate
+    // double buffers, V one stage behind K. Step j: the QK^T MFMAs of stage j next to
+    // the exponentials (and sums) of stage j-1; then the split P V MFMAs of stage j-1
+    // next to the hi/lo packs of its following key step and, in pass 1, stage j's
+    // running max. Every wave computes every stage of the workgroup: a stage whose keys
+    // all lie above the wave's rows is fully masked, so its weights are exactly zero
+    // (such stages are the last few of the wave). In pass 2 o is read back only when a
+    // block is finalised.
+    __shared__ __attribute__((aligned(16))) char kb0[St::TENSOR];
+    __shared__ __attribute__((aligned(16))) char kb1[St::TENSOR];
+    __shared__ __attribute__((aligned(16))) char vb0[St::TENSOR];
+    __shared__ __attribute__((aligned(16))) char vb1[St::TENSOR];
+    constexpr int NQK = 2 * (D / 16);  // QK^T MFMAs per stage
+    constexpr int NDT = D / 32;        // d tiles of O
+    constexpr int NPV = 4 * NDT;       // (V fragment, key step) pairs per stage, two MFMAs each
+    constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
+    constexpr int XPM = 32 / NPV;      // max candidates per V fragment (pass 1)
+    const typename St::LaneOffsets lofs = St::lane_offsets(row_stride, tid);
+    float m_use = 0.f;  // pass 1: exponent reference of the stage being exponentiated
+    auto kfrag = [&](const char* kbuf, int i) {  // K operand of QK MFMA i
+      const int kt = i & 1, st = i >> 1;
+      const int r = 32 * kt + (lane & 31);
+      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + r * St::ROW +
+                                                                          ((2 * st + g2) ^ St::kswz(r)) * 16));
+    };
+    auto mask = [&](f32x16 (&S)[2], int key0) {
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (key0 + acc_key(kt, r, g2) > my_pos) S[kt][r] = -INFINITY;
+    };
+    auto finish_max = [&](float mx) {  // pass 1: running max of a stage, rare rescale
+      mx = fmaxf(mx, wave_xor32(mx));
+      const float m_new = fmaxf(m_run, mx * c);
+      const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_next);
+      m_run = m_new;
+      m_use = m_next;
+      if (__any(alpha != 1.f)) {
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) O[dt] *= alpha;
+        l_run *= alpha;
+      }
+    };
+    f32x16 Sp[2] = {f32x16{}, f32x16{}};
+    {
+      St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0, lofs);
+      wait_vmem_all();
+      __syncthreads();
+      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lofs);
+      St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0, lofs);
+      if (total > 0) {
+        Sp[0] = St::qk_tile(kb0, qf, 0, lane);
+        Sp[1] = St::qk_tile(kb0, qf, 1, lane);
+        if (kStageKeys - 1 > wave_pos_min) mask(Sp, 0);
+        if constexpr (!PASS2) {
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sp[e >> 4][e & 15]);
+          finish_max(mx);
+        }
+      }
+      wait_vmem_all();
+      __syncthreads();
+    }
+    // step it (1 <= it <= total): QK of stage it (it < total), softmax and P V of it - 1
+    auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
+      const bool more = it < total;
+      const int key0 = more ? stage_key0(it) : 0;
+      if (more) {
+        St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext, lofs);
+        St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lofs);
+      }
+      const int pit = it - 1;
+      if constexpr (PASS2) {
+        if (pit % SUBS == 0) {  // the block of stage it - 1 starts: fresh U and weight sum
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x16{};
+          mloc = 0.f;
+        }
+      }
+      f32x16 Sn[2] = {f32x16{}, f32x16{}};
+      float mx = -INFINITY;
+      // QK phase
+      bf16x8 ka[3];
+      if (more) {
+        ka[0] = kfrag(kcur, 0);
+        ka[1] = kfrag(kcur, 1);
+      }
+      const float ref = PASS2 ? m2 : m_use;
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < NQK; ++i) {
+        if (more) {
+          Sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf.q[i >> 1], Sn[i & 1], 0, 0, 0);
+          if (i + 2 < NQK) ka[(i + 2) % 3] = kfrag(kcur, i + 2);
+        }
+#pragma unroll
+        for (int u = 0; u < EPM; ++u) {
+          const int e = i * EPM + u;
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -ref));
+          Sp[e >> 4][e & 15] = x;
+          rs += x;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (PASS2) mloc += rs;
+      else l_run += rs;
+      // PV phase: O += V^T (P_hi + P_lo) with the packs one key step ahead
+      __builtin_amdgcn_s_setprio(1);
+      bf16x8 ph[2], pl[2];
+      p_step<true>(Sp, 0, ph[0], pl[0]);
+      bf16x8 va[2];
+      va[0] = St::v_frag(vprev, 0, 0, lane);
+#pragma unroll
+      for (int i = 0; i < NPV; ++i) {
+        const int dt = i % NDT, st = i / NDT;
+        if (i + 1 < NPV) va[(i + 1) & 1] = St::v_frag(vprev, (i + 1) % NDT, (i + 1) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st & 1], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st & 1], O[dt], 0, 0, 0);
+        if (dt == 0 && st + 1 < 4) p_step<true>(Sp, st + 1, ph[(st + 1) & 1], pl[(st + 1) & 1]);
+        if constexpr (!PASS2) {
+#pragma unroll
+          for (int u = 0; u < XPM; ++u) {
+            const int e = i * XPM + u;
+            mx = fmaxf(mx, Sn[e >> 4][e & 15]);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      __builtin_amdgcn_s_setprio(0);
+      if (more) {
+        if (key0 + kStageKeys - 1 > wave_pos_min) {
+          mask(Sn, key0);
+          if constexpr (!PASS2) {
+            mx = -INFINITY;
+#pragma unroll
+            for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
+          }
+        }
+        if constexpr (!PASS2) finish_max(mx);
+      }
+      if constexpr (PASS2) {
+        // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
+        const int blk = pit / SUBS;
+        if (pit % SUBS == SUBS - 1 && in_range && blk <= diag) {
+          f32x16 o[NDT];
+          load_o(o);
+          finalize_block(blk, o);
+        }
+      }
+      Sp[0] = Sn[0];
+      Sp[1] = Sn[1];
+      wait_vmem_all();
+      __syncthreads();
+    };
+    for (int it = 1; it <= total; it += 2) {
+      step(it, kb1, kb0, vb0, vb1);
+      if (it + 1 <= total) step(it + 1, kb0, kb1, vb1, vb0);
+    }
+  } else {
+  __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
+  __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
+  // pass 2 stage for bf16 (see its call below); MASKED: the stage reaches past a row
+  auto pass2_stage = [&](auto masked_tag, const char* cur, int key0) {
+    constexpr bool MASKED = decltype(masked_tag)::value;
+    if constexpr (St::ASYNC && PASS2 && !MASS) {
+      constexpr int ST = D / 16;   // d steps of one QK^T tile
+      constexpr int NDT = D / 32;  // d tiles of O
+      auto kfrag = [&](int kt, int st) {
+        const int r = 32 * kt + (lane & 31);
+        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + r * St::ROW +
+                                                                            ((2 * st + g2) ^ St::kswz(r)) * 16));
+      };
+      auto weight = [&](float s, int kt, int r) {
+        if (MASKED && key0 + acc_key(kt, r, g2) > my_pos) return 0.f;
+        return __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -m2));
+      };
+      const char* vt = cur + St::TENSOR;
+      f32x16 S0 = {}, S1 = {};
+      bf16x8 ka[3];
+      ka[0] = kfrag(0, 0);
+      ka[1] = kfrag(0, 1);
+#pragma unroll
+      for (int i = 0; i < ST; ++i) {  // key tile 0
+        S0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf.q[i], S0, 0, 0, 0);
+        ka[(i + 2) % 3] = kfrag((i + 2) / ST, (i + 2) % ST);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      f32x16 Sp[2];
+      bf16x8 ph[4], pl[4];
+      float rs = 0.f;
+#pragma unroll
+      for (int i = 0; i < ST; ++i) {  // key tile 1, next to the weights of key tile 0
+        S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[(ST + i) % 3], qf.q[i], S1, 0, 0, 0);
+        if (i + 2 < ST) ka[(ST + i + 2) % 3] = kfrag(1, i + 2);
+#pragma unroll
+        for (int u = 0; u < 16 / ST; ++u) {
+          const int r = i * (16 / ST) + u;
+          S0[r] = weight(S0[r], 0, r);
+          rs += S0[r];
+        }
+        if (i == ST - 1) {
+          Sp[0] = S0;
+          p_step<true>(Sp, 0, ph[0], pl[0]);
+          p_step<true>(Sp, 1, ph[1], pl[1]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // P V over key steps 0 and 1, next to the weights and packs of key tile 1
+      bf16x8 va[2];
+      va[0] = St::v_frag(vt, 0, 0, lane);
+#pragma unroll
+      for (int i = 0; i < 2 * NDT; ++i) {
+        const int dt = i % NDT, st = i / NDT;
+        va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st], O[dt], 0, 0, 0);
+#pragma unroll
+        for (int u = 0; u < 16 / (2 * NDT); ++u) {
+          const int r = i * (16 / (2 * NDT)) + u;
+          S1[r] = weight(S1[r], 1, r);
+          rs += S1[r];
+        }
+        if (i == 2 * NDT - 1) {
+          Sp[1] = S1;
+          p_step<true>(Sp, 2, ph[2], pl[2]);
+          p_step<true>(Sp, 3, ph[3], pl[3]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      mloc += rs;
+#pragma unroll
+      for (int i = 2 * NDT; i < 4 * NDT; ++i) {  // key steps 2 and 3
+        const int dt = i % NDT, st = i / NDT;
+        if (i + 1 < 4 * NDT) va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st], O[dt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
+  };
   sweep<St, MASS>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
     const int blk = it / SUBS, sub = it % SUBS;
     const int key0 = stage_key0(it);
@@ -147,7 +416,15 @@ void sel_sweep_kernel(SelectParams p) {
       for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
       mloc = 0.f;
     }
-    if (key0 <= wave_pos_max) {
+    if constexpr (St::ASYNC && PASS2 && !MASS) {
+      // pass 2, bf16: one stage with its work overlapped inside the wave. The QK^T MFMAs
+      // of key tile 1 run next to the weights of key tile 0; the first half of the split
+      // P V next to the weights and packs of key tile 1; fragments are read ahead.
+      if (key0 <= wave_pos_max) {
+        if (key0 + kStageKeys - 1 > wave_pos_min) pass2_stage(BoolTag<true>{}, cur, key0);
+        else pass2_stage(BoolTag<false>{}, cur, key0);
+      }
+    } else if (key0 <= wave_pos_max) {
       f32x16 S[2];
       S[0] = St::qk_tile(cur, qf, 0, lane);
       S[1] = St::qk_tile(cur, qf, 1, lane);
@@ -197,27 +474,10 @@ void sel_sweep_kernel(SelectParams p) {
     }
     if constexpr (PASS2) {
       // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
-      if (sub == SUBS - 1 && in_range && blk <= diag) {
-        const float mt = mloc + wave_xor32(mloc);
-        float ss = 0.f;
-        if constexpr (!MASS) {
-#pragma unroll
-          for (int dt = 0; dt < D / 32; ++dt)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) {
-              const float dv = __builtin_fmaf(-mt, Od[dt][r], O[dt][r]);
-              ss = __builtin_fmaf(dv, dv, ss);
-            }
-          ss += wave_xor32(ss);
-        }
-        if (col_on && g2 == 0) {
-          float* dst = blk_I + (int64_t)blk * bstride;
-          if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * inv_l;
-          dst[p.cols_rec] = mt * inv_l;
-        }
-      }
+      if (sub == SUBS - 1 && in_range && blk <= diag) finalize_block(blk, Od);
     }
   });
+  }
 
   if constexpr (!PASS2) {
     const float l_tot = l_run + wave_xor32(l_run);
