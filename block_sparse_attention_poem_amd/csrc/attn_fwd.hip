@@ -31,18 +31,22 @@ struct AttnCfg {
   // fp32: two stage buffers (K and transposed V together)
   static constexpr int KBUF = St::ASYNC ? St::BYTES / 2 : St::BYTES;
   static constexpr int VBUF = St::ASYNC ? St::BYTES / 2 : 16;
+  static constexpr int KBUF3 = St::ASYNC ? St::BYTES / 2 : 16;  // bf16 sparse: a third K buffer
+  // direct loads one wave issues for one tensor of a stage (bf16)
+  static constexpr int LOADS = St::ASYNC ? (St::BYTES / 2 / 1024) / WAVES : 0;
 };
 
-#define POEM_ATTN_LDS(T, D, BLK)                                                        \
+#define POEM_ATTN_LDS(T, D, BLK, K3)                                                    \
   __shared__ __attribute__((aligned(16))) char kb0[AttnCfg<T, D, BLK>::KBUF];           \
   __shared__ __attribute__((aligned(16))) char kb1[AttnCfg<T, D, BLK>::KBUF];           \
+  __shared__ __attribute__((aligned(16))) char kb2[(K3) ? AttnCfg<T, D, BLK>::KBUF3 : 16]; \
   __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];           \
   __shared__ __attribute__((aligned(16))) char vb1[AttnCfg<T, D, BLK>::VBUF];
 
 // One (query head h, tile t of sequence seq): the whole workgroup, B rows.
 template <typename T, int D, int BLK, bool SPARSE>
 __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* kb0, char* kb1,
-                                          char* vb0, char* vb1) {
+                                          char* kb2, char* vb0, char* vb1) {
   using C = AttnCfg<T, D, BLK>;
   using St = typename C::St;
   constexpr int SUBS = C::SUBS;
@@ -69,12 +73,17 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   const T* vbase = reinterpret_cast<const T*>(p.v) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
 
   // block list
-  const int32_t* ids = nullptr;
+  // The CSR is read-only for the whole launch, so its reads go through the scalar cache
+  // (constant address space): a vector load here would make each stage's first wait
+  // drain the K/V prefetch along with it.
+  using cint = const __attribute__((address_space(4))) int32_t;
+  cint* ids = nullptr;
   int nblk;
   if constexpr (SPARSE) {
     const int64_t r = (int64_t)h * p.seqs.total_tiles + p.seqs.tile_start[seq] + t;
-    const int a = p.row_ptr[r], b = p.row_ptr[r + 1];
-    ids = p.block_idx + a;
+    cint* rp = (cint*)p.row_ptr;
+    const int a = rp[r], b = rp[r + 1];
+    ids = (cint*)p.block_idx + a;
     int n = b - a;
     // rows are ascending: keep the ids in [0, diag]
     int lo = 0, hi = n;  // first index with id >= 0
@@ -144,9 +153,12 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   };
 
   if constexpr (St::ASYNC) {
-    // Software pipeline over stages. K and V have their own double buffers and V lags K
-    // by one stage: step j reads K(j) and V(j-1) while K(j+1) and V(j) load. The step is
-    // laid out by hand in short chunks fenced off from the scheduler:
+    // Software pipeline over stages. V has two buffers and lags K by one stage: step j
+    // reads K(j) and V(j-1) while V(j) and K(j+KA) load. Sparse rows, whose K/V fetches
+    // mostly miss L2, use KA = 2 and three K buffers, so K, needed first in a step, has
+    // two steps of lead; dense rows (mostly L2 hits) run faster with KA = 1 and the
+    // shorter loop. The step is laid out by hand in short chunks fenced off from the
+    // scheduler:
     //   QK phase : each QK^T MFMA of stage j with the next-but-one K fragment read and
     //              the exponentials (and bf16 packs) of stage j-1;
     //   mask     : only on stages that reach past a row;
@@ -180,12 +192,24 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         l_run *= alpha;
       }
     };
+    const typename St::LaneOffsets lo = St::lane_offsets(row_stride, tid);
+    constexpr int KA = SPARSE ? 2 : 1;
+    // KA = 2: s_waitcnt vmcnt(LOADS), every direct load but this wave's newest K stage
+    // has landed; KA = 1: vmcnt(0)
+    constexpr int kWait = KA == 2 ? (C::LOADS | 0x0F70) : 0x0F70;
+    static_assert(C::LOADS < 16, "vmcnt field");
     auto first = [&]() {
-      St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0);
-      wait_vmem_all();
-      __syncthreads();
-      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1);
-      St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0);
+      // the waits count this wave's loads in issue order, which the fences keep
+      St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0, lo);
+      if constexpr (KA == 2) {
+        __builtin_amdgcn_sched_barrier(0);
+        St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lo);
+      }
+      __builtin_amdgcn_s_waitcnt(kWait);
+      lds_barrier();
+      St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0, lo);
+      __builtin_amdgcn_sched_barrier(0);
+      St::load_k(kbase, row_stride, stage_key0(min(KA, total - 1)), n_k, tid, KA == 2 ? kb2 : kb1, lo);
       Sp[0] = St::qk_tile(kb0, qf, 0, lane);
       Sp[1] = St::qk_tile(kb0, qf, 1, lane);
       mask(Sp, stage_key0(0));
@@ -193,14 +217,16 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 #pragma unroll
       for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sp[e >> 4][e & 15]);
       finish_max(mx);
-      wait_vmem_all();
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(kWait);
+      lds_barrier();
     };
-    const typename St::LaneOffsets lo = St::lane_offsets(row_stride, tid);
     auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
       const int key0 = stage_key0(it);
-      St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext, lo);
+      // V(it) first, then K(it + KA): with KA = 2 the wait below leaves only the K loads
+      // in flight
       St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lo);
+      __builtin_amdgcn_sched_barrier(0);
+      St::load_k(kbase, row_stride, stage_key0(min(it + KA, total - 1)), n_k, tid, knext, lo);
       // QK phase
       f32x16 Sn[2] = {f32x16{}, f32x16{}};
       bf16x8 P[4];
@@ -259,14 +285,27 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       finish_max(mx);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
-      wait_vmem_all();
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(kWait);
+      lds_barrier();
     };
     if (total > 0) {
       first();
-      for (int it = 1; it < total; it += 2) {
-        step(it, kb1, kb0, vb0, vb1);
-        if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
+      if constexpr (KA == 2) {
+        // stage it: K in kb[it % 3], V in vb[it % 2]; six steps per trip keep every
+        // buffer a distinct LDS object in each step
+        for (int it = 1; it < total; it += 6) {
+          step(it, kb1, kb0, vb0, vb1);
+          if (it + 1 < total) step(it + 1, kb2, kb1, vb1, vb0);
+          if (it + 2 < total) step(it + 2, kb0, kb2, vb0, vb1);
+          if (it + 3 < total) step(it + 3, kb1, kb0, vb1, vb0);
+          if (it + 4 < total) step(it + 4, kb2, kb1, vb0, vb1);
+          if (it + 5 < total) step(it + 5, kb0, kb2, vb1, vb0);
+        }
+      } else {
+        for (int it = 1; it < total; it += 2) {
+          step(it, kb1, kb0, vb0, vb1);
+          if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
+        }
       }
       bf16x8 P[4], unused;
       float rs = 0.f;
@@ -279,6 +318,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       }
       l_run += rs;
       St::pv_packed(((total - 1) & 1) ? vb1 : vb0, P, O, lane);
+      // the last K prefetch (a repeat of the final stage) may still be in flight: it
+      // lands before this workgroup's LDS can be reused
+      wait_vmem_all();
     }
   } else {
     sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, kb0, kb1, [&](int it, const char* cur) {
@@ -321,7 +363,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 template <typename T, int D, int BLK, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_fwd_kernel(AttnParams p) {
-  POEM_ATTN_LDS(T, D, BLK)
+  POEM_ATTN_LDS(T, D, BLK, SPARSE)
   const int bid = blockIdx.x;
   const int gk = bid % p.hkv;
   const int rest = bid / p.hkv;
@@ -330,7 +372,7 @@ void attn_fwd_kernel(AttnParams p) {
   int seq, t;
   rank_to_item(p.seqs, 1, rank, seq, t);
   if (seq < 0) return;
-  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, kb0, kb1, vb0, vb1);
+  attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, kb0, kb1, kb2, vb0, vb1);
 }
 
 // Persistent schedule for sparse rows, whose lengths vary from a few blocks to
@@ -340,19 +382,26 @@ void attn_fwd_kernel(AttnParams p) {
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_sparse_persistent_kernel(AttnParams p) {
-  POEM_ATTN_LDS(T, D, BLK)
-  __shared__ int item_sh;
+  POEM_ATTN_LDS(T, D, BLK, true)
+  // the queue slot borrows kb2, which no wave reads between rows (bf16: this keeps the
+  // workgroup's LDS at 80 KB, two workgroups per CU)
+  int* item_sh = reinterpret_cast<int*>(kb2);
   const int n_tiles = p.seqs.total_tiles;
   for (;;) {
-    if (threadIdx.x == 0) item_sh = atomicAdd(p.queue, 1);
+    // every wave's direct loads of the previous row have landed (attn_tile ends with
+    // them drained); the barrier orders them before the slot is written
     __syncthreads();
-    const int item = item_sh;
+    if (threadIdx.x == 0) *item_sh = atomicAdd(p.queue, 1);
+    __syncthreads();
+    // uniform by construction; readfirstlane lets the row's CSR and block ids load
+    // through the scalar cache (vector loads here would each drain the K/V prefetch)
+    const int item = __builtin_amdgcn_readfirstlane(*item_sh);
     __syncthreads();
     if (item >= p.num_rows) break;
     const int r = p.order[item];
     const int h = r / n_tiles, gtile = r % n_tiles;
     const int seq = find_seq(p.seqs, gtile);
-    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], kb0, kb1, vb0, vb1);
+    attn_tile<T, D, BLK, true>(p, h, seq, gtile - p.seqs.tile_start[seq], kb0, kb1, kb2, vb0, vb1);
   }
 }
 

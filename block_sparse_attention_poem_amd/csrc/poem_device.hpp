@@ -521,6 +521,14 @@ __device__ __forceinline__ void sched_stage() {
   }
 }
 
+// Workgroup barrier that does not drain global loads (__syncthreads waits for every
+// outstanding load, including direct loads into LDS still meant to be in flight).
+// Each wave has already waited, with an explicit s_waitcnt vmcnt, for the direct loads
+// the other waves will read after the barrier. Waiting for its own LDS reads first
+// keeps a buffer from being refilled under a pending read, and the memory clobber
+// keeps the compiler from moving LDS accesses across the barrier.
+__device__ __forceinline__ void lds_barrier() { __asm__ volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima). Issued once after the
 // per-column loads that precede a sweep: otherwise those loads stay "pending" at the
 // loop header on some path and every iteration waits for its own K/V prefetch too.
