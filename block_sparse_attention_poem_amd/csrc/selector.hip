@@ -17,8 +17,12 @@
 //   the same rounding in U_b as in o and u_b - m_b o does not lose its digits.
 // Both passes stream the visible K/V blocks through the same LDS stages as the
 // attention kernel; a workgroup holds several tiles of one KV head so each fetch is
-// shared by up to 128 columns. P V runs as two bf16 MFMAs (P = hi + lo) so the
-// block sums keep about 16 bits of P: u_b - m_b o cancels when v_b is close to o.
+// shared by up to 128 columns. In pass 2, P V runs as two bf16 MFMAs (P = hi + lo)
+// so the block sums keep about 16 bits of P: with one bf16 P, a block whose mass
+// sits on a few keys would carry up to 2^-9 relative error in I_b. Pass 1 takes one
+// bf16 P for o: the row's maximum key weighs exactly 1 and the rounding of the other
+// weights averages out over every visible key (the scores move by about 1e-6
+// relative either way on the 128K layer).
 //
 // Threshold (sel_threshold_kernel): per (query head, tile), the tile score is the
 // mean of I over the sampled rows; candidates (visible, not mandatory) are sorted
@@ -167,19 +171,18 @@ void sel_sweep_kernel(SelectParams p) {
   if constexpr (PIPE) {
     // Software pipeline over stages, as in the attention kernel: K and V in separate
     // double buffers, V one stage behind K. Step j: the QK^T MFMAs of stage j next to
-    // the exponentials (and sums) of stage j-1; then the split P V MFMAs of stage j-1
-    // next to the hi/lo packs of its following key step and, in pass 1, stage j's
-    // running max. Every wave computes every stage of the workgroup: a stage whose keys
-    // all lie above the wave's rows is fully masked, so its weights are exactly zero
-    // (such stages are the last few of the wave). In pass 2 o is read back only when a
-    // block is finalised.
+    // the exponentials (and sums) of stage j-1; then the P V MFMAs of stage j-1 next
+    // to the bf16 packs of its following key step and stage j's running max. Every
+    // wave computes every stage of the workgroup: a stage whose keys all lie above the
+    // wave's rows is fully masked, so its weights are exactly zero (such stages are the
+    // last few of the wave).
     __shared__ __attribute__((aligned(16))) char kb0[St::TENSOR];
     __shared__ __attribute__((aligned(16))) char kb1[St::TENSOR];
     __shared__ __attribute__((aligned(16))) char vb0[St::TENSOR];
     __shared__ __attribute__((aligned(16))) char vb1[St::TENSOR];
     constexpr int NQK = 2 * (D / 16);  // QK^T MFMAs per stage
     constexpr int NDT = D / 32;        // d tiles of O
-    constexpr int NPV = 4 * NDT;       // (V fragment, key step) pairs per stage, two MFMAs each
+    constexpr int NPV = 4 * NDT;       // P V MFMAs per stage (V fragment, key step)
     constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
     constexpr int XPM = 32 / NPV;      // max candidates per V fragment (pass 1)
     const typename St::LaneOffsets lofs = St::lane_offsets(row_stride, tid);
@@ -274,10 +277,11 @@ void sel_sweep_kernel(SelectParams p) {
       }
       if constexpr (PASS2) mloc += rs;
       else l_run += rs;
-      // PV phase: O += V^T (P_hi + P_lo) with the packs one key step ahead
+      // PV phase: O += V^T P with the packs one key step ahead (one bf16 P: see the
+      // file header)
       __builtin_amdgcn_s_setprio(1);
-      bf16x8 ph[2], pl[2];
-      p_step<true>(Sp, 0, ph[0], pl[0]);
+      bf16x8 ph[2], unused;
+      p_step<false>(Sp, 0, ph[0], unused);
       bf16x8 va[2];
       va[0] = St::v_frag(vprev, 0, 0, lane);
 #pragma unroll
@@ -285,8 +289,7 @@ void sel_sweep_kernel(SelectParams p) {
         const int dt = i % NDT, st = i / NDT;
         if (i + 1 < NPV) va[(i + 1) & 1] = St::v_frag(vprev, (i + 1) % NDT, (i + 1) / NDT, lane);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st & 1], O[dt], 0, 0, 0);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st & 1], O[dt], 0, 0, 0);
-        if (dt == 0 && st + 1 < 4) p_step<true>(Sp, st + 1, ph[(st + 1) & 1], pl[(st + 1) & 1]);
+        if (dt == 0 && st + 1 < 4) p_step<false>(Sp, st + 1, ph[(st + 1) & 1], unused);
         if constexpr (!PASS2) {
 #pragma unroll
           for (int u = 0; u < XPM; ++u) {
