@@ -113,8 +113,15 @@ poem_status build_geometry(const poem_problem* p, Geometry& g) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct SelLayout {
-  size_t row_stats = 0, blk_stats = 0, counts = 0, slots = 0, total = 0;
+  size_t row_stats = 0, blk_stats = 0, counts = 0, slots = 0, v16 = 0, vscale = 0, total = 0;
 };
+
+// key blocks over all sequences (ceil(N_k / B) each)
+int64_t total_key_blocks(const Geometry& g) {
+  int64_t n = 0;
+  for (int s = 0; s < g.st.num_seqs; ++s) n += g.st.diag0[s] + g.st.n_tiles[s];
+  return n;
+}
 
 // Record columns per (KV head, tile): per-head lists pack the G heads' S rows into
 // 32-column tiles; a group-shared list has S columns.
@@ -134,6 +141,12 @@ SelLayout sel_layout(const poem_problem* p, const Geometry& g, int cols) {
   off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.num_tiles);
   L.slots = off;
   off += align256(sizeof(int32_t) * (size_t)p->num_heads_q * g.vis_per_head);
+  if (p->in_dtype == POEM_BF16) {  // fp16 V and its block scales for pass 2
+    L.v16 = off;
+    off += align256(sizeof(uint16_t) * (size_t)g.total_k * p->num_heads_kv * p->head_dim);
+    L.vscale = off;
+    off += align256(sizeof(float) * (size_t)p->num_heads_kv * total_key_blocks(g));
+  }
   L.total = off;
   return L;
 }
@@ -258,6 +271,11 @@ static poem_status select_impl(int mode, bool group_mode, float prac_w, float pr
   sp.blk_stats = reinterpret_cast<float*>(ws + L.blk_stats);
   sp.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   sp.slots = reinterpret_cast<int32_t*>(ws + L.slots);
+  if (problem->in_dtype == POEM_BF16) {
+    sp.v16 = reinterpret_cast<uint16_t*>(ws + L.v16);
+    sp.vscale = reinterpret_cast<float*>(ws + L.vscale);
+  }
+  sp.total_kb = (int32_t)total_key_blocks(g);
   sp.row_ptr = row_ptr;
   sp.block_idx = block_idx;
   sp.tile_scores = tile_scores;

@@ -21,6 +21,8 @@ namespace poem {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
@@ -47,6 +49,13 @@ struct SeqTable {
   int64_t vis_start[kMaxSeqs];   // per head: visible (tile, block) pairs of earlier sequences
   int64_t vis_per_head;          // per head: all visible (tile, block) pairs
 };
+
+// Key blocks of the sequences before s (a sequence has diag0 + n_tiles of them).
+__host__ __device__ __forceinline__ int kblocks_before(const SeqTable& st, int s) {
+  int n = 0;
+  for (int i = 0; i < s; ++i) n += st.diag0[i] + st.n_tiles[i];
+  return n;
+}
 
 // Visible (tile, block) pairs before tile t of sequence s, per head.
 __host__ __device__ __forceinline__ int64_t vis_offset(const SeqTable& st, int s, int t) {
@@ -200,6 +209,30 @@ __device__ __forceinline__ void p_step(const f32x16 (&p)[2], int s, bf16x8& hi, 
   }
   hi = __builtin_bit_cast(bf16x8, w);
   if constexpr (SPLIT) lo = __builtin_bit_cast(bf16x8, wl);
+}
+
+// One 16-key step of fp32 weights as fp16 (round to nearest even), in the operand
+// layout of p_step.
+__device__ __forceinline__ f16x8 p_step_f16(const f32x16 (&p)[2], int s) {
+  const int kt = s >> 1, r0 = 8 * (s & 1);
+  f16x8 h;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const f32x2 ab = {p[kt][r0 + 2 * e], p[kt][r0 + 2 * e + 1]};
+    const f16x2 w = __builtin_convertvector(ab, f16x2);
+    h[2 * e] = w[0];
+    h[2 * e + 1] = w[1];
+  }
+  return h;
+}
+
+// Sum of the eight fp16 weights of a packed step, added to acc in fp32.
+__device__ __forceinline__ float row_sum_f16(const f16x8& p, float acc) {
+  const f16x2 one = {(_Float16)1.0f, (_Float16)1.0f};
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 0, 1), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 2, 3), one, acc, false);
+  acc = __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 4, 5), one, acc, false);
+  return __builtin_amdgcn_fdot2(__builtin_shufflevector(p, p, 6, 7), one, acc, false);
 }
 
 // ---------------------------------------------------------------------------

@@ -64,6 +64,11 @@ struct SelectParams {
   float* blk_stats;          // per (KV head, gtile, visible block): I[cols_rec] then m[cols_rec]
   int32_t* counts;           // [hq * total_tiles]
   int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets
+  // bf16 inputs: V for pass 2 as fp16, each (key block, KV head) scaled by a power of
+  // two vscale so that its largest |v| lies in [2^14, 2^15); same layout as V
+  uint16_t* v16;             // [total_k][hkv][D]
+  float* vscale;             // [hkv][total_kb]
+  int32_t total_kb;          // key blocks over all sequences
   // outputs
   int32_t* row_ptr;
   int32_t* block_idx;

@@ -17,12 +17,18 @@
 //   the same rounding in U_b as in o and u_b - m_b o does not lose its digits.
 // Both passes stream the visible K/V blocks through the same LDS stages as the
 // attention kernel; a workgroup holds several tiles of one KV head so each fetch is
-// shared by up to 128 columns. In pass 2, P V runs as two bf16 MFMAs (P = hi + lo)
-// so the block sums keep about 16 bits of P: with one bf16 P, a block whose mass
-// sits on a few keys would carry up to 2^-9 relative error in I_b. Pass 1 takes one
-// bf16 P for o: the row's maximum key weighs exactly 1 and the rounding of the other
-// weights averages out over every visible key (the scores move by about 1e-6
-// relative either way on the 128K layer).
+// shared by up to 128 columns.
+//
+// Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o: the row's maximum
+// key weighs exactly 1 and the rounding of the other weights averages out over every
+// visible key. Pass 2 needs more: with bf16 weights (2^-9 relative rounding), a block
+// whose mass sits on a few keys would carry up to 2^-9 relative error in I_b. It runs
+// P V on fp16 instead (2^-11): v16_kernel first writes V as fp16, each (key block,
+// KV head) scaled by a power of two s_b that puts its largest |v| in [2^14, 2^15)
+// (exact for bf16 values, whose 8-bit significands fit fp16's 11, down to s_b |v| =
+// 2^-14); the weights are formed as 2^14 w_j, at most 2^14, so fp16 keeps 11 bits of
+// them down to w_j = 2^-28. U_b - L_b o is formed with L_b the sum of the same fp16
+// weights, so I_b sees each weight's rounding once, as a perturbation of the weight.
 //
 // Threshold (sel_threshold_kernel): per (query head, tile), the tile score is the
 // mean of I over the sampled rows; candidates (visible, not mandatory) are sorted
@@ -37,6 +43,9 @@ namespace poem {
 constexpr int kSelThreads = 256;
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 constexpr int kSelWaves = 4;
+// fp16 P V of pass 2: weights carry 2^14 (log2 and inverse)
+constexpr float kP16Log2 = 14.f;
+constexpr float kP16Inv = 1.f / 16384.f;
 
 // MASS: the mass-only selector needs neither o nor U_b, so both passes skip P V and
 // stage K alone.
@@ -50,6 +59,8 @@ void sel_sweep_kernel(SelectParams p) {
   // (which also holds o for its per-block norms), the mass-only passes and fp32 run
   // the plain double-buffered sweep
   constexpr bool PIPE = St::ASYNC && !MASS && !PASS2;
+  // bf16 pass 2 of the output-relative selectors: P V on fp16 (see the file header)
+  constexpr bool F16PV = St::ASYNC && PASS2 && !MASS;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
@@ -105,7 +116,15 @@ void sel_sweep_kernel(SelectParams p) {
 
   const int64_t row_stride = (int64_t)p.hkv * D;
   const T* kbase = reinterpret_cast<const T*>(p.k) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
-  const T* vbase = reinterpret_cast<const T*>(p.v) + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+  const T* vsrc;
+  if constexpr (F16PV) vsrc = reinterpret_cast<const T*>(p.v16);
+  else vsrc = reinterpret_cast<const T*>(p.v);
+  const T* vbase = vsrc + ((int64_t)p.seqs.k_start[seq] * p.hkv + gk) * D;
+  // fp16 V: the scale of each key block of this sequence and KV head (read-only here,
+  // so the reads go through the scalar cache)
+  using cfloat = const __attribute__((address_space(4))) float;
+  cfloat* vsc = nullptr;
+  if constexpr (F16PV) vsc = (cfloat*)p.vscale + (int64_t)gk * p.total_kb + kblocks_before(p.seqs, seq);
   // per column: M2, l, two pad words, then o (16-byte aligned)
   float* rs_col = p.row_stats + (((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + (in_range ? col : 0)) * (D + 4);
   const float c = p.scale_log2;
@@ -116,6 +135,7 @@ void sel_sweep_kernel(SelectParams p) {
   // pass 1: running max and sum; pass 2: M2, l, dense output o, block weight sum
   float m_run = -INFINITY, l_run = 0.f;
   float m2 = 0.f, inv_l = 0.f, mloc = 0.f;
+  float lt = 0.f;  // fp16 P V: the block's sum of the fp16 weights
   f32x16 Od[D / 32];
   if constexpr (PASS2) {
     if (col_on) {
@@ -149,22 +169,31 @@ void sel_sweep_kernel(SelectParams p) {
   const int total = nblk_wg * SUBS;
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
   // pass 2: I and m of one block from its weight sum and U (O), for the pair's column
+  // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
+  // U - L o is formed at that scale, with L the sum of the same fp16 weights
   auto finalize_block = [&](int blk, const f32x16 (&o)[D / 32]) {
-    const float mt = mloc + wave_xor32(mloc);
+    float mt = mloc + wave_xor32(mloc);
+    float lo_coef = mt, i_scale = inv_l;
+    if constexpr (F16PV) {
+      const float sb = vsc[blk];
+      lo_coef = (lt + wave_xor32(lt)) * sb;
+      i_scale = inv_l * kP16Inv / sb;
+      mt *= kP16Inv;
+    }
     float ss = 0.f;
     if constexpr (!MASS) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float dv = __builtin_fmaf(-mt, o[dt][r], O[dt][r]);
+          const float dv = __builtin_fmaf(-lo_coef, o[dt][r], O[dt][r]);
           ss = __builtin_fmaf(dv, dv, ss);
         }
       ss += wave_xor32(ss);
     }
     if (col_on && g2 == 0) {
       float* dst = blk_I + (int64_t)blk * bstride;
-      if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * inv_l;
+      if constexpr (!MASS) dst[0] = __builtin_sqrtf(ss) * i_scale;
       dst[p.cols_rec] = mt * inv_l;
     }
   };
@@ -335,7 +364,7 @@ void sel_sweep_kernel(SelectParams p) {
   // pass 2 stage for bf16 (see its call below); MASKED: the stage reaches past a row
   auto pass2_stage = [&](auto masked_tag, const char* cur, int key0) {
     constexpr bool MASKED = decltype(masked_tag)::value;
-    if constexpr (St::ASYNC && PASS2 && !MASS) {
+    if constexpr (F16PV) {
       constexpr int ST = D / 16;   // d steps of one QK^T tile
       constexpr int NDT = D / 32;  // d tiles of O
       auto kfrag = [&](int kt, int st) {
@@ -343,9 +372,10 @@ void sel_sweep_kernel(SelectParams p) {
         return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + r * St::ROW +
                                                                             ((2 * st + g2) ^ St::kswz(r)) * 16));
       };
+      const float wbias = kP16Log2 - m2;  // weights 2^14 w_j, at most 2^14 (fp16 range)
       auto weight = [&](float s, int kt, int r) {
         if (MASKED && key0 + acc_key(kt, r, g2) > my_pos) return 0.f;
-        return __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, -m2));
+        return __builtin_amdgcn_exp2f(__builtin_fmaf(s, c, wbias));
       };
       const char* vt = cur + St::TENSOR;
       f32x16 S0 = {}, S1 = {};
@@ -359,7 +389,7 @@ void sel_sweep_kernel(SelectParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       f32x16 Sp[2];
-      bf16x8 ph[4], pl[4];
+      f16x8 ph[4];
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < ST; ++i) {  // key tile 1, next to the weights of key tile 0
@@ -373,8 +403,9 @@ void sel_sweep_kernel(SelectParams p) {
         }
         if (i == ST - 1) {
           Sp[0] = S0;
-          p_step<true>(Sp, 0, ph[0], pl[0]);
-          p_step<true>(Sp, 1, ph[1], pl[1]);
+          ph[0] = p_step_f16(Sp, 0);
+          ph[1] = p_step_f16(Sp, 1);
+          lt = row_sum_f16(ph[1], row_sum_f16(ph[0], lt));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -385,8 +416,7 @@ void sel_sweep_kernel(SelectParams p) {
       for (int i = 0; i < 2 * NDT; ++i) {
         const int dt = i % NDT, st = i / NDT;
         va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st], O[dt], 0, 0, 0);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st], O[dt], 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 16 / (2 * NDT); ++u) {
           const int r = i * (16 / (2 * NDT)) + u;
@@ -395,8 +425,9 @@ void sel_sweep_kernel(SelectParams p) {
         }
         if (i == 2 * NDT - 1) {
           Sp[1] = S1;
-          p_step<true>(Sp, 2, ph[2], pl[2]);
-          p_step<true>(Sp, 3, ph[3], pl[3]);
+          ph[2] = p_step_f16(Sp, 2);
+          ph[3] = p_step_f16(Sp, 3);
+          lt = row_sum_f16(ph[3], row_sum_f16(ph[2], lt));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -405,8 +436,7 @@ void sel_sweep_kernel(SelectParams p) {
       for (int i = 2 * NDT; i < 4 * NDT; ++i) {  // key steps 2 and 3
         const int dt = i % NDT, st = i / NDT;
         if (i + 1 < 4 * NDT) va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st], O[dt], 0, 0, 0);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], pl[st], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st], O[dt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -418,10 +448,11 @@ void sel_sweep_kernel(SelectParams p) {
 #pragma unroll
       for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
       mloc = 0.f;
+      lt = 0.f;
     }
-    if constexpr (St::ASYNC && PASS2 && !MASS) {
+    if constexpr (F16PV) {
       // pass 2, bf16: one stage with its work overlapped inside the wave. The QK^T MFMAs
-      // of key tile 1 run next to the weights of key tile 0; the first half of the split
+      // of key tile 1 run next to the weights of key tile 0; the first half of the fp16
       // P V next to the weights and packs of key tile 1; fragments are read ahead.
       if (key0 <= wave_pos_max) {
         if (key0 + kStageKeys - 1 > wave_pos_min) pass2_stage(BoolTag<true>{}, cur, key0);
@@ -1095,6 +1126,67 @@ __global__ __launch_bounds__(64) void csr_scatter_kernel(SelectParams p) {
   for (int i = threadIdx.x; i < n; i += 64) dst[i] = src[i];
 }
 
+// fp16 copy of V for pass 2 (bf16 inputs): one workgroup per (key block, KV head),
+// KV head fastest. s_b = 2^(15 - e) with e the binary exponent of the block's largest
+// |v| (|v| = f 2^e, f in [0.5, 1)), clamped to normal floats; a block that holds
+// non-finite values keeps s_b = 1. Rows past the sequence end are not written (pass 2
+// reads them as zeros).
+constexpr int kV16Threads = 256;
+template <int D, int BLK>
+__global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
+  constexpr int CH = D / 8;  // 16-byte chunks per row
+  constexpr int PER = BLK * CH / kV16Threads;
+  static_assert(PER * kV16Threads == BLK * CH, "block must split evenly");
+  __shared__ uint32_t red[kV16Threads / 64];
+  const int tid = threadIdx.x;
+  const int g = blockIdx.x % p.hkv, kb = blockIdx.x / p.hkv;
+  int seq = 0, base = 0;
+  while (seq + 1 < p.seqs.num_seqs && kb >= base + p.seqs.diag0[seq] + p.seqs.n_tiles[seq]) {
+    base += p.seqs.diag0[seq] + p.seqs.n_tiles[seq];
+    ++seq;
+  }
+  const int row0 = (kb - base) * BLK;
+  const int rows = min(BLK, p.seqs.n_k[seq] - row0);
+  const int64_t first = ((int64_t)p.seqs.k_start[seq] + row0) * p.hkv + g;  // row 0 of the block, in rows of D
+  const uint16_t* src = reinterpret_cast<const uint16_t*>(p.v);
+  u32x4 w[PER];
+  uint32_t amax = 0;  // largest |v| as bf16 bits (ordered like the values)
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * kV16Threads, r = c / CH, ch = c % CH;
+    w[i] = u32x4{0u, 0u, 0u, 0u};
+    if (r < rows) w[i] = *reinterpret_cast<const u32x4*>(src + (first + (int64_t)r * p.hkv) * D + ch * 8);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) amax = max(amax, max(w[i][e] & 0x7FFFu, (w[i][e] >> 16) & 0x7FFFu));
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) amax = max(amax, (uint32_t)__shfl_xor((int)amax, off));
+  if ((tid & 63) == 0) red[tid >> 6] = amax;
+  __syncthreads();
+  amax = red[0];
+#pragma unroll
+  for (int i = 1; i < kV16Threads / 64; ++i) amax = max(amax, red[i]);
+  // biased exponent E of the largest |v|: |v| in [2^(E-127), 2^(E-126)), so e = E - 126
+  const int E = (int)(amax >> 7);
+  const int k = E >= 255 ? 0 : min(141 - E, 127);  // s_b = 2^(15 - e) = 2^(141 - E)
+  const float sb = __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
+  uint16_t* dst = p.v16;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int c = tid + i * kV16Threads, r = c / CH, ch = c % CH;
+    if (r < rows) {
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const f32x2 ab = {bf16_lo_to_f32(w[i][e]) * sb, bf16_hi_to_f32(w[i][e]) * sb};
+        o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(ab, f16x2));
+      }
+      *reinterpret_cast<u32x4*>(dst + (first + (int64_t)r * p.hkv) * D + ch * 8) = o;
+    }
+  }
+  if (tid == 0) p.vscale[(int64_t)g * p.total_kb + kb] = sb;
+}
+
 template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   const int TG = p.group_mode ? kSelWaves * p.tiles_per_wave : max(1, kSelWaves / p.col_tiles);
@@ -1112,6 +1204,9 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
   } else {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    if (sizeof(T) == 2 && p.total_kb > 0)
+      hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
+                         p);
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
   }
   // threshold grid: (KV-head unit, head in group) with the unit's XCD kept fixed
