@@ -90,7 +90,9 @@ int64_t poem_max_visible_blocks(const poem_problem* problem);
 
 /* Bytes of device workspace the selectors need (256-byte aligned start): enough for
  * poem_select, poem_select_mass, poem_select_practical and poem_select_group at this
- * rows_per_tile; < 0 on error. */
+ * rows_per_tile; < 0 on error. It holds per-row softmax statistics, per-block masses
+ * and scores, retained-id slots and, for bf16 inputs, an fp16 copy of V (the size of
+ * V) with one scale per (key block, KV head) for the second pass. */
 int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile);
 
 /*
