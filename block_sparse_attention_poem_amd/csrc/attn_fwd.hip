@@ -291,15 +291,25 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     if (total > 0) {
       first();
       if constexpr (KA == 2) {
-        // stage it: K in kb[it % 3], V in vb[it % 2]; six steps per trip keep every
-        // buffer a distinct LDS object in each step
-        for (int it = 1; it < total; it += 6) {
+        // stage it: K in kb[it % 3], V in vb[it % 2]. Six unconditional steps per trip
+        // keep every buffer a distinct LDS object in each step, so the compiler sees
+        // that reading K(it) never waits on the K(it + 1) load still in flight (a
+        // conditional step would merge the two); the last stages take the buffers
+        // picked at run time.
+        int it = 1;
+        for (; it + 5 < total; it += 6) {
           step(it, kb1, kb0, vb0, vb1);
-          if (it + 1 < total) step(it + 1, kb2, kb1, vb1, vb0);
-          if (it + 2 < total) step(it + 2, kb0, kb2, vb0, vb1);
-          if (it + 3 < total) step(it + 3, kb1, kb0, vb1, vb0);
-          if (it + 4 < total) step(it + 4, kb2, kb1, vb0, vb1);
-          if (it + 5 < total) step(it + 5, kb0, kb2, vb1, vb0);
+          step(it + 1, kb2, kb1, vb1, vb0);
+          step(it + 2, kb0, kb2, vb0, vb1);
+          step(it + 3, kb1, kb0, vb1, vb0);
+          step(it + 4, kb2, kb1, vb0, vb1);
+          step(it + 5, kb0, kb2, vb1, vb0);
+        }
+        for (; it < total; ++it) {
+          const int r3 = it % 3;
+          char* kc = r3 == 0 ? kb0 : (r3 == 1 ? kb1 : kb2);
+          char* kn = r3 == 0 ? kb2 : (r3 == 1 ? kb0 : kb1);
+          step(it, kc, kn, (it & 1) ? vb0 : vb1, (it & 1) ? vb1 : vb0);
         }
       } else {
         for (int it = 1; it < total; it += 2) {
