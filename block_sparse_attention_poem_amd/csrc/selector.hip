@@ -263,49 +263,40 @@ void sel_sweep_kernel(SelectParams p) {
       wait_vmem_all();
       __syncthreads();
     }
-    // step it (1 <= it <= total): QK of stage it (it < total), softmax and P V of it - 1
-    auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
-      const bool more = it < total;
-      const int key0 = more ? stage_key0(it) : 0;
-      if (more) {
+    // step it (1 <= it <= total): with MORE (it < total) the QK of stage it, then the
+    // softmax and P V of stage it - 1; the last step (it = total) has P V alone
+    auto step = [&](auto more_tag, int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
+      constexpr bool MORE = decltype(more_tag)::value;
+      const int key0 = MORE ? stage_key0(it) : 0;
+      if constexpr (MORE) {
         St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext, lofs);
         St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lofs);
-      }
-      const int pit = it - 1;
-      if constexpr (PASS2) {
-        if (pit % SUBS == 0) {  // the block of stage it - 1 starts: fresh U and weight sum
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x16{};
-          mloc = 0.f;
-        }
       }
       f32x16 Sn[2] = {f32x16{}, f32x16{}};
       float mx = -INFINITY;
       // QK phase
       bf16x8 ka[3];
-      if (more) {
+      if constexpr (MORE) {
         ka[0] = kfrag(kcur, 0);
         ka[1] = kfrag(kcur, 1);
       }
-      const float ref = PASS2 ? m2 : m_use;
       float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
-        if (more) {
+        if constexpr (MORE) {
           Sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf.q[i >> 1], Sn[i & 1], 0, 0, 0);
           if (i + 2 < NQK) ka[(i + 2) % 3] = kfrag(kcur, i + 2);
         }
 #pragma unroll
         for (int u = 0; u < EPM; ++u) {
           const int e = i * EPM + u;
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -ref));
+          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
           Sp[e >> 4][e & 15] = x;
           rs += x;
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (PASS2) mloc += rs;
-      else l_run += rs;
+      l_run += rs;
       // PV phase: O += V^T P with the packs one key step ahead (one bf16 P: see the
       // file header)
       __builtin_amdgcn_s_setprio(1);
@@ -319,7 +310,7 @@ void sel_sweep_kernel(SelectParams p) {
         if (i + 1 < NPV) va[(i + 1) & 1] = St::v_frag(vprev, (i + 1) % NDT, (i + 1) / NDT, lane);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st & 1], O[dt], 0, 0, 0);
         if (dt == 0 && st + 1 < 4) p_step<false>(Sp, st + 1, ph[(st + 1) & 1], unused);
-        if constexpr (!PASS2) {
+        if constexpr (MORE) {
 #pragma unroll
           for (int u = 0; u < XPM; ++u) {
             const int e = i * XPM + u;
@@ -329,35 +320,31 @@ void sel_sweep_kernel(SelectParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
-      if (more) {
+      if constexpr (MORE) {
         if (key0 + kStageKeys - 1 > wave_pos_min) {
           mask(Sn, key0);
-          if constexpr (!PASS2) {
-            mx = -INFINITY;
+          mx = -INFINITY;
 #pragma unroll
-            for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
-          }
+          for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
         }
-        if constexpr (!PASS2) finish_max(mx);
+        finish_max(mx);
+        Sp[0] = Sn[0];
+        Sp[1] = Sn[1];
+        wait_vmem_all();
+        __syncthreads();
       }
-      if constexpr (PASS2) {
-        // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
-        const int blk = pit / SUBS;
-        if (pit % SUBS == SUBS - 1 && in_range && blk <= diag) {
-          f32x16 o[NDT];
-          load_o(o);
-          finalize_block(blk, o);
-        }
-      }
-      Sp[0] = Sn[0];
-      Sp[1] = Sn[1];
-      wait_vmem_all();
-      __syncthreads();
     };
-    for (int it = 1; it <= total; it += 2) {
-      step(it, kb1, kb0, vb0, vb1);
-      if (it + 1 <= total) step(it + 1, kb0, kb1, vb1, vb0);
+    int it = 1;
+    for (; it + 1 < total; it += 2) {
+      step(BoolTag<true>{}, it, kb1, kb0, vb0, vb1);
+      step(BoolTag<true>{}, it + 1, kb0, kb1, vb1, vb0);
     }
+    if (it < total) {
+      step(BoolTag<true>{}, it, kb1, kb0, vb0, vb1);
+      ++it;
+    }
+    // it == total: the P V of the last stage, whose V sits in vb[(total - 1) & 1]
+    if (total > 0) step(BoolTag<false>{}, it, nullptr, nullptr, ((total - 1) & 1) ? vb1 : vb0, nullptr);
   } else {
   __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
   __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
