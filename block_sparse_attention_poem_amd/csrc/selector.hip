@@ -28,7 +28,8 @@
 // (exact for bf16 values, whose 8-bit significands fit fp16's 11, down to s_b |v| =
 // 2^-14); the weights are formed as 2^14 w_j, at most 2^14, so fp16 keeps 11 bits of
 // them down to w_j = 2^-28. U_b - L_b o is formed with L_b the sum of the same fp16
-// weights, so I_b sees each weight's rounding once, as a perturbation of the weight.
+// weights, so I_b sees each weight's rounding once, as a perturbation of the weight;
+// m_b = L_b / l comes from that sum too (at most 2^-12 relative per weight).
 //
 // Threshold (sel_threshold_kernel): per (query head, tile), the tile score is the
 // mean of I over the sampled rows; candidates (visible, not mandatory) are sorted
@@ -170,15 +171,19 @@ void sel_sweep_kernel(SelectParams p) {
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
   // pass 2: I and m of one block from its weight sum and U (O), for the pair's column
   // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
-  // U - L o is formed at that scale, with L the sum of the same fp16 weights
+  // U - L o is formed at that scale, with L the sum of the same fp16 weights (which
+  // also gives m_b = L / l)
   auto finalize_block = [&](int blk, const f32x16 (&o)[D / 32]) {
-    float mt = mloc + wave_xor32(mloc);
-    float lo_coef = mt, i_scale = inv_l;
+    float mt, lo_coef, i_scale = inv_l;
     if constexpr (F16PV) {
       const float sb = vsc[blk];
-      lo_coef = (lt + wave_xor32(lt)) * sb;
+      const float ltt = lt + wave_xor32(lt);
+      lo_coef = ltt * sb;
       i_scale = inv_l * kP16Inv / sb;
-      mt *= kP16Inv;
+      mt = ltt * kP16Inv;
+    } else {
+      mt = mloc + wave_xor32(mloc);
+      lo_coef = mt;
     }
     float ss = 0.f;
     if constexpr (!MASS) {
@@ -349,8 +354,11 @@ void sel_sweep_kernel(SelectParams p) {
   __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
   __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
   // pass 2 stage for bf16 (see its call below); MASKED: the stage reaches past a row
-  auto pass2_stage = [&](auto masked_tag, const char* cur, int key0) {
+  // MASKED: the stage reaches past a row; FIRST: it opens a block, so its first P V
+  // MFMA of each d tile starts from zero instead of O
+  auto pass2_stage = [&](auto masked_tag, auto first_tag, const char* cur, int key0) {
     constexpr bool MASKED = decltype(masked_tag)::value;
+    constexpr bool FIRST = decltype(first_tag)::value;
     if constexpr (F16PV) {
       constexpr int ST = D / 16;   // d steps of one QK^T tile
       constexpr int NDT = D / 32;  // d tiles of O
@@ -377,7 +385,6 @@ void sel_sweep_kernel(SelectParams p) {
       }
       f32x16 Sp[2];
       f16x8 ph[4];
-      float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < ST; ++i) {  // key tile 1, next to the weights of key tile 0
         S1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[(ST + i) % 3], qf.q[i], S1, 0, 0, 0);
@@ -386,7 +393,6 @@ void sel_sweep_kernel(SelectParams p) {
         for (int u = 0; u < 16 / ST; ++u) {
           const int r = i * (16 / ST) + u;
           S0[r] = weight(S0[r], 0, r);
-          rs += S0[r];
         }
         if (i == ST - 1) {
           Sp[0] = S0;
@@ -403,12 +409,12 @@ void sel_sweep_kernel(SelectParams p) {
       for (int i = 0; i < 2 * NDT; ++i) {
         const int dt = i % NDT, st = i / NDT;
         va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st], O[dt], 0, 0, 0);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st],
+                                                       (FIRST && st == 0) ? f32x16{} : O[dt], 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 16 / (2 * NDT); ++u) {
           const int r = i * (16 / (2 * NDT)) + u;
           S1[r] = weight(S1[r], 1, r);
-          rs += S1[r];
         }
         if (i == 2 * NDT - 1) {
           Sp[1] = S1;
@@ -418,7 +424,6 @@ void sel_sweep_kernel(SelectParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      mloc += rs;
 #pragma unroll
       for (int i = 2 * NDT; i < 4 * NDT; ++i) {  // key steps 2 and 3
         const int dt = i % NDT, st = i / NDT;
@@ -432,18 +437,28 @@ void sel_sweep_kernel(SelectParams p) {
     const int blk = it / SUBS, sub = it % SUBS;
     const int key0 = stage_key0(it);
     if (PASS2 && sub == 0) {
+      if constexpr (!F16PV) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
+        for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
+      }
       mloc = 0.f;
       lt = 0.f;
     }
     if constexpr (F16PV) {
       // pass 2, bf16: one stage with its work overlapped inside the wave. The QK^T MFMAs
       // of key tile 1 run next to the weights of key tile 0; the first half of the fp16
-      // P V next to the weights and packs of key tile 1; fragments are read ahead.
+      // P V next to the weights and packs of key tile 1; fragments are read ahead. A
+      // block's first stage always runs when the block is finalised (its keys start at
+      // or below the tile's first row), so it is the one that starts U from zero.
       if (key0 <= wave_pos_max) {
-        if (key0 + kStageKeys - 1 > wave_pos_min) pass2_stage(BoolTag<true>{}, cur, key0);
-        else pass2_stage(BoolTag<false>{}, cur, key0);
+        const bool masked = key0 + kStageKeys - 1 > wave_pos_min;
+        if (sub == 0) {
+          if (masked) pass2_stage(BoolTag<true>{}, BoolTag<true>{}, cur, key0);
+          else pass2_stage(BoolTag<false>{}, BoolTag<true>{}, cur, key0);
+        } else {
+          if (masked) pass2_stage(BoolTag<true>{}, BoolTag<false>{}, cur, key0);
+          else pass2_stage(BoolTag<false>{}, BoolTag<false>{}, cur, key0);
+        }
       }
     } else if (key0 <= wave_pos_max) {
       f32x16 S[2];
