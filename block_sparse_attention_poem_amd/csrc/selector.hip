@@ -687,11 +687,13 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   const int64_t diag_row = ((int64_t)w.h0 * T + w.gtile) * p.max_vis;
   auto tau_of = [&](int i) { return p.tau[w.h0 + (w.tau_group ? i % w.tau_group : 0)]; };
 
-  // scores of this thread's blocks tid * E + e, as sort keys (score bits, ~id)
+  // scores of blocks e * 256 + tid (consecutive lanes read consecutive records, so
+  // the staged reads stay off each other's banks), as sort keys (score bits, ~id);
+  // the sort does not care where a key starts
   uint64_t x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int b = tid * E + e;
+    const int b = e * kThrThreads + tid;
     x[e] = ~0ull;
     if (b < n_vis) {
       float si = 0.f, sm = 0.f;
@@ -732,7 +734,11 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   // sums its E consecutive positions, a vector scan gives each thread its exclusive
   // prefixes, and the first prefix length whose per-row bound exceeds tau is a block
   // minimum. With `limit` = the cut, the same walk yields the per-row bound at the cut.
-  auto walk = [&](int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
+  // KEEP (one chunk holds every row): the find walk also keeps each position's per-row
+  // bounds, so the bounds at the cut need no second walk.
+  float kept_b[E][kRowChunk];
+  auto walk = [&](auto keep_tag, int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
+    constexpr bool KEEP = decltype(keep_tag)::value;
     double A[kRowChunk], Dl[kRowChunk];
 #pragma unroll
     for (int r = 0; r < kRowChunk; ++r) A[r] = Dl[r] = 0.0;
@@ -760,6 +766,7 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
             Dl[r] += (double)m_of(ids[e], i0 + r);
             const double bound = bound_of(A[r], Dl[r]);
             over |= bound > (double)tau_of(i0 + r);
+            if constexpr (KEEP) kept_b[e][r] = (float)bound;
             if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
           }
         if (find && over && local_fail == INT_MAX) local_fail = k + 1;
@@ -767,18 +774,34 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
     }
   };
   int k_fail = n_cand + 1;
-  for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+  const bool one_chunk = s_t <= kRowChunk;
+  if (one_chunk) {
     int local_fail = INT_MAX;
-    walk(i0, min(kRowChunk, s_t - i0), n_cand, true, local_fail, nullptr);
+    walk(BoolTag<true>{}, 0, s_t, n_cand, true, local_fail, nullptr);
     k_fail = min(k_fail, block_min_int(local_fail, shi));
+  } else {
+    for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+      int local_fail = INT_MAX;
+      walk(BoolTag<false>{}, i0, min(kRowChunk, s_t - i0), n_cand, true, local_fail, nullptr);
+      k_fail = min(k_fail, block_min_int(local_fail, shi));
+    }
   }
   const int k_star = k_fail - 1;
 
   if (p.row_bound) {
     float* rb = p.row_bound + ((int64_t)w.h0 * T + w.gtile) * S;
-    for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
-      int unused = INT_MAX;
-      walk(i0, min(kRowChunk, s_t - i0), k_star, false, unused, rb);
+    if (one_chunk) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (k_star > 0 && tid * E + e == k_star - 1)
+#pragma unroll
+          for (int r = 0; r < kRowChunk; ++r)
+            if (r < s_t) rb[r] = kept_b[e][r];
+    } else {
+      for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+        int unused = INT_MAX;
+        walk(BoolTag<false>{}, i0, min(kRowChunk, s_t - i0), k_star, false, unused, rb);
+      }
     }
     for (int i = tid; i < S; i += kThrThreads)
       if (i >= s_t) rb[i] = -1.f;
