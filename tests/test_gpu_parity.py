@@ -320,6 +320,54 @@ def test_selector_matches_oracle(case, sink, n_local):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
+def _scale_value_blocks(inp, w, lo, hi, seed):
+    """V with each (key block, KV head) multiplied by 2^k, k uniform on lo..hi: exact in
+    bf16, and it spans far more than fp16's range, so the fp16 copy of V that the
+    selector's second pass reads must take a scale per block."""
+    import dataclasses
+    rng = np.random.default_rng(seed)
+    v = synth.bf16_bits_to_f32(inp.v) if inp.is_bf16 else inp.v.astype(np.float32)
+    B = w.block_size
+    out = v.copy()
+    k0 = 0
+    for nk in w.seqlens_k:
+        for b0 in range(0, nk, B):
+            for g in range(w.num_heads_kv):
+                out[k0 + b0:k0 + min(b0 + B, nk), g] *= np.float32(2.0 ** int(rng.integers(lo, hi + 1)))
+        k0 += nk
+    out_v = synth.round_to_bf16_bits(out) if inp.is_bf16 else out
+    if inp.is_bf16:
+        assert np.array_equal(synth.bf16_bits_to_f32(out_v), out)  # the scaling is exact
+    return dataclasses.replace(inp, v=out_v)
+
+
+SCALES = [
+    # case, block scale exponents lo..hi
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 20, 20),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), -24, -24),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), -20, 20),
+    ((256, 4096, 8, 2, 128, 128, "bf16", 1), -20, 20),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), -12, 12),
+]
+
+
+@pytest.mark.parametrize("case,lo,hi", SCALES, ids=lambda x: str(x))
+def test_selector_value_scales(case, lo, hi):
+    """Scores and masks when V's blocks range from 2^-24 to 2^20 in scale (the second
+    pass's fp16 V carries one power-of-two scale per key block and KV head)."""
+    w = _small(case, seed=11)
+    inp = _scale_value_blocks(synth.make(w), w, lo, hi, seed=3)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("selector with V block scales 2^", lo, "..", hi)
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v)
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
 MASS = [
     # case, sink_offset, n_local, eps (omitted-mass budget)
     ((300, 428, 4, 1, 64, 64, "bf16", 1), 6.0, 1, 0.002),
