@@ -526,34 +526,6 @@ template <typename T, int D, int NT> using Stage = typename StageSel<T, D, NT>::
 
 __device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
 
-// Scheduling hints (instruction groups the compiler fills in order within the current
-// basic block; results do not depend on them). Masks: MFMA, VALU, LDS read, VMEM read.
-constexpr int kSgMfma = 0x008, kSgValu = 0x002, kSgDsRead = 0x100, kSgVmemRead = 0x020;
-// One pipelined attention stage: 16 QK^T MFMAs (16 K reads) next to the previous
-// stage's exponentials and bf16 packs, then its 16 P V MFMAs (32 transposing V
-// reads). LDS reads run ahead of the MFMAs that consume them.
-__device__ __forceinline__ void sched_stage() {
-  __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-#pragma unroll
-  for (int i = 0; i < 14; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 7, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 16; ++i) {
-    __builtin_amdgcn_sched_group_barrier(kSgMfma, 1, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgDsRead, 2, 0);
-    __builtin_amdgcn_sched_group_barrier(kSgValu, 1, 0);
-  }
-}
-
 // Workgroup barrier that does not drain global loads (__syncthreads waits for every
 // outstanding load, including direct loads into LDS still meant to be in flight).
 // Each wave has already waited, with an explicit s_waitcnt vmcnt, for the direct loads
