@@ -19,9 +19,9 @@
 // attention kernel; a workgroup holds several tiles of one KV head so each fetch is
 // shared by up to 128 columns.
 //
-// Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o: the row's maximum
-// key weighs exactly 1 and the rounding of the other weights averages out over every
-// visible key. Pass 2 needs more: with bf16 weights (2^-9 relative rounding), a block
+// Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o and l: the row's
+// maximum key weighs exactly 1, the rounding of the other weights averages out over
+// every visible key, and o is the exact mean under the rounded weights. Pass 2 needs more: with bf16 weights (2^-9 relative rounding), a block
 // whose mass sits on a few keys would carry up to 2^-9 relative error in I_b. It runs
 // P V on fp16 instead (2^-11): v16_kernel first writes V as fp16, each (key block,
 // KV head) scaled by a power of two s_b that puts its largest |v| in [2^14, 2^15)
@@ -285,7 +285,6 @@ void sel_sweep_kernel(SelectParams p) {
         ka[0] = kfrag(kcur, 0);
         ka[1] = kfrag(kcur, 1);
       }
-      float rs = 0.f;
 #pragma unroll
       for (int i = 0; i < NQK; ++i) {
         if constexpr (MORE) {
@@ -295,18 +294,17 @@ void sel_sweep_kernel(SelectParams p) {
 #pragma unroll
         for (int u = 0; u < EPM; ++u) {
           const int e = i * EPM + u;
-          const float x = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
-          Sp[e >> 4][e & 15] = x;
-          rs += x;
+          Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += rs;
       // PV phase: O += V^T P with the packs one key step ahead (one bf16 P: see the
-      // file header)
+      // file header); l adds the same bf16 weights, two per dot instruction, so o is
+      // their exact weighted mean
       __builtin_amdgcn_s_setprio(1);
       bf16x8 ph[2], unused;
       p_step<false>(Sp, 0, ph[0], unused);
+      float rs = row_sum_bf16(ph[0], 0.f);
       bf16x8 va[2];
       va[0] = St::v_frag(vprev, 0, 0, lane);
 #pragma unroll
@@ -314,7 +312,10 @@ void sel_sweep_kernel(SelectParams p) {
         const int dt = i % NDT, st = i / NDT;
         if (i + 1 < NPV) va[(i + 1) & 1] = St::v_frag(vprev, (i + 1) % NDT, (i + 1) / NDT, lane);
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st & 1], O[dt], 0, 0, 0);
-        if (dt == 0 && st + 1 < 4) p_step<false>(Sp, st + 1, ph[(st + 1) & 1], unused);
+        if (dt == 0 && st + 1 < 4) {
+          p_step<false>(Sp, st + 1, ph[(st + 1) & 1], unused);
+          rs = row_sum_bf16(ph[(st + 1) & 1], rs);
+        }
         if constexpr (MORE) {
 #pragma unroll
           for (int u = 0; u < XPM; ++u) {
@@ -325,6 +326,7 @@ void sel_sweep_kernel(SelectParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       __builtin_amdgcn_s_setprio(0);
+      l_run += rs;
       if constexpr (MORE) {
         if (key0 + kStageKeys - 1 > wave_pos_min) {
           mask(Sn, key0);
