@@ -57,6 +57,19 @@ def test_geometry_queries(lib):
     assert ws > 0 and ws % 256 == 0
 
 
+def test_select_workspace_holds_fp16_values():
+    """bf16 inputs add an fp16 copy of V (2 bytes per element) and one fp32 scale per
+    (key block, KV head) to the select workspace; fp32 inputs need neither."""
+    a256 = lambda x: -(-x // 256) * 256
+    for kw in (dict(), dict(seqlens_q=[64, 0, 100], seqlens_k=[128, 64, 100]),
+               dict(seqlens_q=[100], seqlens_k=[4196], head_dim=128, block_size=128)):
+        pb, pf = prob(**kw), prob(dtype="fp32", **kw)
+        nk = sum(pb.seqlens_k)
+        kblocks = sum(-(-n // pb.block_size) for n in pb.seqlens_k)
+        extra = a256(2 * nk * pb.num_heads_kv * pb.head_dim) + a256(4 * pb.num_heads_kv * kblocks)
+        assert L.select_workspace_bytes(pb, 8) - L.select_workspace_bytes(pf, 8) == extra, kw
+
+
 @pytest.mark.parametrize("kw,status", [
     (dict(seqlens_q=[300], seqlens_k=[429]), L.POEM_ERR_INVALID_ARG),   # N_k - N_q not a multiple of B
     (dict(seqlens_q=[300], seqlens_k=[200]), L.POEM_ERR_INVALID_ARG),   # N_k < N_q
