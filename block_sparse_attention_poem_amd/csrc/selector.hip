@@ -550,13 +550,15 @@ void sel_sweep_kernel(SelectParams p) {
 // ---------------------------------------------------------------------------
 
 constexpr int kThrThreads = 256;
+constexpr int kThrWaves = kThrThreads / 64;
 constexpr int kMaxVis = 4096;
 constexpr int kStageVis = 1024;   // STAGED: visible blocks per tile
 constexpr int kStageVals = 8192;  // STAGED: visible blocks x sampled rows
 constexpr int kXcds = 8;
 
 // Exclusive prefix over the workgroup, in thread order, of N pairs of doubles (each
-// thread's A[r], D[r] are replaced by the sums over lower threads). sh: 8 * N doubles.
+// thread's A[r], D[r] are replaced by the sums over lower threads). sh: 2 * N *
+// kThrWaves doubles.
 constexpr int kRowChunk = 8;
 template <int N>
 __device__ __forceinline__ void block_excl_scan_vec(double (&A)[N], double (&D)[N], double* sh) {
@@ -574,7 +576,10 @@ __device__ __forceinline__ void block_excl_scan_vec(double (&A)[N], double (&D)[
   }
   if (lane == 63) {
 #pragma unroll
-    for (int r = 0; r < N; ++r) { sh[(2 * r) * 4 + wave] = ia[r]; sh[(2 * r + 1) * 4 + wave] = id[r]; }
+    for (int r = 0; r < N; ++r) {
+      sh[(2 * r) * kThrWaves + wave] = ia[r];
+      sh[(2 * r + 1) * kThrWaves + wave] = id[r];
+    }
   }
   __syncthreads();
 #pragma unroll
@@ -582,7 +587,7 @@ __device__ __forceinline__ void block_excl_scan_vec(double (&A)[N], double (&D)[
     double xa = __shfl_up(ia[r], 1), xd = __shfl_up(id[r], 1);
     if (lane == 0) { xa = 0.0; xd = 0.0; }
     double oa = 0.0, od = 0.0;
-    for (int w = 0; w < wave; ++w) { oa += sh[(2 * r) * 4 + w]; od += sh[(2 * r + 1) * 4 + w]; }
+    for (int w = 0; w < wave; ++w) { oa += sh[(2 * r) * kThrWaves + w]; od += sh[(2 * r + 1) * kThrWaves + w]; }
     A[r] = oa + xa;
     D[r] = od + xd;
   }
@@ -1031,8 +1036,8 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   __shared__ float st_I[STAGED && NEED_I ? kStageVals : 1];
   __shared__ float bar_I[PRAC ? NK : 1], bar_m[PRAC ? NK : 1];  // practical: pooled estimates
   __shared__ float st_m[STAGED ? kStageVals : 1];
-  __shared__ double shd[8 * kRowChunk];
-  __shared__ int shi[8];
+  __shared__ double shd[2 * kRowChunk * kThrWaves];
+  __shared__ int shi[kThrWaves];
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
   const int G = p.group_mode ? 1 : p.group;  // workgroups per (KV head, tile)
@@ -1102,16 +1107,14 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
     if constexpr (PRAC) practical_tile<STAGED, E>(p, w, st_I, st_m, bar_I, bar_m, sh, keep, shd, shi);
     else threshold_tile<MODE, STAGED, E>(p, w, st_I, st_m, sh, keep, shd, shi);
   };
+  // keys per thread; staged tiles hold at most kStageVis blocks
+  constexpr int EMAX = STAGED ? kStageVis / kThrThreads : kMaxVis / kThrThreads;
   switch (n_pad / kThrThreads) {
     case 1: run(IntTag<1>{}); break;
-    case 2: run(IntTag<2>{}); break;
-    case 4: run(IntTag<4>{}); break;
-    default:
-      if constexpr (!STAGED) {
-        if (n_pad == 8 * kThrThreads) run(IntTag<8>{});
-        else run(IntTag<16>{});
-      }
-      break;
+    case 2: if constexpr (EMAX >= 2) run(IntTag<2>{}); break;
+    case 4: if constexpr (EMAX >= 4) run(IntTag<4>{}); break;
+    case 8: if constexpr (EMAX >= 8) run(IntTag<8>{}); break;
+    default: if constexpr (EMAX >= 16) run(IntTag<16>{}); break;
   }
 }
 
