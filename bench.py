@@ -188,8 +188,8 @@ def _time_select_sparse(gp, L, w, q, k, v, ws, sws, taus, mode, steps, **kw):
         r = L.select(gp, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, workspace=ws, mode=mode,
                      **kw)
         ev[i][1].record()
-        L.sparse_prefill(gp, q, k, v, r["row_ptr"], r["block_idx"], out_dtype="bf16", want_lse=False,
-                         workspace=sws)
+        prefill = L.sparse_prefill_group if mode == "group" else L.sparse_prefill
+        prefill(gp, q, k, v, r["row_ptr"], r["block_idx"], out_dtype="bf16", want_lse=False, workspace=sws)
         ev[i][2].record()
     torch.cuda.synchronize()
     t_sel = float(np.median([ev[i][0].elapsed_time(ev[i][1]) for i in range(steps)]))
@@ -213,9 +213,9 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
     tau = torch.tensor([float(x) for x in inp.tau], device="cuda")
     od, _ = L.dense_prefill(gp, q, k, v, out_dtype="fp32", want_lse=False)
 
-    def errors(rr):
-        o, _ = L.sparse_prefill(gp, q, k, v, rr["row_ptr"], rr["block_idx"], out_dtype="fp32", want_lse=False,
-                                workspace=sws)
+    def errors(rr, group=False):
+        prefill = L.sparse_prefill_group if group else L.sparse_prefill
+        o, _ = prefill(gp, q, k, v, rr["row_ptr"], rr["block_idx"], out_dtype="fp32", want_lse=False, workspace=sws)
         e = torch.linalg.vector_norm(o - od, dim=-1)
         del o
         return e
@@ -277,11 +277,12 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
     del e_pr
 
     r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, inp.tau, "group", steps)
-    e_g = errors(r)
+    e_g = errors(r, group=True)
     res_g = {"select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap,
              "err_group": _err_stats(e_g, si, tau), "err_poem": out["err_poem"],
              "note": "same per-head thresholds as the headline step; one list per (KV head, tile) from the "
-                     "group's 8 sampled rows; sampled_rows_within_tau is taken on the per-head selector's rows"}
+                     "group's 8 sampled rows, run by poem_sparse_prefill_group; sampled_rows_within_tau is taken "
+                     "on the per-head selector's rows"}
     del od, e_g
     torch.cuda.empty_cache()
     return res_m, res_g, res_p

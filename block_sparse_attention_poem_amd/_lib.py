@@ -22,7 +22,7 @@ STATUS_NAMES = {0: "POEM_OK", -1: "POEM_ERR_INVALID_ARG", -2: "POEM_ERR_UNSUPPOR
                 -4: "POEM_ERR_CAPACITY", -5: "POEM_ERR_HIP"}
 SYMBOLS = ["poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_select_workspace_bytes",
            "poem_sparse_workspace_bytes", "poem_select", "poem_select_mass", "poem_select_group", "poem_select_practical",
-           "poem_sparse_prefill", "poem_dense_prefill",
+           "poem_sparse_prefill", "poem_sparse_prefill_group", "poem_dense_prefill",
            "poem_last_error", "poem_version"]
 
 
@@ -79,6 +79,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.poem_select_practical.restype = ctypes.c_int
     lib.poem_sparse_prefill.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.poem_sparse_prefill.restype = ctypes.c_int
+    lib.poem_sparse_prefill_group.argtypes = lib.poem_sparse_prefill.argtypes
+    lib.poem_sparse_prefill_group.restype = ctypes.c_int
     lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp]
     lib.poem_dense_prefill.restype = ctypes.c_int
     lib.poem_last_error.restype = ctypes.c_char_p
@@ -280,6 +282,24 @@ def sparse_prefill(problem: Problem, q, k, v, row_ptr, block_idx, out_dtype: str
     _check(load().poem_sparse_prefill(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
                                       _ptr(block_idx), _ptr(out), POEM_FP32 if out_dtype == "fp32" else POEM_BF16,
                                       _ptr(lse), wp, wb, _stream_ptr(stream)))
+    return out, lse
+
+
+def sparse_prefill_group(problem: Problem, q, k, v, row_ptr, block_idx, out_dtype: str = "bf16",
+                         want_lse: bool = True, out=None, lse=None, workspace="auto", stream=None):
+    """Run poem_sparse_prefill_group (lists shared by each GQA group, read from the
+    group's first head). Returns (out, lse). workspace as for sparse_prefill."""
+    _check_qkv(problem, q, k, v)
+    if out is None:
+        out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+    if isinstance(workspace, str):
+        workspace = SparseWorkspace(problem, q.device)
+    wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.nbytes if workspace is not None else 0
+    _check(load().poem_sparse_prefill_group(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                            _ptr(block_idx), _ptr(out),
+                                            POEM_FP32 if out_dtype == "fp32" else POEM_BF16, _ptr(lse), wp, wb,
+                                            _stream_ptr(stream)))
     return out, lse
 
 

@@ -43,7 +43,8 @@ struct AttnCfg {
   __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];           \
   __shared__ __attribute__((aligned(16))) char vb1[AttnCfg<T, D, BLK>::VBUF];
 
-// One (query head h, tile t of sequence seq): the whole workgroup, B rows.
+// One (query head h, tile t of sequence seq): the whole workgroup, B rows. Sparse: the
+// list of h, or with p.shared that of h's GQA group's first head.
 template <typename T, int D, int BLK, bool SPARSE>
 __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* kb0, char* kb1,
                                           char* kb2, char* vb0, char* vb1) {
@@ -80,7 +81,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   cint* ids = nullptr;
   int nblk;
   if constexpr (SPARSE) {
-    const int64_t r = (int64_t)h * p.seqs.total_tiles + p.seqs.tile_start[seq] + t;
+    const int hl = p.shared ? (h / p.group) * p.group : h;  // the head whose list is walked
+    const int64_t r = (int64_t)hl * p.seqs.total_tiles + p.seqs.tile_start[seq] + t;
     cint* rp = (cint*)p.row_ptr;
     const int a = rp[r], b = rp[r + 1];
     ids = (cint*)p.block_idx + a;
@@ -419,11 +421,13 @@ void attn_sparse_persistent_kernel(AttnParams p) {
 // in LDS; one workgroup per KV head, whose rows h*T .. are contiguous), KV heads one
 // after another, and resets the queue head. Pulling rows in this order keeps the
 // running workgroups on one KV head's K/V at a time (64 MiB at 128K tokens), which
-// the 256 MiB memory-side cache can hold while the rows re-read it.
+// the 256 MiB memory-side cache can hold while the rows re-read it. shared_tiles > 0
+// (shared lists): row i of a KV head's block takes the count of its group's first-head
+// row, i mod shared_tiles.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 4097;  // counts are clamped to 4096 for ordering only
 __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const int32_t* __restrict__ row_ptr,
-                                                                       int rows_per_group,
+                                                                       int rows_per_group, int shared_tiles,
                                                                        int32_t* __restrict__ order_all,
                                                                        int32_t* __restrict__ queue) {
   __shared__ int hist[kSchedBins];
@@ -435,7 +439,7 @@ __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const in
   for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
   auto bin = [&](int i) {
-    const int r = first + i;
+    const int r = first + (shared_tiles > 0 ? i % shared_tiles : i);
     const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), kSchedBins - 1);
     return kSchedBins - 1 - c;  // longest first
   };
@@ -469,7 +473,7 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   if (grid == 0) return hipSuccess;
   if (SPARSE && p.queue != nullptr) {
     hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
-                       p.num_rows / p.hkv, p.order, p.queue);
+                       p.num_rows / p.hkv, p.shared ? p.seqs.total_tiles : 0, p.order, p.queue);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);

@@ -336,7 +336,8 @@ static size_t sparse_ws_bytes(const poem_problem* p, const Geometry& g) {
 
 static poem_status attention(const poem_problem* problem, const void* q, const void* k, const void* v,
                              const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
-                             float* lse, void* workspace, size_t workspace_bytes, void* stream, bool sparse) {
+                             float* lse, void* workspace, size_t workspace_bytes, void* stream, bool sparse,
+                             bool shared) {
   Geometry g;
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
@@ -368,6 +369,7 @@ static poem_status attention(const poem_problem* problem, const void* q, const v
   ap.total_q = (int32_t)g.total_q;
   ap.scale_log2 = g.scale * poem::kLog2e;
   ap.num_rows = (int32_t)(problem->num_heads_q * g.num_tiles);
+  ap.shared = shared ? 1 : 0;
   if (sparse && workspace != nullptr) {
     ap.queue = static_cast<int32_t*>(workspace);
     ap.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
@@ -375,7 +377,8 @@ static poem_status attention(const poem_problem* problem, const void* q, const v
   ap.seqs = g.st;
   return hip_status(poem::launch_attention(ap, problem->in_dtype, problem->head_dim, problem->block_size, sparse,
                                            static_cast<hipStream_t>(stream)),
-                    sparse ? "poem_sparse_prefill launch" : "poem_dense_prefill launch");
+                    !sparse ? "poem_dense_prefill launch"
+                            : (shared ? "poem_sparse_prefill_group launch" : "poem_sparse_prefill launch"));
 }
 
 int64_t poem_sparse_workspace_bytes(const poem_problem* problem) {
@@ -390,12 +393,20 @@ poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, cons
                                 const int32_t* row_ptr, const int32_t* block_idx, void* out, int32_t out_dtype,
                                 float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, workspace, workspace_bytes, stream,
-                   true);
+                   true, false);
+}
+
+poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q, const void* k, const void* v,
+                                      const int32_t* row_ptr, const int32_t* block_idx, void* out,
+                                      int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes,
+                                      void* stream) {
+  return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, workspace, workspace_bytes, stream,
+                   true, true);
 }
 
 poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k, const void* v, void* out,
                                int32_t out_dtype, float* lse, void* stream) {
-  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, nullptr, 0, stream, false);
+  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, nullptr, 0, stream, false, false);
 }
 
 const char* poem_last_error(void) { return g_error.c_str(); }

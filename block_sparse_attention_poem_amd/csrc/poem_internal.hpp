@@ -26,6 +26,7 @@ struct AttnParams {
   int32_t* queue;            // queue head, reset by the schedule kernel
   int32_t* order;            // [num_rows] rows by retained count, descending
   int32_t num_rows;          // hq * total_tiles
+  int32_t shared;            // sparse: every head reads the list of its GQA group's first head
   SeqTable seqs;
 };
 

@@ -258,6 +258,20 @@ poem_status poem_sparse_prefill(const poem_problem* problem, const void* q, cons
                                 size_t workspace_bytes, void* stream);
 
 /*
+ * poem_sparse_prefill_group: poem_sparse_prefill for lists shared by the query heads of
+ * each GQA group, as poem_select_group writes them (BFLA Section 3.3 groups heads by
+ * KV head; Section 3.4 restricts the kernel to the listed blocks). Every head of a
+ * group walks the list of the group's first head, row (g G) * num_tiles + tile (the
+ * schedule orders rows by that list's length); the other heads' rows are not read. The
+ * result equals poem_sparse_prefill on a CSR that repeats each first head's row under
+ * every head of its group. Arguments, workspace and errors as for poem_sparse_prefill.
+ */
+poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q, const void* k,
+                                      const void* v, const int32_t* row_ptr, const int32_t* block_idx,
+                                      void* out, int32_t out_dtype, float* lse, void* workspace,
+                                      size_t workspace_bytes, void* stream);
+
+/*
  * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t
  * (dense causal attention, the speedup baseline). Arguments as above.
  */

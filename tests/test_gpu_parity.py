@@ -479,6 +479,32 @@ def test_group_selector_matches_oracle(case, sink, n_local, S):
     nc, nm, ws = check_group_selection(w, inp.tau, gp, op, r, units, q, k, v, d_out.cpu().numpy(),
                                        s_out.cpu().numpy())
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+    check_group_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"])
+
+
+def check_group_prefill(gp, qd, kd, vd, row_ptr, block_idx):
+    """poem_sparse_prefill_group on a shared-list CSR equals poem_sparse_prefill bit for
+    bit, and reads only each group's first-head rows: with the other heads' rows emptied
+    the result is the same, under both schedules (count-ordered queue and static)."""
+    import torch
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, row_ptr, block_idx, out_dtype="fp32")
+    g_out, g_lse = L.sparse_prefill_group(gp, qd, kd, vd, row_ptr, block_idx, out_dtype="fp32")
+    rp, bi = H.csr_rows(row_ptr, block_idx)
+    T = L.num_tiles(gp)
+    G = gp.num_heads_q // gp.num_heads_kv
+    rows, ids = [0], []
+    for r in range(gp.num_heads_q * T):
+        if (r // T) % G == 0:
+            ids.extend(bi[rp[r]:rp[r + 1]].tolist())
+        rows.append(len(ids))
+    rp1 = torch.tensor(rows, dtype=torch.int32, device=qd.device)
+    bi1 = torch.tensor(ids + [0], dtype=torch.int32, device=qd.device)
+    f_out, f_lse = L.sparse_prefill_group(gp, qd, kd, vd, rp1, bi1, out_dtype="fp32")
+    h_out, h_lse = L.sparse_prefill_group(gp, qd, kd, vd, rp1, bi1, out_dtype="fp32", workspace=None)
+    _sync()
+    assert torch.equal(g_out, s_out) and torch.equal(g_lse, s_lse)
+    assert torch.equal(f_out, s_out) and torch.equal(f_lse, s_lse)
+    assert torch.equal(h_out, s_out) and torch.equal(h_lse, s_lse)
 
 
 def check_practical(w, eps_h, wt, rho, gp, op, r, which, q, k, v):
