@@ -16,9 +16,9 @@
 //   maximum key exactly 1, so the block that dominates o (typically the sink) sees
 //   the same rounding in U_b as in o and u_b - m_b o does not lose its digits.
 // Both passes stream the visible K/V blocks through the same LDS stages as the
-// attention kernel; a workgroup of eight waves holds several tiles of one KV head
-// (one CU each: two waves per SIMD), so each fetch is shared by up to 256 columns and
-// the direct loads per MFMA are half those of four-wave workgroups (measured: the
+// attention kernel; a workgroup of eight waves (bf16) holds several tiles of one KV
+// head (one CU each: two waves per SIMD), so each fetch is shared by up to 256 columns
+// and the direct loads per MFMA are half those of four-wave workgroups (measured: the
 // selector's two passes run 6% faster at 128K).
 //
 // Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o and l: the row's
@@ -43,9 +43,10 @@
 
 namespace poem {
 
-constexpr int kSelThreads = 512;
+// Sweep workgroup: eight waves for bf16; fp32 stages need more than the 256 VGPRs two
+// waves per SIMD leave, so fp32 keeps four waves (one per SIMD).
+template <typename T> constexpr int sel_threads() { return sizeof(T) == 2 ? 512 : 256; }
 template <bool B> struct BoolTag { static constexpr bool value = B; };
-constexpr int kSelWaves = kSelThreads / 64;
 // fp16 P V of pass 2: weights carry 2^14 (log2 and inverse)
 constexpr float kP16Log2 = 14.f;
 constexpr float kP16Inv = 1.f / 16384.f;
@@ -53,9 +54,10 @@ constexpr float kP16Inv = 1.f / 16384.f;
 // MASS: the mass-only selector needs neither o nor U_b, so both passes skip P V and
 // stage K alone.
 template <typename T, int D, int BLK, bool PASS2, bool MASS>
-__global__ __launch_bounds__(kSelThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(sel_threads<T>()) __attribute__((amdgpu_waves_per_eu(sizeof(T) == 2 ? 2 : 1, 2)))
 void sel_sweep_kernel(SelectParams p) {
-  using St = Stage<T, D, kSelThreads>;
+  constexpr int kSelWaves = sel_threads<T>() / 64;
+  using St = Stage<T, D, sel_threads<T>()>;
   constexpr int SUBS = BLK / kStageKeys;
   constexpr bool SPLIT = sizeof(T) == 2;
   // bf16 pass 1 of the output-relative selectors runs the pipelined sweep below; pass 2
@@ -1221,6 +1223,8 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
 
 template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
+  constexpr int kSelWaves = sel_threads<T>() / 64;
+  constexpr int kSelThreads = sel_threads<T>();
   const int TG = p.group_mode ? kSelWaves * p.tiles_per_wave : max(1, kSelWaves / p.col_tiles);
   int items = 0;
   for (int i = 0; i < p.seqs.num_seqs; ++i) items += (p.seqs.n_tiles[i] + TG - 1) / TG;
