@@ -245,6 +245,8 @@ SEL = [
     ((300, 428, 2, 1, 64, 64, "fp32", 1), 6.0, 1),
     ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1),
     ((64, 4160, 2, 1, 64, 64, "bf16", 1), 7.0, 1),
+    # more than 1024 visible blocks: the threshold reads the records from the workspace
+    ((128, 66048, 2, 1, 64, 64, "bf16", 1), 6.0, 1),
 ]
 
 
@@ -376,6 +378,7 @@ MASS = [
     ((300, 428, 2, 1, 64, 64, "fp32", 1), 6.0, 1, 0.002),
     ((100, 356, 4, 1, 128, 128, "bf16", 3), 6.0, 1, 0.003),
     ((64, 4160, 2, 1, 64, 64, "bf16", 1), 7.0, 1, 0.001),
+    ((128, 66048, 2, 1, 64, 64, "bf16", 1), 6.0, 1, 0.002),  # > 1024 visible blocks
 ]
 
 
