@@ -175,11 +175,9 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     // The row sums add the bf16 weights the P V MFMAs use (two per dot instruction), so
     // numerator and denominator see the same rounding.
     f32x16 Sp[2];
+    const typename St::KOffsets ko = St::k_offsets(lane);
     auto kfrag = [&](const char* kbuf, int i) {  // K operand of QK MFMA i
-      const int kt = i & 1, st = i >> 1;
-      const int r = 32 * kt + (lane & 31);
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + r * St::ROW +
-                                                                          ((2 * st + g2) ^ St::kswz(r)) * 16));
+      return St::k_frag(kbuf, ko, i & 1, i >> 1);
     };
     auto finish_max = [&](float mx) {  // running max of the stage, rare rescale
       mx = fmaxf(mx, wave_xor32(mx));

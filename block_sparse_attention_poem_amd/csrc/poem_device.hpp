@@ -291,9 +291,14 @@ struct StageB16 {
     const uint32_t wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const uint32_t lane = (uint32_t)tid & 63u;
     const uint32_t row_bytes = (uint32_t)(row_stride * 2);
-    const int rows = max(0, min(n_valid - key0, kStageKeys));
-    // uniform by construction; readfirstlane keeps the descriptor in scalar registers
-    const int records = __builtin_amdgcn_readfirstlane((int)(rows * row_bytes));
+    // Valid rows of the stage, clamped to [0, kStageKeys] with scalar instructions: the
+    // empty statement between the two clamps keeps them from fusing into a vector med3.
+    // Uniform by construction; the "s" constraint keeps the value in a scalar register.
+    int rows = n_valid - key0;
+    rows = rows < kStageKeys ? rows : kStageKeys;
+    __asm__("" : "+s"(rows));
+    rows = rows > 0 ? rows : 0;
+    const int records = rows * (int)row_bytes;
     const __amdgpu_buffer_rsrc_t rsrc = __builtin_amdgcn_make_buffer_rsrc(
         (void*)(reinterpret_cast<const char*>(base_ptr) + (int64_t)key0 * row_stride * 2), (short)0, records,
         0x00020000);
@@ -305,8 +310,10 @@ struct StageB16 {
       if constexpr (IS_V) off = lo.v;
       else if constexpr (K_FIXED) off = lo.k;
       else off = lane_off(row_bytes, lane, r0, false);
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_char*)(dst + blk * 1024), 16, (int)(r0 * row_bytes + off),
-                                               0, 0, 0);
+      // the row group's byte offset goes in the scalar offset (it counts toward the
+      // range check like the lane's vector offset), so no vector add per load
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rsrc, (lds_char*)(dst + blk * 1024), 16, (int)off,
+                                               (int)(r0 * row_bytes), 0, 0);
     }
   }
   static __device__ __forceinline__ void load_k(const uint16_t* kbase, int64_t row_stride, int key0, int n_valid,
@@ -335,6 +342,28 @@ struct StageB16 {
   static __device__ __forceinline__ void store(const Regs&, char*, int) {}
   // the direct loads write LDS asynchronously: wait for this wave's before the barrier
   static constexpr bool ASYNC = true;
+
+  // Per-lane byte offsets of the QK^T K operands within a K buffer, one per d step s:
+  // row lane % 32, chunk (2s + lane / 32) ^ swizzle. Key tile kt adds 32 rows, which
+  // leaves the swizzle unchanged. The empty statements make the offsets opaque, so the
+  // compiler keeps them whole and folds each buffer's fixed LDS address into the
+  // read's immediate offset instead of re-adding it every stage.
+  struct KOffsets {
+    uint32_t o[D / 16];
+  };
+  static __device__ __forceinline__ KOffsets k_offsets(int lane) {
+    KOffsets ko;
+    const int r = lane & 31, g = (lane >> 5) & 1;
+#pragma unroll
+    for (int st = 0; st < D / 16; ++st) {
+      ko.o[st] = (uint32_t)(r * ROW + (((2 * st + g) ^ kswz(r)) << 4));
+      __asm__ volatile("" : "+v"(ko.o[st]));
+    }
+    return ko;
+  }
+  static __device__ __forceinline__ bf16x8 k_frag(const char* kbuf, const KOffsets& ko, int kt, int st) {
+    return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + 32 * kt * ROW + ko.o[st]));
+  }
 
   // S^T for 32-key tile kt: acc = K[32kt + i][:] . Q[:][j]
   static __device__ __forceinline__ f32x16 qk_tile(const char* lds, const QFrag<uint16_t, D>& qf, int kt, int lane) {
@@ -418,6 +447,8 @@ struct StageF32 {
   static constexpr int V_UNITS = (kStageKeys / 4) * CH_PER_ROW;  // 4 keys x 16 bytes
   static constexpr int V_ITERS = (V_UNITS + NT - 1) / NT;
   static constexpr bool ASYNC = false;
+  struct KOffsets {};  // the fp32 stage reads its K operands through qk_tile only
+  static __device__ __forceinline__ KOffsets k_offsets(int) { return {}; }
 
   struct Regs {
     u32x4 k[K_ITERS];

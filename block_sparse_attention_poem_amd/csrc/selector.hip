@@ -225,11 +225,9 @@ void sel_sweep_kernel(SelectParams p) {
     constexpr int XPM = 32 / NPV;      // max candidates per V fragment (pass 1)
     const typename St::LaneOffsets lofs = St::lane_offsets(row_stride, tid);
     float m_use = 0.f;  // pass 1: exponent reference of the stage being exponentiated
+    const typename St::KOffsets ko = St::k_offsets(lane);
     auto kfrag = [&](const char* kbuf, int i) {  // K operand of QK MFMA i
-      const int kt = i & 1, st = i >> 1;
-      const int r = 32 * kt + (lane & 31);
-      return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(kbuf + r * St::ROW +
-                                                                          ((2 * st + g2) ^ St::kswz(r)) * 16));
+      return St::k_frag(kbuf, ko, i & 1, i >> 1);
     };
     auto mask = [&](f32x16 (&S)[2], int key0) {
 #pragma unroll
@@ -359,6 +357,7 @@ void sel_sweep_kernel(SelectParams p) {
   } else {
   __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
   __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
+  const typename St::KOffsets ko = St::k_offsets(lane);
   // pass 2 stage for bf16 (see its call below); MASKED: the stage reaches past a row
   // MASKED: the stage reaches past a row; FIRST: it opens a block, so its first P V
   // MFMA of each d tile starts from zero instead of O
@@ -368,11 +367,7 @@ void sel_sweep_kernel(SelectParams p) {
     if constexpr (F16PV) {
       constexpr int ST = D / 16;   // d steps of one QK^T tile
       constexpr int NDT = D / 32;  // d tiles of O
-      auto kfrag = [&](int kt, int st) {
-        const int r = 32 * kt + (lane & 31);
-        return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(cur + r * St::ROW +
-                                                                            ((2 * st + g2) ^ St::kswz(r)) * 16));
-      };
+      auto kfrag = [&](int kt, int st) { return St::k_frag(cur, ko, kt, st); };
       const float wbias = kP16Log2 - m2;  // weights 2^14 w_j, at most 2^14 (fp16 range)
       auto weight = [&](float s, int kt, int r) {
         if (MASKED && key0 + acc_key(kt, r, g2) > my_pos) return 0.f;
