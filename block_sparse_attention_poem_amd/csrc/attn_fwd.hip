@@ -131,7 +131,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, S[kt][r]);
-    mx = fmaxf(mx, wave_xor32(mx));
+    mx = half_max(mx);
     const float m_new = fmaxf(m_run, mx * c);
     m_use = (m_new == -INFINITY) ? 0.f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -180,7 +180,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       return St::k_frag(kbuf, ko, i & 1, i >> 1);
     };
     auto finish_max = [&](float mx) {  // running max of the stage, rare rescale
-      mx = fmaxf(mx, wave_xor32(mx));
+      mx = half_max(mx);
       const float m_new = fmaxf(m_run, mx * c);
       const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_next);
@@ -346,7 +346,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     });
   }
 
-  const float l_tot = l_run + wave_xor32(l_run);
+  const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
     char* orow = reinterpret_cast<char*>(p.out) + (qrow * p.hq + h) * D * (p.out_f32 ? 4 : 2);

@@ -555,7 +555,25 @@ template <int D, int NT> struct StageSel<uint16_t, D, NT> { using type = StageB1
 template <int D, int NT> struct StageSel<float, D, NT> { using type = StageF32<D, NT>; };
 template <typename T, int D, int NT> using Stage = typename StageSel<T, D, NT>::type;
 
-__device__ __forceinline__ float wave_xor32(float x) { return __shfl_xor(x, 32); }
+// Lanes l and l ^ 32 hold the two halves of one accumulator column. half_sum and
+// half_max combine them with one v_permlane32_swap (a VALU lane swap between the wave's
+// halves) instead of an LDS permute and its wait. With a = b = x the swap leaves
+// a = x[l & 31] and b = x[(l & 31) + 32] in every lane, so both halves get the same
+// result. The leading s_nop gives the two wait states the swap needs after a VALU
+// write of its operands (the compiler does not see inside the statement).
+__device__ __forceinline__ void swap_halves(float& a, float& b) {
+  __asm__ volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ __forceinline__ float half_sum(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return a + b;
+}
+__device__ __forceinline__ float half_max(float x) {
+  float a = x, b = x;
+  swap_halves(a, b);
+  return fmaxf(a, b);
+}
 
 // Workgroup barrier that does not drain global loads (__syncthreads waits for every
 // outstanding load, including direct loads into LDS still meant to be in flight).

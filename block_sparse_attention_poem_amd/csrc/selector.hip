@@ -181,12 +181,12 @@ void sel_sweep_kernel(SelectParams p) {
     float mt, lo_coef, i_scale = inv_l;
     if constexpr (F16PV) {
       const float sb = vsc[blk];
-      const float ltt = lt + wave_xor32(lt);
+      const float ltt = half_sum(lt);
       lo_coef = ltt * sb;
       i_scale = inv_l * kP16Inv / sb;
       mt = ltt * kP16Inv;
     } else {
-      mt = mloc + wave_xor32(mloc);
+      mt = half_sum(mloc);
       lo_coef = mt;
     }
     float ss = 0.f;
@@ -198,7 +198,7 @@ void sel_sweep_kernel(SelectParams p) {
           const float dv = __builtin_fmaf(-lo_coef, o[dt][r], O[dt][r]);
           ss = __builtin_fmaf(dv, dv, ss);
         }
-      ss += wave_xor32(ss);
+      ss = half_sum(ss);
     }
     if (col_on && g2 == 0) {
       float* dst = blk_I + (int64_t)blk * bstride;
@@ -237,7 +237,7 @@ void sel_sweep_kernel(SelectParams p) {
           if (key0 + acc_key(kt, r, g2) > my_pos) S[kt][r] = -INFINITY;
     };
     auto finish_max = [&](float mx) {  // pass 1: running max of a stage, rare rescale
-      mx = fmaxf(mx, wave_xor32(mx));
+      mx = half_max(mx);
       const float m_new = fmaxf(m_run, mx * c);
       const float m_next = (m_new == -INFINITY) ? 0.f : m_new;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_next);
@@ -476,7 +476,7 @@ void sel_sweep_kernel(SelectParams p) {
             S[kt][r] = s;
             mx = fmaxf(mx, s);
           }
-        mx = fmaxf(mx, wave_xor32(mx));
+        mx = half_max(mx);
         const float m_new = fmaxf(m_run, mx * c);
         const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
@@ -517,7 +517,7 @@ void sel_sweep_kernel(SelectParams p) {
   }
 
   if constexpr (!PASS2) {
-    const float l_tot = l_run + wave_xor32(l_run);
+    const float l_tot = half_sum(l_run);
     if (col_on) {
       const float inv = 1.f / l_tot;
       if (g2 == 0) {
