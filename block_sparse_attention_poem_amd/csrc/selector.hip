@@ -735,6 +735,13 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
     if constexpr (POEM) return (1.0 - dl > 0.0) ? a / (1.0 - dl) : INFINITY;
     else return dl;
   };
+  // bound > t without the division: A / (1 - Delta) > t  <=>  A > t (1 - Delta) when
+  // 1 - Delta > 0 (otherwise the bound is infinite). The two forms can differ only
+  // when the bound lies within an fp64 rounding of t.
+  auto exceeds = [&](double a, double dl, double t) -> bool {
+    if constexpr (POEM) return !(1.0 - dl > 0.0) || a > t * (1.0 - dl);
+    else return dl > t;
+  };
 
   // Prefix sums over the discard order, kRowChunk sampled rows at a time: each thread
   // sums its E consecutive positions, a vector scan gives each thread its exclusive
@@ -743,6 +750,7 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   // KEEP (one chunk holds every row): the find walk also keeps each position's per-row
   // bounds, so the bounds at the cut need no second walk.
   float kept_b[E][kRowChunk];
+  const bool keep_bounds = p.row_bound != nullptr;  // the bounds at the cut are an optional output
   auto walk = [&](auto keep_tag, int i0, int nr, int limit, bool find, int& local_fail, float* rb_out) {
     constexpr bool KEEP = decltype(keep_tag)::value;
     double A[kRowChunk], Dl[kRowChunk];
@@ -770,10 +778,10 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
           if (r < nr) {
             if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
             Dl[r] += (double)m_of(ids[e], i0 + r);
-            const double bound = bound_of(A[r], Dl[r]);
-            over |= bound > (double)tau_of(i0 + r);
-            if constexpr (KEEP) kept_b[e][r] = (float)bound;
-            if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound;
+            if (find) over |= exceeds(A[r], Dl[r], (double)tau_of(i0 + r));
+            if constexpr (KEEP)
+              if (keep_bounds) kept_b[e][r] = (float)bound_of(A[r], Dl[r]);
+            if (!find && k == limit - 1) rb_out[i0 + r] = (float)bound_of(A[r], Dl[r]);
           }
         if (find && over && local_fail == INT_MAX) local_fail = k + 1;
       }
