@@ -227,7 +227,11 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lo);
       __builtin_amdgcn_sched_barrier(0);
       St::load_k(kbase, row_stride, stage_key0(min(it + KA, total - 1)), n_k, tid, knext, lo);
-      // QK phase
+      // QK phase. Raised wave priority (s_setprio) marks the phase whose issue slots this
+      // wave takes ahead of the other wave on its SIMD; measured at 128K, the sparse
+      // kernel runs best with it on the QK phase (-1.8% against the PV phase) and the
+      // dense kernel with it on the PV phase (-3.6% against the QK phase).
+      if constexpr (SPARSE) __builtin_amdgcn_s_setprio(1);
       f32x16 Sn[2] = {f32x16{}, f32x16{}};
       bf16x8 P[4];
       bf16x8 ka[3];
@@ -255,10 +259,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += rs;
-      // PV phase (the max is taken over the raw scores; masked stages redo it below). The
-      // wave issues at raised priority here, so the MFMA-heavy phase of one wave gets the
-      // issue slots ahead of the VALU-heavy phase of the other wave on its SIMD.
-      __builtin_amdgcn_s_setprio(1);
+      // PV phase (the max is taken over the raw scores; masked stages redo it below)
+      __builtin_amdgcn_s_setprio(SPARSE ? 0 : 1);
       bf16x8 va[3];
       va[0] = St::v_frag(vprev, 0, 0, lane);
       va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
@@ -281,7 +283,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 #pragma unroll
         for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
       }
-      __builtin_amdgcn_s_setprio(0);
+      if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
       finish_max(mx);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
