@@ -370,9 +370,12 @@ def main():
                                          L._ptr(block_idx), L._ptr(out), odt, L._ptr(lse),
                                          ctypes.c_void_p(sws.ptr), sws.nbytes, ctypes.c_void_p(stream.cuda_stream)))
 
+    dws = L.DenseWorkspace()
+
     def dense():
         L._check(lib.poem_dense_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(out), odt,
-                                        L._ptr(lse), ctypes.c_void_p(stream.cuda_stream)))
+                                        L._ptr(lse), ctypes.c_void_p(dws.ptr), dws.nbytes,
+                                        ctypes.c_void_p(stream.cuda_stream)))
 
     log(f"[bench] warmup {args.warmup}")
     for _ in range(args.warmup):

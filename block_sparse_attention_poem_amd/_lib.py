@@ -18,6 +18,7 @@ LIB_PATH = os.path.join(_HERE, "libpoem.so")
 POEM_OK, POEM_ERR_INVALID_ARG, POEM_ERR_UNSUPPORTED, POEM_ERR_WORKSPACE, POEM_ERR_CAPACITY, POEM_ERR_HIP = \
     0, -1, -2, -3, -4, -5
 POEM_BF16, POEM_FP32 = 0, 1
+POEM_DENSE_WORKSPACE_BYTES = 256  # include/poem.h
 STATUS_NAMES = {0: "POEM_OK", -1: "POEM_ERR_INVALID_ARG", -2: "POEM_ERR_UNSUPPORTED", -3: "POEM_ERR_WORKSPACE",
                 -4: "POEM_ERR_CAPACITY", -5: "POEM_ERR_HIP"}
 SYMBOLS = ["poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_select_workspace_bytes",
@@ -81,7 +82,7 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.poem_sparse_prefill.restype = ctypes.c_int
     lib.poem_sparse_prefill_group.argtypes = lib.poem_sparse_prefill.argtypes
     lib.poem_sparse_prefill_group.restype = ctypes.c_int
-    lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp]
+    lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.poem_dense_prefill.restype = ctypes.c_int
     lib.poem_last_error.restype = ctypes.c_char_p
     lib.poem_version.restype = ctypes.c_char_p
@@ -217,6 +218,13 @@ class SparseWorkspace(Workspace):
         super().__init__(sparse_workspace_bytes(problem), device)
 
 
+class DenseWorkspace(Workspace):
+    """Workspace for dense_prefill()'s tile queue (POEM_DENSE_WORKSPACE_BYTES)."""
+
+    def __init__(self, device="cuda"):
+        super().__init__(POEM_DENSE_WORKSPACE_BYTES, device)
+
+
 def select(problem: Problem, q, k, v, tau, n_sink_blocks: int = 1, n_local_blocks: int = 1,
            rows_per_tile: int = 8, diagnostics: bool = False, workspace: Optional[SelectWorkspace] = None,
            stream=None, mode: str = "poem", weight: float = 0.5, presel_fraction: float = 0.95):
@@ -304,13 +312,21 @@ def sparse_prefill_group(problem: Problem, q, k, v, row_ptr, block_idx, out_dtyp
 
 
 def dense_prefill(problem: Problem, q, k, v, out_dtype: str = "bf16", want_lse: bool = True, out=None, lse=None,
-                  stream=None):
-    """Run poem_dense_prefill. Returns (out, lse)."""
+                  workspace="auto", stream=None):
+    """Run poem_dense_prefill. Returns (out, lse).
+
+    workspace: a DenseWorkspace, "auto" (allocate one: tiles pulled from a queue) or
+    None (the fixed interleave of the same order)."""
     _check_qkv(problem, q, k, v)
     if out is None:
         out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+    if isinstance(workspace, str):
+        workspace = DenseWorkspace(q.device)
+    wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
+    wb = workspace.nbytes if workspace is not None else 0
     _check(load().poem_dense_prefill(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                     POEM_FP32 if out_dtype == "fp32" else POEM_BF16, _ptr(lse), _stream_ptr(stream)))
+                                     POEM_FP32 if out_dtype == "fp32" else POEM_BF16, _ptr(lse), wp, wb,
+                                     _stream_ptr(stream)))
     return out, lse
 
 

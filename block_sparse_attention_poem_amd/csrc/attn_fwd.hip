@@ -8,10 +8,14 @@
 // Online softmax runs in the log2 domain in fp32; QK^T and PV run on bf16 (or
 // fp32) MFMAs with fp32 accumulation. Only the diagonal block is masked.
 //
-// Work order: workgroups are ranked by the tile's diagonal block, longest first.
-// The KV head is the fastest-varying index of the workgroup id, so with 8 KV heads
-// and the round-robin dispatch over the 8 XCDs every XCD streams one KV head's
-// K/V through its own L2, and the query heads sharing a KV head run back to back.
+// Work order. Sparse rows: a persistent kernel pulls rows from a queue that a schedule
+// kernel sorts by retained count, one KV head after another (or, without a workspace,
+// one workgroup per row in the static order below). Dense tiles: a persistent kernel
+// walks one KV head after another, longest tile first, pulling from a queue when the
+// caller gives a workspace. Static order: workgroups ranked by the tile's diagonal
+// block, longest first, with the KV head as the fastest-varying index of the
+// workgroup id, so with 8 KV heads and the round-robin dispatch over the 8 XCDs every
+// XCD streams one KV head's K/V through its own L2.
 #include "poem_internal.hpp"
 
 namespace poem {
@@ -31,16 +35,16 @@ struct AttnCfg {
   // fp32: two stage buffers (K and transposed V together)
   static constexpr int KBUF = St::ASYNC ? St::BYTES / 2 : St::BYTES;
   static constexpr int VBUF = St::ASYNC ? St::BYTES / 2 : 16;
-  static constexpr int KBUF3 = St::ASYNC ? St::BYTES / 2 : 16;  // bf16 sparse: a third K buffer
+  static constexpr int KBUF3 = St::ASYNC ? St::BYTES / 2 : 16;  // bf16: a third K buffer
   // direct loads one wave issues for one tensor of a stage (bf16)
   static constexpr int LOADS = St::ASYNC ? (St::BYTES / 2 / 1024) / WAVES : 0;
 };
 
-#define POEM_ATTN_LDS(T, D, BLK, K3)                                                    \
-  __shared__ __attribute__((aligned(16))) char kb0[AttnCfg<T, D, BLK>::KBUF];           \
-  __shared__ __attribute__((aligned(16))) char kb1[AttnCfg<T, D, BLK>::KBUF];           \
-  __shared__ __attribute__((aligned(16))) char kb2[(K3) ? AttnCfg<T, D, BLK>::KBUF3 : 16]; \
-  __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];           \
+#define POEM_ATTN_LDS(T, D, BLK)                                              \
+  __shared__ __attribute__((aligned(16))) char kb0[AttnCfg<T, D, BLK>::KBUF];  \
+  __shared__ __attribute__((aligned(16))) char kb1[AttnCfg<T, D, BLK>::KBUF];  \
+  __shared__ __attribute__((aligned(16))) char kb2[AttnCfg<T, D, BLK>::KBUF3]; \
+  __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];  \
   __shared__ __attribute__((aligned(16))) char vb1[AttnCfg<T, D, BLK>::VBUF];
 
 // One (query head h, tile t of sequence seq): the whole workgroup, B rows. Sparse: the
@@ -156,11 +160,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
 
   if constexpr (St::ASYNC) {
     // Software pipeline over stages. V has two buffers and lags K by one stage: step j
-    // reads K(j) and V(j-1) while V(j) and K(j+KA) load. Sparse rows, whose K/V fetches
-    // mostly miss L2, use KA = 2 and three K buffers, so K, needed first in a step, has
-    // two steps of lead; dense rows (mostly L2 hits) run faster with KA = 1 and the
-    // shorter loop. The step is laid out by hand in short chunks fenced off from the
-    // scheduler:
+    // reads K(j) and V(j-1) while V(j) and K(j+2) load. K has three buffers, so K, needed
+    // first in a step, has two steps of lead (sparse rows mostly miss L2; with the same
+    // pipeline the dense tiles ran 0.3% faster than with one step of K lead). The step
+    // is laid out by hand in short chunks fenced off from the scheduler:
     //   QK phase : each QK^T MFMA of stage j with the next-but-one K fragment read and
     //              the exponentials (and bf16 packs) of stage j-1;
     //   mask     : only on stages that reach past a row;
@@ -193,23 +196,19 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       }
     };
     const typename St::LaneOffsets lo = St::lane_offsets(row_stride, tid);
-    constexpr int KA = SPARSE ? 2 : 1;
-    // KA = 2: s_waitcnt vmcnt(LOADS), every direct load but this wave's newest K stage
-    // has landed; KA = 1: vmcnt(0)
-    constexpr int kWait = KA == 2 ? (C::LOADS | 0x0F70) : 0x0F70;
+    // s_waitcnt vmcnt(LOADS): every direct load but this wave's newest K stage has landed
+    constexpr int kWait = C::LOADS | 0x0F70;
     static_assert(C::LOADS < 16, "vmcnt field");
     auto first = [&]() {
       // the waits count this wave's loads in issue order, which the fences keep
       St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0, lo);
-      if constexpr (KA == 2) {
-        __builtin_amdgcn_sched_barrier(0);
-        St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lo);
-      }
+      __builtin_amdgcn_sched_barrier(0);
+      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lo);
       __builtin_amdgcn_s_waitcnt(kWait);
       lds_barrier();
       St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0, lo);
       __builtin_amdgcn_sched_barrier(0);
-      St::load_k(kbase, row_stride, stage_key0(min(KA, total - 1)), n_k, tid, KA == 2 ? kb2 : kb1, lo);
+      St::load_k(kbase, row_stride, stage_key0(min(2, total - 1)), n_k, tid, kb2, lo);
       Sp[0] = St::qk_tile(kb0, qf, 0, lane);
       Sp[1] = St::qk_tile(kb0, qf, 1, lane);
       mask(Sp, stage_key0(0));
@@ -222,16 +221,14 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     };
     auto step = [&](int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
       const int key0 = stage_key0(it);
-      // V(it) first, then K(it + KA): with KA = 2 the wait below leaves only the K loads
-      // in flight
+      // V(it) first, then K(it + 2): the wait below leaves only the K loads in flight
       St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lo);
       __builtin_amdgcn_sched_barrier(0);
-      St::load_k(kbase, row_stride, stage_key0(min(it + KA, total - 1)), n_k, tid, knext, lo);
-      // QK phase. Raised wave priority (s_setprio) marks the phase whose issue slots this
-      // wave takes ahead of the other wave on its SIMD; measured at 128K, the sparse
-      // kernel runs best with it on the QK phase (-1.8% against the PV phase) and the
-      // dense kernel with it on the PV phase (-3.6% against the QK phase).
-      if constexpr (SPARSE) __builtin_amdgcn_s_setprio(1);
+      St::load_k(kbase, row_stride, stage_key0(min(it + 2, total - 1)), n_k, tid, knext, lo);
+      // QK phase at raised wave priority (s_setprio): its issue slots go ahead of the PV
+      // phase of the other wave on the SIMD (measured at 128K: -1.8% for the sparse
+      // kernel against raising the PV phase instead)
+      __builtin_amdgcn_s_setprio(1);
       f32x16 Sn[2] = {f32x16{}, f32x16{}};
       bf16x8 P[4];
       bf16x8 ka[3];
@@ -246,25 +243,22 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         for (int u = 0; u < EPM; ++u) {
           const int e = i * EPM + u;
           Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
-          // bf16 packs and row sums: all four key steps here (sparse), or only the first
-          // (dense; the other three go with the PV MFMAs, one key step ahead). Measured at
-          // 128K: packs in the PV phase make the dense kernel 1.9% faster and the sparse
-          // one 4.4% slower, whose raised priority sits on this phase.
-          if ((e & 7) == 7 && (SPARSE || (e >> 3) == 0)) {
+          // bf16 packs and row sums of all four key steps in this phase (measured at
+          // 128K: packs next to the PV MFMAs make the sparse kernel 4.4% slower)
+          if ((e & 7) == 7) {
             bf16x8 unused;
             p_step<false>(Sp, e >> 3, P[e >> 3], unused);
             rs = row_sum_bf16(P[e >> 3], rs);
-            // Sparse rows: keep the sum in this chunk (an empty statement, no code); left
-            // free, the compiler sinks it past the mask branch. Measured either way at
-            // 128K: pinned is faster for the sparse kernel and slower for the dense one.
-            if constexpr (SPARSE) __asm__ volatile("" : "+v"(rs));
+            // keep the sum in this chunk (an empty statement, no code); left free, the
+            // compiler sinks it past the mask branch (slower, measured at 128K)
+            __asm__ volatile("" : "+v"(rs));
           }
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (SPARSE) l_run += rs;
+      l_run += rs;
       // PV phase (the max is taken over the raw scores; masked stages redo it below)
-      __builtin_amdgcn_s_setprio(SPARSE ? 0 : 1);
+      __builtin_amdgcn_s_setprio(0);
       bf16x8 va[3];
       va[0] = St::v_frag(vprev, 0, 0, lane);
       va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
@@ -274,13 +268,6 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         const int dt = i % NDT, st = i / NDT;
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], P[st], O[dt], 0, 0, 0);
         if (i + 2 < NPV) va[(i + 2) % 3] = St::v_frag(vprev, (i + 2) % NDT, (i + 2) / NDT, lane);
-        if constexpr (!SPARSE) {
-          if (dt == 0 && st + 1 < 4) {
-            bf16x8 unused;
-            p_step<false>(Sp, st + 1, P[st + 1], unused);
-            rs = row_sum_bf16(P[st + 1], rs);
-          }
-        }
 #pragma unroll
         for (int u = 0; u < XPM; ++u) {
           const int e = i * XPM + u;
@@ -288,14 +275,12 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (!SPARSE) l_run += rs;
       if (key0 + kStageKeys - 1 > wave_pos_min) {
         mask(Sn, key0);
         mx = -INFINITY;
 #pragma unroll
         for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
       }
-      if constexpr (!SPARSE) __builtin_amdgcn_s_setprio(0);
       finish_max(mx);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
@@ -304,32 +289,24 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     };
     if (total > 0) {
       first();
-      if constexpr (KA == 2) {
-        // stage it: K in kb[it % 3], V in vb[it % 2]. Six unconditional steps per trip
-        // keep every buffer a distinct LDS object in each step, so the compiler sees
-        // that reading K(it) never waits on the K(it + 1) load still in flight (a
-        // conditional step would merge the two); the last stages take the buffers
-        // picked at run time.
-        int it = 1;
-        for (; it + 5 < total; it += 6) {
-          step(it, kb1, kb0, vb0, vb1);
-          step(it + 1, kb2, kb1, vb1, vb0);
-          step(it + 2, kb0, kb2, vb0, vb1);
-          step(it + 3, kb1, kb0, vb1, vb0);
-          step(it + 4, kb2, kb1, vb0, vb1);
-          step(it + 5, kb0, kb2, vb1, vb0);
-        }
-        for (; it < total; ++it) {
-          const int r3 = it % 3;
-          char* kc = r3 == 0 ? kb0 : (r3 == 1 ? kb1 : kb2);
-          char* kn = r3 == 0 ? kb2 : (r3 == 1 ? kb0 : kb1);
-          step(it, kc, kn, (it & 1) ? vb0 : vb1, (it & 1) ? vb1 : vb0);
-        }
-      } else {
-        for (int it = 1; it < total; it += 2) {
-          step(it, kb1, kb0, vb0, vb1);
-          if (it + 1 < total) step(it + 1, kb0, kb1, vb1, vb0);
-        }
+      // stage it: K in kb[it % 3], V in vb[it % 2]. Six unconditional steps per trip
+      // keep every buffer a distinct LDS object in each step, so the compiler sees that
+      // reading K(it) never waits on the K(it + 1) load still in flight (a conditional
+      // step would merge the two); the last stages take the buffers picked at run time.
+      int it = 1;
+      for (; it + 5 < total; it += 6) {
+        step(it, kb1, kb0, vb0, vb1);
+        step(it + 1, kb2, kb1, vb1, vb0);
+        step(it + 2, kb0, kb2, vb0, vb1);
+        step(it + 3, kb1, kb0, vb1, vb0);
+        step(it + 4, kb2, kb1, vb0, vb1);
+        step(it + 5, kb0, kb2, vb1, vb0);
+      }
+      for (; it < total; ++it) {
+        const int r3 = it % 3;
+        char* kc = r3 == 0 ? kb0 : (r3 == 1 ? kb1 : kb2);
+        char* kn = r3 == 0 ? kb2 : (r3 == 1 ? kb0 : kb1);
+        step(it, kc, kn, (it & 1) ? vb0 : vb1, (it & 1) ? vb1 : vb0);
       }
       bf16x8 P[4], unused;
       float rs = 0.f;
@@ -382,12 +359,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   }
 }
 
-// Static schedule: one workgroup per (head, tile), ranked by the tile's diagonal block
-// (longest first) with the KV head as the fastest-varying index (see the file header).
+// Static schedule (sparse rows without a workspace): one workgroup per (head, tile),
+// ranked by the tile's diagonal block (longest first) with the KV head as the
+// fastest-varying index (see the file header).
 template <typename T, int D, int BLK, bool SPARSE>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_fwd_kernel(AttnParams p) {
-  POEM_ATTN_LDS(T, D, BLK, SPARSE)
+  POEM_ATTN_LDS(T, D, BLK)
   const int bid = blockIdx.x;
   const int gk = bid % p.hkv;
   const int rest = bid / p.hkv;
@@ -399,6 +377,54 @@ void attn_fwd_kernel(AttnParams p) {
   attn_tile<T, D, BLK, SPARSE>(p, gk * p.group + hg, seq, t, kb0, kb1, kb2, vb0, vb1);
 }
 
+// Persistent schedule for dense rows: one workgroup per resident slot walks the tiles
+// in a fixed order, one KV head after another (its K/V stays in the memory-side cache)
+// and, within a KV head, longest first with the G query heads of a tile adjacent.
+// With a queue (p.queue) each slot pulls its next tile from it; without one, round k
+// of the order goes to the slots forward on even rounds and backward on odd ones, so
+// each slot pairs long tiles with short ones. The queue adapts to slots that run
+// faster or slower than others (3.8% faster than the fixed interleave at 128K).
+__global__ void dense_queue_reset_kernel(int32_t* queue) { *queue = 0; }
+
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
+void attn_dense_persistent_kernel(AttnParams p) {
+  POEM_ATTN_LDS(T, D, BLK)
+  // the queue slot borrows kb2, which no wave reads between tiles
+  int* item_sh = reinterpret_cast<int*>(kb2);
+  const int total = p.num_rows;
+  const int per_kv = total / p.hkv;
+  const int S = gridDim.x;
+  for (int round = 0;; ++round) {
+    int bid;
+    if (p.queue != nullptr) {
+      // every wave's direct loads of the previous tile have landed (attn_tile ends
+      // with them drained); the barrier orders them before the slot is written
+      __syncthreads();
+      if (threadIdx.x == 0) *item_sh = atomicAdd(p.queue, 1);
+      __syncthreads();
+      bid = __builtin_amdgcn_readfirstlane(*item_sh);  // uniform by construction
+      __syncthreads();
+      if (bid >= total) break;
+    } else {
+      const int base = round * S;
+      if (base >= total) break;
+      bid = base + ((round & 1) ? S - 1 - (int)blockIdx.x : (int)blockIdx.x);
+      if (bid >= total) continue;
+      // every wave is done with the previous tile's buffers before they are refilled
+      __syncthreads();
+    }
+    const int gk = bid / per_kv;
+    const int rest = bid % per_kv;
+    const int hg = rest % p.group;
+    const int rank = rest / p.group;
+    int seq, t;
+    rank_to_item(p.seqs, 1, rank, seq, t);
+    if (seq < 0) continue;
+    attn_tile<T, D, BLK, false>(p, gk * p.group + hg, seq, t, kb0, kb1, kb2, vb0, vb1);
+  }
+}
+
 // Persistent schedule for sparse rows, whose lengths vary from a few blocks to
 // thousands: one workgroup per resident slot pulls CSR rows from a queue that the
 // schedule kernel ordered by retained count, longest first. Rows are independent,
@@ -406,7 +432,7 @@ void attn_fwd_kernel(AttnParams p) {
 template <typename T, int D, int BLK>
 __global__ __launch_bounds__(BLK * 2) __attribute__((amdgpu_waves_per_eu(attn_waves_per_eu<T, D>(), 2)))
 void attn_sparse_persistent_kernel(AttnParams p) {
-  POEM_ATTN_LDS(T, D, BLK, true)
+  POEM_ATTN_LDS(T, D, BLK)
   // the queue slot borrows kb2, which no wave reads between rows (bf16: this keeps the
   // workgroup's LDS at 80 KB, two workgroups per CU)
   int* item_sh = reinterpret_cast<int*>(kb2);
@@ -497,8 +523,22 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
                        dim3(BLK * 2), 0, stream, p);
     return hipGetLastError();
   }
-  hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, SPARSE>), dim3((unsigned)grid), dim3(BLK * 2), 0, stream, p);
-  return hipGetLastError();
+  if constexpr (!SPARSE) {
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+      e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_dense_persistent_kernel<T, D, BLK>, BLK * 2, 0);
+    if (e != hipSuccess) return e;
+    const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+    if (p.queue != nullptr) hipLaunchKernelGGL(dense_queue_reset_kernel, dim3(1), dim3(1), 0, stream, p.queue);
+    hipLaunchKernelGGL((attn_dense_persistent_kernel<T, D, BLK>), dim3((unsigned)(slots < grid ? slots : grid)),
+                       dim3(BLK * 2), 0, stream, p);
+    return hipGetLastError();
+  } else {
+    hipLaunchKernelGGL((attn_fwd_kernel<T, D, BLK, SPARSE>), dim3((unsigned)grid), dim3(BLK * 2), 0, stream, p);
+    return hipGetLastError();
+  }
 }
 
 template <typename T, int D, int BLK>

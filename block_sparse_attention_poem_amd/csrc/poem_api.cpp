@@ -342,9 +342,9 @@ static poem_status attention(const poem_problem* problem, const void* q, const v
   poem_status s = build_geometry(problem, g);
   if (s != POEM_OK) return s;
   if (workspace != nullptr) {
-    if (workspace_bytes < sparse_ws_bytes(problem, g))
-      return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes,
-                  sparse_ws_bytes(problem, g));
+    const size_t need = sparse ? sparse_ws_bytes(problem, g) : (size_t)POEM_DENSE_WORKSPACE_BYTES;
+    if (workspace_bytes < need)
+      return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, need);
     if (((uintptr_t)workspace & 255) != 0) return fail(POEM_ERR_WORKSPACE, "workspace is not 256-byte aligned");
   }
   if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
@@ -370,9 +370,9 @@ static poem_status attention(const poem_problem* problem, const void* q, const v
   ap.scale_log2 = g.scale * poem::kLog2e;
   ap.num_rows = (int32_t)(problem->num_heads_q * g.num_tiles);
   ap.shared = shared ? 1 : 0;
-  if (sparse && workspace != nullptr) {
+  if (workspace != nullptr) {
     ap.queue = static_cast<int32_t*>(workspace);
-    ap.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
+    if (sparse) ap.order = reinterpret_cast<int32_t*>(static_cast<char*>(workspace) + 256);
   }
   ap.seqs = g.st;
   return hip_status(poem::launch_attention(ap, problem->in_dtype, problem->head_dim, problem->block_size, sparse,
@@ -405,8 +405,9 @@ poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q
 }
 
 poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k, const void* v, void* out,
-                               int32_t out_dtype, float* lse, void* stream) {
-  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, nullptr, 0, stream, false, false);
+                               int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
+  return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, workspace, workspace_bytes, stream, false,
+                   false);
 }
 
 const char* poem_last_error(void) { return g_error.c_str(); }

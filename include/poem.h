@@ -271,13 +271,25 @@ poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q
                                       void* out, int32_t out_dtype, float* lse, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* Bytes of the optional device workspace poem_dense_prefill uses for its tile queue. */
+#define POEM_DENSE_WORKSPACE_BYTES 256
+
 /*
  * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t
- * (dense causal attention, the speedup baseline). Arguments as above.
+ * (dense causal attention, the speedup baseline). out, lse and errors as for
+ * poem_sparse_prefill.
+ *
+ *   workspace        nullable device buffer of >= POEM_DENSE_WORKSPACE_BYTES bytes,
+ *                    256-byte aligned, contents ignored on entry. With it, a persistent
+ *                    kernel pulls tiles from a queue (reset by a one-thread kernel on the
+ *                    stream), one KV head after another and longest first within each;
+ *                    without it, the resident workgroups take the tiles of that order in
+ *                    a fixed interleave. Results are identical either way. Calls that
+ *                    share a workspace must not overlap.
  */
 poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k,
                                const void* v, void* out, int32_t out_dtype, float* lse,
-                               void* stream);
+                               void* workspace, size_t workspace_bytes, void* stream);
 
 /* Message of the last failing call on this thread ("" if none); valid until the next call. */
 const char* poem_last_error(void);

@@ -1,10 +1,10 @@
 """The hot path under HIP graph capture.
 
-poem_select, poem_sparse_prefill (with its persistent schedule) and
-poem_dense_prefill are recorded once into a torch.cuda.CUDAGraph (a HIP graph on
+poem_select, poem_sparse_prefill and poem_dense_prefill (both with their
+persistent queues) are recorded once into a torch.cuda.CUDAGraph (a HIP graph on
 ROCm) and replayed. The library allocates nothing, clears nothing with memset and
-never synchronises the host, so every launch records; the row queue is reset by the
-schedule kernel inside the graph. The kernels are deterministic (the persistent
+never synchronises the host, so every launch records; the queues are reset by
+kernels inside the graph. The kernels are deterministic (the persistent
 schedule changes which workgroup runs a row, not the row's arithmetic), so each
 replay must reproduce the eager results bit for bit. Eager work and host
 synchronisations run between the replays, and the inputs are refreshed in place
@@ -20,7 +20,7 @@ from . import helpers as H
 pytestmark = pytest.mark.gpu
 
 
-def _run(gp, w, inp, q, k, v, ws, sws, bufs):
+def _run(gp, w, inp, q, k, v, ws, sws, dws, bufs):
     """The hot path into fixed buffers, on torch's current stream."""
     import ctypes
     import torch
@@ -37,7 +37,8 @@ def _run(gp, w, inp, q, k, v, ws, sws, bufs):
                                      L._ptr(bufs["block_idx"]), L._ptr(bufs["sparse"]), L.POEM_FP32,
                                      L._ptr(bufs["sparse_lse"]), ctypes.c_void_p(sws.ptr), sws.nbytes, stream))
     L._check(lib.poem_dense_prefill(ctypes.byref(cp), L._ptr(q), L._ptr(k), L._ptr(v), L._ptr(bufs["dense"]),
-                                    L.POEM_FP32, L._ptr(bufs["dense_lse"]), stream))
+                                    L.POEM_FP32, L._ptr(bufs["dense_lse"]), ctypes.c_void_p(dws.ptr), dws.nbytes,
+                                    stream))
 
 
 def _snapshot(bufs):
@@ -67,6 +68,7 @@ def test_graph_replay_matches_eager():
     q, k, v = H.device_inputs(inp)
     ws = L.SelectWorkspace(gp, w.rows_per_tile)
     sws = L.SparseWorkspace(gp)
+    dws = L.DenseWorkspace()
     T = L.num_tiles(gp)
     dev = q.device
     bufs = dict(
@@ -80,10 +82,10 @@ def test_graph_replay_matches_eager():
     print("graph case", w.seqlens_q, w.seqlens_k, w.num_heads_q, w.num_heads_kv, flush=True)
 
     # eager reference (run twice: the path is deterministic)
-    _run(gp, w, inp, q, k, v, ws, sws, bufs)
+    _run(gp, w, inp, q, k, v, ws, sws, dws, bufs)
     torch.cuda.synchronize()
     eager = _snapshot(bufs)
-    _run(gp, w, inp, q, k, v, ws, sws, bufs)
+    _run(gp, w, inp, q, k, v, ws, sws, dws, bufs)
     torch.cuda.synchronize()
     _same(eager, _snapshot(bufs), "eager repeat")
     nnz = int(eager["row_ptr"][-1])
@@ -93,7 +95,7 @@ def test_graph_replay_matches_eager():
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        _run(gp, w, inp, q, k, v, ws, sws, bufs)  # warm-up on the capture stream
+        _run(gp, w, inp, q, k, v, ws, sws, dws, bufs)  # warm-up on the capture stream
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graph = torch.cuda.CUDAGraph()
@@ -101,7 +103,7 @@ def test_graph_replay_matches_eager():
         t.zero_()
     torch.cuda.synchronize()
     with torch.cuda.graph(graph):
-        _run(gp, w, inp, q, k, v, ws, sws, bufs)
+        _run(gp, w, inp, q, k, v, ws, sws, dws, bufs)
     torch.cuda.synchronize()
 
     scratch = torch.randn(1 << 20, device=dev)
@@ -123,7 +125,7 @@ def test_graph_replay_matches_eager():
     k.copy_(k2)
     v.copy_(v2)
     torch.cuda.synchronize()
-    _run(gp, w, inp, q, k, v, ws, sws, bufs)
+    _run(gp, w, inp, q, k, v, ws, sws, dws, bufs)
     torch.cuda.synchronize()
     eager2 = _snapshot(bufs)
     assert not bool((eager2["dense"] == eager["dense"]).all()), "the refreshed inputs should change the output"

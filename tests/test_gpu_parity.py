@@ -180,6 +180,11 @@ def test_sparse_full_list_is_bitwise_dense(case):
     for od in ("fp32", "bf16"):
         d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype=od)
         bits = (lambda x: x.view(torch.int16)) if od == "bf16" else (lambda x: x.view(torch.int32))
+        # the dense kernel's fixed interleave (no workspace) against its tile queue
+        i_out, i_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype=od, workspace=None)
+        _sync()
+        assert torch.equal(bits(d_out), bits(i_out))
+        assert torch.equal(d_lse, i_lse)
         for ws in ("auto", None):  # persistent queue and one-workgroup-per-row schedules
             s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, torch.from_numpy(rp).cuda(),
                                             torch.from_numpy(bi).cuda(), out_dtype=od, workspace=ws)

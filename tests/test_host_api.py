@@ -37,6 +37,12 @@ def test_exports_every_declared_symbol(lib):
     assert "gfx950" in L.version()
 
 
+def test_binding_constants_match_header():
+    src = open(os.path.join(ROOT, "include", "poem.h")).read()
+    m = re.search(r"#define\s+POEM_DENSE_WORKSPACE_BYTES\s+(\d+)", src)
+    assert m and int(m.group(1)) == L.POEM_DENSE_WORKSPACE_BYTES
+
+
 def prob(**kw):
     d = dict(seqlens_q=[300], seqlens_k=[428], num_heads_q=4, num_heads_kv=2, head_dim=64, block_size=64,
              softmax_scale=0.0, dtype="bf16")
@@ -89,7 +95,7 @@ def test_problem_validation(lib, kw, status):
     p = prob(**kw).c()
     assert lib.poem_num_tiles(ctypes.byref(p)) == status
     assert lib.poem_last_error().decode() != ""
-    rc = lib.poem_dense_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None)
+    rc = lib.poem_dense_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None, 0, None)
     assert rc == status
 
 
@@ -171,11 +177,11 @@ def test_select_limits(lib):
 
 def test_attention_validation(lib):
     cp = prob().c()
-    assert lib.poem_dense_prefill(ctypes.byref(cp), None, FAKE, FAKE, FAKE, L.POEM_FP32, None, None) == \
+    assert lib.poem_dense_prefill(ctypes.byref(cp), None, FAKE, FAKE, FAKE, L.POEM_FP32, None, None, 0, None) == \
         L.POEM_ERR_INVALID_ARG
-    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, L.POEM_FP32, None, None) == \
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, L.POEM_FP32, None, None, 0, None) == \
         L.POEM_ERR_INVALID_ARG
-    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 5, None, None) == \
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, 5, None, None, 0, None) == \
         L.POEM_ERR_INVALID_ARG
     assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, None, FAKE, FAKE, L.POEM_FP32, None,
                                    None, 0, None) == L.POEM_ERR_INVALID_ARG
@@ -188,6 +194,12 @@ def test_attention_validation(lib):
                                    ws, need - 1, None) == L.POEM_ERR_WORKSPACE
     assert lib.poem_sparse_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None,
                                    ctypes.c_void_p(0x300004), need, None) == L.POEM_ERR_WORKSPACE
+    # the dense tile queue: POEM_DENSE_WORKSPACE_BYTES, 256-byte aligned
+    assert L.POEM_DENSE_WORKSPACE_BYTES == 256
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, ws,
+                                  L.POEM_DENSE_WORKSPACE_BYTES - 1, None) == L.POEM_ERR_WORKSPACE
+    assert lib.poem_dense_prefill(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None,
+                                  ctypes.c_void_p(0x300004), L.POEM_DENSE_WORKSPACE_BYTES, None) == L.POEM_ERR_WORKSPACE
 
 
 def test_error_is_thread_local(lib):
