@@ -383,7 +383,8 @@ void attn_fwd_kernel(AttnParams p) {
 // With a queue (p.queue) each slot pulls its next tile from it; without one, round k
 // of the order goes to the slots forward on even rounds and backward on odd ones, so
 // each slot pairs long tiles with short ones. The queue adapts to slots that run
-// faster or slower than others (3.8% faster than the fixed interleave at 128K).
+// faster or slower than others (at 128K: 2.8% faster than the fixed interleave, 3.8%
+// faster than one workgroup per tile).
 __global__ void dense_queue_reset_kernel(int32_t* queue) { *queue = 0; }
 
 template <typename T, int D, int BLK>
