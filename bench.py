@@ -321,8 +321,8 @@ def main():
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this build runs on one GPU: the path shards by KV head with no intra-op "
-                                   "communication, but only the single-GPU kernel is built; run with --gpus 1"}))
+        print(json.dumps({"error": "libpoem runs on one GPU: the path would shard by KV head with no intra-op "
+                                   "communication, but only the single-GPU kernels exist; run with --gpus 1"}))
         sys.exit(2)
 
     import torch
