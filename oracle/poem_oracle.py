@@ -620,8 +620,9 @@ def dense_prefill(p: Problem, q, k, v, which=None):
 
 
 def sparse_prefill(p: Problem, q, k, v, row_ptr, block_idx, which=None):
-    """{(h, gtile): (O, LSE)} attending only to the CSR row's blocks (ids above the
-    tile's diagonal are ignored)."""
+    """{(h, gtile): (O, LSE)} attending only to the CSR row's blocks. A retained set is
+    a subset of the tile's visible blocks 0 .. diag ([note] Section 4.1), so ids
+    outside that range take no part."""
     tl = tiles(p)
     T = len(tl)
     if which is None:
@@ -629,6 +630,6 @@ def sparse_prefill(p: Problem, q, k, v, row_ptr, block_idx, which=None):
     out = {}
     for (h, gt) in which:
         r = h * T + gt
-        ids = [int(b) for b in block_idx[row_ptr[r]:row_ptr[r + 1]] if b <= tl[gt].diag]
+        ids = [int(b) for b in block_idx[row_ptr[r]:row_ptr[r + 1]] if 0 <= b <= tl[gt].diag]
         out[(h, gt)] = tile_attention(p, q, k, v, h, tl[gt], ids)
     return out

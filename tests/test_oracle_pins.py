@@ -48,7 +48,7 @@ def pin_toy_pairs(toy):
     for got, exp in zip(I, toy["proxy_scores"]):
         assert abs(got - frac(exp)) < 1e-12
     assert abs(O.triangle_bound(m, v, [1, 2]) - frac(toy["triangle_bound"]["B,C"])) < 1e-12
-    # singleton bounds equal the exact errors after division by the retained mass
+    # one deleted block: the bound is tight, I_b / (1 - m_b) = |o - o_tilde| (POEM note, Eq. (4))
     for b in range(3):
         assert abs(O.triangle_bound(m, v, [b]) - abs(O.deletion_error(m, v, [b])[0])) < 1e-12
 
@@ -628,6 +628,145 @@ def test_gpu_toy_geometry_in_oracle():
     assert abs(np.abs(od[:, 0] - os_[:, 0]).max() - 2 / 3) < 1e-12
 
 
+# --- whole-problem prefill and the CSR row walk ------------------------------------------
+#
+# Two sequences (the second is a chunk: queries at positions 8 .. 12 of 13 keys, BFLA
+# Section 3.6), four query heads on two KV heads (head h reads KV head h // 2, BFLA
+# Section 3.3), blocks of 4 keys, d = 3. The tile geometry and the CSR are written out
+# by hand, and every output row is recomputed by pure-Python softmax over exactly the
+# keys its tile may see (the retained-block output of the POEM note, Section 4.1).
+
+# (global tile, first packed query row, rows, first position, diagonal block, first packed key row)
+HAND_TILES = [(0, 0, 4, 0, 0, 0), (1, 4, 3, 4, 1, 0), (2, 7, 4, 8, 2, 7), (3, 11, 1, 12, 3, 7)]
+# listed ids of each (query head, global tile); ids outside 0 .. diag take no part
+HAND_ROWS = {
+    (0, 0): [0], (0, 1): [1], (0, 2): [0, 2], (0, 3): [1, 3],
+    (1, 0): [], (1, 1): [0, 1], (1, 2): [-3, 1, 2, 5], (1, 3): [0, 2],
+    (2, 0): [0, 3], (2, 1): [0], (2, 2): [2], (2, 3): [3],
+    (3, 0): [0], (3, 1): [1, 2], (3, 2): [0, 1, 2], (3, 3): [0, 1, 2, 3],
+}
+
+
+def _prefill_problem():
+    rng = np.random.default_rng(61)
+    p = O.Problem((7, 5), (7, 13), 4, 2, 3, 4, 0.6)
+    q = rng.standard_normal((12, 4, 3)) * 1.5
+    k = rng.standard_normal((20, 2, 3)) * 1.5
+    v = rng.standard_normal((20, 2, 3))
+    return p, q, k, v
+
+
+def _brute_row(q, k, v, scale, qrow, h, g, k0, pos, blocks, B):
+    """Softmax attention of packed query row qrow (head h) over the keys j <= pos of its
+    sequence whose block j // B is in blocks; pure Python."""
+    d = q.shape[2]
+    s = [(scale * math.fsum(q[qrow, h, c] * k[k0 + j, g, c] for c in range(d)), j)
+         for j in range(pos + 1) if j // B in blocks]
+    if not s:
+        return [0.0] * d, -math.inf
+    mx = max(x for x, _ in s)
+    e = [(math.exp(x - mx), j) for x, j in s]
+    z = math.fsum(w for w, _ in e)
+    return [math.fsum(w * v[k0 + j, g, c] for w, j in e) / z for c in range(d)], mx + math.log(z)
+
+
+def _hand_csr(H, T):
+    rows = [HAND_ROWS[(h, gt)] for h in range(H) for gt in range(T)]  # row h * T + gtile
+    row_ptr = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int64)
+    return row_ptr, np.array([b for r in rows for b in r], np.int64)
+
+
+def pin_prefill_walk():
+    p, q, k, v = _prefill_problem()
+    T = len(HAND_TILES)
+    assert [(t.gtile, t.q_row0, t.n_rows, t.pos0, t.diag, t.k_row0) for t in O.tiles(p)] == HAND_TILES
+    row_ptr, block_idx = _hand_csr(p.num_heads_q, T)
+    sp = O.sparse_prefill(p, q, k, v, row_ptr, block_idx)
+    de = O.dense_prefill(p, q, k, v)
+    keys = [(h, gt) for h in range(p.num_heads_q) for gt in range(T)]
+    assert sorted(sp) == keys and sorted(de) == keys
+    for (gt, q0, n, pos0, diag, k0) in HAND_TILES:
+        for h in range(p.num_heads_q):
+            listed = {b for b in HAND_ROWS[(h, gt)] if 0 <= b <= diag}
+            for (O_, L_), blocks in ((sp[(h, gt)], listed), (de[(h, gt)], set(range(diag + 1)))):
+                assert O_.shape == (n, p.head_dim) and L_.shape == (n,)
+                for i in range(n):
+                    o, lse = _brute_row(q, k, v, p.scale, q0 + i, h, h // 2, k0, pos0 + i, blocks, p.block_size)
+                    assert np.abs(O_[i] - np.array(o)).max() < 1e-12, (h, gt, i)
+                    assert (L_[i] == lse == -math.inf) or abs(L_[i] - lse) < 1e-12, (h, gt, i)
+    # a subset of the (head, tile) pairs gives the same rows
+    sub = O.sparse_prefill(p, q, k, v, row_ptr, block_idx, which=[(3, 2), (1, 0)])
+    assert sorted(sub) == [(1, 0), (3, 2)]
+    assert np.array_equal(sub[(3, 2)][0], sp[(3, 2)][0])
+
+
+def test_prefill_walk():
+    pin_prefill_walk()
+
+
+def pin_csr():
+    """csr() lays the retained lists out in rows h * num_tiles + gtile, each ascending."""
+    from types import SimpleNamespace
+    p = O.Problem((7, 5), (7, 13), 2, 1, 3, 4)  # four tiles (HAND_TILES), two heads
+    kept = {(0, 0): [0], (0, 1): [0, 1], (0, 2): [2], (0, 3): [0, 3],
+            (1, 0): [0], (1, 1): [1], (1, 2): [0, 1, 2], (1, 3): [3]}
+    rp, ids = O.csr(p, {key: SimpleNamespace(retained=r) for key, r in kept.items()})
+    assert rp.tolist() == [0, 1, 3, 4, 6, 7, 8, 11, 12]
+    assert ids.tolist() == [0, 0, 1, 2, 0, 3, 0, 1, 0, 1, 2, 3]
+    assert O.csr_capacity(p) == 2 * (1 + 2 + 3 + 4)
+
+
+def test_csr():
+    pin_csr()
+
+
+def pin_practical_tile():
+    """select_tile_practical end to end: pooled masses and scores recomputed by brute
+    force with scipy's softmax, the rerank key with math.log, the kept set equal to
+    practical_retain on those values (itself pinned by subset brute force above), and
+    the per-row omitted mass of the final discard set."""
+    retain_ref = _orig_practical
+    p, q, k, v = _tiny_problem(91, nq=256, nk=640, B=32, sink=8.0)  # 8 tiles, up to 20 visible blocks
+    B = p.block_size
+    for eps, w, rho in ((0.002, 0.5, 0.95), (0.05, 1.0, 0.9), (0.2, 0.0, 1.0), (0.01, 2.0, 0.99)):
+        n_drop = 0
+        sels = O.select(p, q, k, v, [eps, 2 * eps], 1, 1, 8, mode="practical", practical=dict(w=w, rho=rho))
+        for (h, gt), s in sels.items():
+            t = s.tile
+            n_vis = t.diag + 1
+            m_rows, I_rows = [], []
+            for r in O.sampled_rows(t.n_rows, 8):
+                pos = t.pos0 + r
+                pr = softmax(p.scale * (k[:pos + 1, 0] @ q[t.q_row0 + r, h]))
+                o = pr @ v[:pos + 1, 0]
+                mb = np.array([pr[b * B:min((b + 1) * B, pos + 1)].sum() for b in range(n_vis)])
+                ub = np.array([pr[b * B:min((b + 1) * B, pos + 1)] @ v[b * B:min((b + 1) * B, pos + 1), 0]
+                               for b in range(n_vis)])
+                m_rows.append(mb)
+                I_rows.append(np.linalg.norm(ub - mb[:, None] * o[None, :], axis=1))
+            m_rows, I_rows = np.array(m_rows), np.array(I_rows)
+            mbar, Ibar = m_rows.mean(0), I_rows.mean(0)
+            assert np.allclose(s.mass, mbar, rtol=1e-10, atol=1e-15)
+            for b in range(n_vis):
+                if mbar[b] > 0 and (w == 0.0 or Ibar[b] > 0):
+                    want = math.log(mbar[b]) + (w * math.log(Ibar[b] / mbar[b]) if w != 0.0 else 0.0)
+                    assert abs(s.score[b] - want) < 1e-9 * (1 + abs(want)), (h, gt, b)
+            mand = O.mandatory_blocks(t.diag, 1, 1)
+            cand = [b for b in range(n_vis) if b not in set(mand)]
+            _, order, kept = retain_ref(mbar, Ibar, mand, cand, eps * (1 + h), w, rho)
+            assert s.retained == sorted(set(mand) | set(kept)), (h, gt)
+            assert s.order == order
+            dropped = [b for b in range(n_vis) if b not in set(s.retained)]
+            assert np.allclose(s.per_row[0], m_rows[:, dropped].sum(1), rtol=1e-10, atol=1e-15)
+            assert s.k_star == len(dropped)
+            n_drop += len(dropped)
+        assert n_drop > 0
+
+
+def test_practical_tile():
+    pin_practical_tile()
+
+
 def toy_blocks(shift=0.0):
     """Inputs of the block-level toy (shared with the GPU toy test)."""
     from block_sparse_attention_poem_amd.synth import toy_block_inputs
@@ -729,6 +868,87 @@ def _practical_rerank_ascending(mbar, Ibar, mandatory, candidates, eps, w, rho):
 _orig_practical = O.practical_retain
 
 
+def _sparse_prefill_tile_major(p, q, k, v, row_ptr, block_idx, which=None):
+    """CSR row read as gtile * H + h instead of h * num_tiles + gtile."""
+    tl = O.tiles(p)
+    if which is None:
+        which = [(h, t.gtile) for h in range(p.num_heads_q) for t in tl]
+    out = {}
+    for (h, gt) in which:
+        r = gt * p.num_heads_q + h
+        ids = [int(b) for b in block_idx[row_ptr[r]:row_ptr[r + 1]] if 0 <= b <= tl[gt].diag]
+        out[(h, gt)] = O.tile_attention(p, q, k, v, h, tl[gt], ids)
+    return out
+
+
+def _sparse_prefill_filter(lo_ok, hi_ok):
+    def f(p, q, k, v, row_ptr, block_idx, which=None):
+        tl = O.tiles(p)
+        T = len(tl)
+        if which is None:
+            which = [(h, t.gtile) for h in range(p.num_heads_q) for t in tl]
+        out = {}
+        for (h, gt) in which:
+            r = h * T + gt
+            ids = [int(b) for b in block_idx[row_ptr[r]:row_ptr[r + 1]] if lo_ok(b) and hi_ok(b, tl[gt].diag)]
+            out[(h, gt)] = O.tile_attention(p, q, k, v, h, tl[gt], ids)
+        return out
+    return f
+
+
+_sparse_prefill_drops_diagonal = _sparse_prefill_filter(lambda b: b >= 0, lambda b, d: b < d)
+_sparse_prefill_no_lower_bound = _sparse_prefill_filter(lambda b: True, lambda b, d: b <= d)
+
+
+def _tile_attention_kv_modulo(p, q, k, v, h, tile, blocks=None):
+    """KV head h % H_kv instead of h // G."""
+    g = h % p.num_heads_kv
+    Q = q[tile.q_row0:tile.q_row0 + tile.n_rows, h, :]
+    K = k[tile.k_row0:tile.k_row0 + tile.n_k, g, :]
+    V = v[tile.k_row0:tile.k_row0 + tile.n_k, g, :]
+    allowed = None
+    if blocks is not None:
+        allowed = np.zeros(tile.n_k, dtype=bool)
+        for b in blocks:
+            allowed[b * p.block_size:(b + 1) * p.block_size] = True
+    return O.attention_rows(Q, K, V, p.scale, [tile.pos0 + i for i in range(tile.n_rows)], allowed)
+
+
+def _csr_tile_major(p, selections):
+    tl = O.tiles(p)
+    rp = [0]
+    ids = []
+    for t in tl:
+        for h in range(p.num_heads_q):
+            r = selections[(h, t.gtile)].retained
+            ids.extend(r)
+            rp.append(len(ids))
+    return np.asarray(rp, np.int64), np.asarray(ids, np.int64)
+
+
+def _practical_tile_swapped(p, q, k, v, h, tile, eps, n_sink, n_local, S, w=0.5, rho=0.95):
+    """select_tile_practical with mbar and Ibar swapped in its call to practical_retain."""
+    g = h // p.group
+    K = k[tile.k_row0:tile.k_row0 + tile.n_k, g, :]
+    V = v[tile.k_row0:tile.k_row0 + tile.n_k, g, :]
+    n_vis = tile.diag + 1
+    rows = O.sampled_rows(tile.n_rows, S)
+    st = [O.row_block_stats(q[tile.q_row0 + r, h, :], K, V, p.scale, tile.pos0 + r, n_vis, p.block_size)
+          for r in rows]
+    I = np.stack([x["I"] for x in st])
+    m = np.stack([x["m"] for x in st])
+    Ibar, mbar = I.mean(axis=0), m.mean(axis=0)
+    mand = O.mandatory_blocks(tile.diag, n_sink, n_local)
+    cand = [b for b in range(n_vis) if b not in set(mand)]
+    pre, order, kept = _orig_practical(Ibar, mbar, mand, cand, float(eps), float(w), float(rho))
+    retained = sorted(set(mand) | set(kept))
+    drop = [b for b in range(n_vis) if b not in set(retained)]
+    omitted = m[:, drop].sum(axis=1) if drop else np.zeros(len(rows))
+    return O.TileSelection(h, tile, rows, I, m, np.array([x["lse"] for x in st]),
+                           np.stack([x["o"] for x in st]), O.practical_keys(mbar, Ibar, w), mbar, mand, order,
+                           np.zeros(0), omitted[None, :], len(drop), retained)
+
+
 @pytest.mark.parametrize("name,fn,pins", [
     ("practical_retain", _practical_rerank_ascending, ["practical"]),
     ("group_excess_curve", _group_curve_loosest_tau, ["group_cut", "group_selection"]),
@@ -741,6 +961,12 @@ _orig_practical = O.practical_retain
     ("discard_order", _order_small_id_first, ["threshold"]),
     ("attention_rows", _attention_off_by_one, ["attention", "toy_logits"]),
     ("row_block_stats", _stats_transposed_mass, ["row_stats", "toy_logits"]),
+    ("sparse_prefill", _sparse_prefill_tile_major, ["prefill"]),
+    ("sparse_prefill", _sparse_prefill_drops_diagonal, ["prefill"]),
+    ("sparse_prefill", _sparse_prefill_no_lower_bound, ["prefill"]),
+    ("tile_attention", _tile_attention_kv_modulo, ["prefill"]),
+    ("csr", _csr_tile_major, ["csr"]),
+    ("select_tile_practical", _practical_tile_swapped, ["practical_tile"]),
 ])
 def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
     runners = {
@@ -757,6 +983,9 @@ def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
         "group_cut": pin_group_cut,
         "practical": pin_practical_selection,
         "group_selection": pin_group_selection,
+        "prefill": pin_prefill_walk,
+        "csr": pin_csr,
+        "practical_tile": pin_practical_tile,
     }
     monkeypatch.setattr(O, name, fn)
     for pin in pins:
