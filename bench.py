@@ -102,10 +102,14 @@ def unique_bytes(gp, rp, bi, in_bytes, out_bytes):
     return int(kv + q_o)
 
 
-def cpu_baseline(w, inp, gp, rp, bi, seconds):
+def cpu_baseline(w, inp, gp, rp, bi, seconds, gpu_scores=None):
     """The fp64 oracle, as it stands, on a bounded sample of the same workload: per
     sampled (head, tile), the selector and the sparse attention over its oracle-kept
-    blocks. Reported in the step's unit (retained-block TFLOP/s)."""
+    blocks. Reported in the step's unit (retained-block TFLOP/s).
+
+    After the timed loop (outside it), the oracle's selections of the sampled pairs are
+    compared with the GPU's CSR and scores (gpu_scores: {(h, gtile): scores}) under the
+    parity gates: the returned dict's "parity_sample" holds the agreement rate."""
     from block_sparse_attention_poem_amd import synth
     from oracle import poem_oracle as O
     try:
@@ -125,6 +129,7 @@ def cpu_baseline(w, inp, gp, rp, bi, seconds):
     B = w.block_size
     flops = 0.0
     done = 0
+    sels = []
     t0 = time.perf_counter()
     for h, gt in order:
         h, gt = int(h), int(gt)
@@ -140,13 +145,96 @@ def cpu_baseline(w, inp, gp, rp, bi, seconds):
         pairs = full * t.n_rows * B + (t.n_rows * (t.n_rows + 1) // 2 if t.diag in kept else 0)
         flops += 4.0 * w.head_dim * pairs
         done += 1
+        sels.append(sel)
         if time.perf_counter() - t0 > seconds:
             break
     el = time.perf_counter() - t0
-    return {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "sample": f"{done} (head, tile) pairs drawn uniformly from the workload; per pair the fp64 selector "
-                      f"(8 sampled rows) and the sparse attention over its kept blocks; {el:.1f} s",
-            "seconds": el, "host_cpus": len(os.sched_getaffinity(0))}
+    res = {"value": flops / el / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+           "sample": f"{done} (head, tile) pairs drawn uniformly from the workload; per pair the fp64 selector "
+                     f"(8 sampled rows) and the sparse attention over its kept blocks; {el:.1f} s",
+           "seconds": el, "host_cpus": len(os.sched_getaffinity(0))}
+    if gpu_scores is not None:
+        res["parity_sample"] = parity_sample(sels, inp, gp, rp, bi, gpu_scores)
+    return res
+
+
+def parity_sample(sels, inp, gp, rp, bi, gpu_scores):
+    """GPU selection against the oracle's on the pairs the CPU leg computed: candidate
+    score error (1e-3 relative gate, floored at tau / n_vis, and unfloored), mandatory
+    score error, mask agreement over candidate blocks, and mismatches outside the
+    near-threshold exemption (which must be zero)."""
+    from tests import helpers as TH
+    T = sum(-(-nq // gp.block_size) for nq in gp.seqlens_q)
+    n_c = n_m = 0
+    bad = 0
+    worst = worst_unf = worst_mand = 0.0
+    detail = {}
+    for sel in sels:
+        h, gt = sel.h, sel.tile.gtile
+        tau = float(inp.tau[h])
+        n_vis = sel.tile.diag + 1
+        se, sm, info = TH.score_errors(sel, gpu_scores[(h, gt)], tau)
+        worst, worst_mand = max(worst, se), max(worst_mand, sm)
+        worst_unf = max(worst_unf, info.get("unfloored", 0.0))
+        kept = bi[rp[h * T + gt]:rp[h * T + gt + 1]].tolist()
+        nc, nm, b = TH.mask_agreement(sel, kept, tau, tau / n_vis, detail=detail)
+        n_c, n_m, bad = n_c + nc, n_m + nm, bad + len(b)
+    return {"pairs": len(sels), "candidates": n_c, "agreement": (n_m / n_c) if n_c else 1.0,
+            "non_exempt_mismatches": bad, "mismatches_score_only_exemption": detail.get("score_only_bad", 0),
+            "worst_candidate_score_rel_err": worst, "worst_candidate_score_rel_err_unfloored": worst_unf,
+            "worst_mandatory_score_rel_err": worst_mand, "score_gate": 1e-3}
+
+
+def mfma_probe():
+    """On-card bf16 MFMA rate (libpoem_probe.so): MFMA-only waves, two per SIMD."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "block_sparse_attention_poem_amd", "libpoem_probe.so")
+    if not os.path.exists(path):
+        return None
+    lib = ctypes.CDLL(path)
+    lib.poem_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
+    lib.poem_probe_mfma_bf16.restype = ctypes.c_double
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks, iters = 2 * cus, 40000
+    sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    st = torch.cuda.current_stream()
+    best = 0.0
+    for i in range(4):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(st)
+        flop = lib.poem_probe_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), blocks, iters,
+                                        ctypes.c_void_p(st.cuda_stream))
+        e1.record(st)
+        torch.cuda.synchronize()
+        if flop < 0:
+            return None
+        if i > 0:  # the first launch warms the clock up
+            best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+    del sink
+    return {"achieved_tflops": best, "quoted_peak_tflops": PEAK_BF16_TFLOPS, "frac_of_quoted": best / PEAK_BF16_TFLOPS,
+            "implied_clock_ghz": best * 1e12 / (cus * 4096) / 1e9, "compute_units": cus,
+            "kernel": "v_mfma_f32_32x32x16_bf16 chains on registers, 2 waves per SIMD, no memory traffic"}
+
+
+def selector_streaming(gp, w, t_sel_ms, workload_id):
+    """K/V streaming of the selector's two sweeps: the unique K and V bytes each pass
+    reads, their rate over the whole selector call, and per sweep the bytes fetched
+    from beyond L2 and the L2 hit rate from the committed rocprofv3 counters (when the
+    selector sources still match the ones profiled)."""
+    import hashlib
+    in_bytes = 2 if w.dtype == "bf16" else 4
+    kv = 2 * gp.total_k * gp.num_heads_kv * gp.head_dim * in_bytes
+    out = {"unique_kv_bytes_per_pass": kv, "passes": 2,
+           "algorithmic_gbs_over_select_call": 2 * kv / (t_sel_ms * 1e-3) / 1e9}
+    path = os.path.join(ROOT, "profiles", f"selector_{WORKLOAD_TAGS.get(workload_id, '')}.json")
+    if os.path.exists(path):
+        rec = json.load(open(path))
+        src = b"".join(open(os.path.join(ROOT, "block_sparse_attention_poem_amd", "csrc", f), "rb").read()
+                       for f in ("poem_device.hpp", "poem_internal.hpp", "selector.hip"))
+        if hashlib.sha256(src).hexdigest() == rec.get("selector_source_sha256"):
+            out["counters"] = rec["sweeps"]
+    return out
 
 
 def sampled_row_index(gp, S):
@@ -299,6 +387,7 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-legs", action="store_true", help="skip the mass-only and group-shared selector legs")
+    ap.add_argument("--no-probe", action="store_true", help="skip the on-card MFMA rate probe")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-only selector leg")
     ap.add_argument("--mass-eps", type=float, default=0.002,
                     help="omitted-mass budget of the mass-only and practical legs")
@@ -455,6 +544,15 @@ def main():
         "keep_fraction_pairs": p_ret / p_dense,
         "roofline": roofline,
     }
+    res["selector_streaming"] = selector_streaming(gp, w, sel_ms, args.workload)
+    res["memory"] = {"select_workspace_bytes": ws.nbytes, "sparse_workspace_bytes": sws.nbytes,
+                     "dense_workspace_bytes": dws.nbytes,
+                     "csr_bytes": 4 * (len(rp) + kept_blocks), "csr_capacity_bytes": 4 * (len(rp) + cap),
+                     "context": "the POEM summary page reports about 2 MiB of peak memory overhead at 128K "
+                                "(whole system, hardware not stated)"}
+    if not args.no_probe:
+        log("[bench] MFMA rate probe")
+        res["mfma_probe"] = mfma_probe()
     if not args.no_legs and inp.is_bf16:
         log("[bench] mass-only and group-shared selector legs")
         res_m, res_g, res_p = selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp, args.steps)
@@ -464,7 +562,28 @@ def main():
         res["practical"] = res_p
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
-        res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds)
+        # the GPU's scores for the parity sample (one more selection, outside the timed steps)
+        rd = L.select(gp, q, k, v, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True,
+                      workspace=ws)
+        assert torch.equal(rd["row_ptr"], row_ptr)
+        scores_dev = rd["tile_scores"]
+        del rd
+        torch.cuda.synchronize()
+
+        class _Scores(dict):
+            def __missing__(self, key):
+                v_ = scores_dev[key[0], key[1]].cpu().numpy()
+                self[key] = v_
+                return v_
+        res["cpu_baseline"] = cpu_baseline(w, inp, gp, rp, bi, args.cpu_seconds, gpu_scores=_Scores())
+        if "parity_sample" in res["cpu_baseline"]:
+            res["parity_sample"] = res["cpu_baseline"].pop("parity_sample")
+        del scores_dev
+    # release device memory and let queued work finish before printing, so the process
+    # ends right after its one line
+    del q, k, v, out, lse, row_ptr, block_idx, ws, sws, dws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     print(json.dumps(res), flush=True)
 
 

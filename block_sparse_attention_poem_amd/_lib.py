@@ -13,7 +13,8 @@ from dataclasses import dataclass
 from typing import Optional, Sequence
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libpoem.so")
+# POEM_LIB selects another build of the same library (the host AddressSanitizer build)
+LIB_PATH = os.environ.get("POEM_LIB") or os.path.join(_HERE, "libpoem.so")
 
 POEM_OK, POEM_ERR_INVALID_ARG, POEM_ERR_UNSUPPORTED, POEM_ERR_WORKSPACE, POEM_ERR_CAPACITY, POEM_ERR_HIP = \
     0, -1, -2, -3, -4, -5
@@ -177,6 +178,17 @@ def _ptr(t):
     return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
 
 
+def _keep_for_stream(stream, *tensors):
+    """Buffers allocated here on torch's current stream but used by a launch on another
+    stream: record that stream, so the caching allocator does not hand their memory to
+    a new allocation before that stream's work on them is done."""
+    if stream is None:
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
 def _check_qkv(problem: Problem, q, k, v):
     torch = _torch()
     want = torch.bfloat16 if problem.dtype == "bf16" else torch.float32
@@ -253,6 +265,7 @@ def select(problem: Problem, q, k, v, tau, n_sink_blocks: int = 1, n_local_block
         rb = torch.empty((problem.num_heads_q, T, rows_per_tile), dtype=torch.float32, device=dev)
         out.update(tile_scores=sc, tile_mass=ms, row_bound=rb)
     ws = workspace if workspace is not None else SelectWorkspace(problem, rows_per_tile, dev)
+    _keep_for_stream(stream, row_ptr, block_idx, sc, ms, rb, ws.buf if workspace is None else None)
     tail = (_ptr(row_ptr), _ptr(block_idx), cap, _ptr(sc), _ptr(ms), _ptr(rb), ctypes.c_void_p(ws.ptr), ws.nbytes,
             _stream_ptr(stream))
     head = (ctypes.byref(cp), _ptr(q), _ptr(k), _ptr(v), tau_arr, int(n_sink_blocks), int(n_local_blocks),
@@ -283,8 +296,10 @@ def sparse_prefill(problem: Problem, q, k, v, row_ptr, block_idx, out_dtype: str
     _check_qkv(problem, q, k, v)
     if out is None:
         out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+        _keep_for_stream(stream, out, lse)
     if isinstance(workspace, str):
         workspace = SparseWorkspace(problem, q.device)
+        _keep_for_stream(stream, workspace.buf)
     wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
     wb = workspace.nbytes if workspace is not None else 0
     _check(load().poem_sparse_prefill(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
@@ -300,8 +315,10 @@ def sparse_prefill_group(problem: Problem, q, k, v, row_ptr, block_idx, out_dtyp
     _check_qkv(problem, q, k, v)
     if out is None:
         out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+        _keep_for_stream(stream, out, lse)
     if isinstance(workspace, str):
         workspace = SparseWorkspace(problem, q.device)
+        _keep_for_stream(stream, workspace.buf)
     wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
     wb = workspace.nbytes if workspace is not None else 0
     _check(load().poem_sparse_prefill_group(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
@@ -320,8 +337,10 @@ def dense_prefill(problem: Problem, q, k, v, out_dtype: str = "bf16", want_lse: 
     _check_qkv(problem, q, k, v)
     if out is None:
         out, lse = _alloc_out(problem, out_dtype, want_lse, q.device)
+        _keep_for_stream(stream, out, lse)
     if isinstance(workspace, str):
         workspace = DenseWorkspace(q.device)
+        _keep_for_stream(stream, workspace.buf)
     wp = ctypes.c_void_p(workspace.ptr) if workspace is not None else ctypes.c_void_p(0)
     wb = workspace.nbytes if workspace is not None else 0
     _check(load().poem_dense_prefill(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(out),

@@ -48,7 +48,7 @@ def retained(rp, bi, r):
     return bi[rp[r]:rp[r + 1]].tolist()
 
 
-def mask_agreement(sel, gpu_retained, tau, floor, target=None):
+def mask_agreement(sel, gpu_retained, tau, floor, target=None, detail=None):
     """Compare one tile's GPU retained set with the oracle's selection.
 
     Returns (n_candidates, n_matching_decisions, non_exempt_mismatches). A mismatch on
@@ -56,7 +56,8 @@ def mask_agreement(sel, gpu_retained, tau, floor, target=None):
     the last discarded or first retained position of the oracle's discard order, or
     when the oracle bound B(j) is within NEAR_REL * tau of tau at b's own position j
     or the one before it (target: the curve value at the cut, tau unless given; the
-    group selector's excess curve cuts at 0)."""
+    group selector's excess curve cuts at 0). detail (a dict) receives
+    "score_only_bad": the mismatches the score rule alone leaves unexempted."""
     target = tau if target is None else target
     order = sel.order
     ks = sel.k_star
@@ -69,6 +70,7 @@ def mask_agreement(sel, gpu_retained, tau, floor, target=None):
     if ks < len(order):
         near_scores.append(sel.score[order[ks]])
     bad = []
+    score_only_bad = 0
     match = 0
     for b in order:
         if (b in keep_o) == (b in keep_g):
@@ -76,12 +78,15 @@ def mask_agreement(sel, gpu_retained, tau, floor, target=None):
             continue
         s = sel.score[b]
         ex = any(abs(s - ns) <= NEAR_REL * max(ns, floor) for ns in near_scores)
+        score_only_bad += 0 if any(abs(s - ns) <= NEAR_REL * ns for ns in near_scores) else 1
         j = pos[b]
         for jj in (j, j - 1):
             if 0 <= jj < len(sel.curve) and abs(sel.curve[jj] - target) <= NEAR_REL * tau:
                 ex = True
         if not ex:
             bad.append(b)
+    if detail is not None:
+        detail["score_only_bad"] = detail.get("score_only_bad", 0) + score_only_bad
     return len(order), match, bad
 
 
@@ -89,7 +94,9 @@ def score_errors(sel, gpu_scores, tau):
     """|gpu - oracle| / max(oracle, tau / n_vis) over a tile's visible blocks.
 
     Returns (worst over candidate blocks, worst over mandatory blocks, detail of the
-    worst candidate). Only candidate scores are ranked and summed into the bound."""
+    worst candidate). Only candidate scores are ranked and summed into the bound. The
+    detail also holds "unfloored": the worst |gpu - oracle| / oracle over candidates
+    with a positive oracle score."""
     n = sel.tile.diag + 1
     floor = tau / n
     ref = sel.score
@@ -101,6 +108,8 @@ def score_errors(sel, gpu_scores, tau):
     wm = float(rel[mand].max()) if len(mand) else 0.0
     b = int(cand[rel[cand].argmax()]) if len(cand) else -1
     info = dict(block=b, oracle=float(ref[b]), gpu=float(g[b]), mass=float(sel.mass[b]), floor=floor) if b >= 0 else {}
+    pos = cand[ref[cand] > 0] if len(cand) else cand
+    info["unfloored"] = float((np.abs(g[pos] - ref[pos]) / ref[pos]).max()) if len(pos) else 0.0
     return wc, wm, info
 
 

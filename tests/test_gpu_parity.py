@@ -269,19 +269,22 @@ def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_spars
     bounds = r["row_bound"].cpu().numpy()
     sels = O.select(op, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which, mode=mode)
     n_cand = n_match = 0
-    worst_score = 0.0
+    worst_score = worst_unfloored = worst_mand = 0.0
+    detail = {}
     for (h, gt), sel in sels.items():
         tau = float(taus[h])
         n_vis = sel.tile.diag + 1
         se, sm, info = H.score_errors(sel, scores[h, gt], tau)
         worst_score = max(worst_score, se)
+        worst_unfloored = max(worst_unfloored, info.get("unfloored", 0.0))
+        worst_mand = max(worst_mand, sm)
         assert se <= H.SCORE_RTOL, (h, gt, se, info)
         assert sm <= H.MANDATORY_SCORE_RTOL, (h, gt, sm)
         assert np.all(scores[h, gt, n_vis:] == -1.0)
         kept = H.retained(rp, bi, h * T + gt)
         assert kept == sorted(kept) and len(set(kept)) == len(kept)
         assert set(sel.mandatory) <= set(kept)
-        nc, nm, bad = H.mask_agreement(sel, kept, tau, tau / n_vis)
+        nc, nm, bad = H.mask_agreement(sel, kept, tau, tau / n_vis, detail=detail)
         n_cand += nc
         n_match += nm
         assert not bad, (h, gt, bad)
@@ -307,6 +310,8 @@ def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_spars
                                           gpu_sparse[t.q_row0 + row, h].astype(np.float64)))
                 assert ge <= b * (1 + 1e-3) + 2e-4, (h, gt, j, ge, b)
         assert np.all(bounds[h, gt, len(sel.rows):] == -1.0)
+    say("  worst candidate score error unfloored", worst_unfloored, "mandatory", worst_mand,
+        "mismatches under the score-only exemption", detail.get("score_only_bad", 0))
     return n_cand, n_match, worst_score
 
 
@@ -423,7 +428,8 @@ def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=No
     sels = O.select(op, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which,
                     mode="group")
     n_cand = n_match = 0
-    worst = 0.0
+    worst = worst_unfloored = worst_mand = 0.0
+    detail = {}
     for (h0, gt), sel in sels.items():
         t = sel.tile
         n_vis = t.diag + 1
@@ -435,12 +441,14 @@ def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=No
             assert np.array_equal(bounds[h, gt], bounds[h0, gt])
         se, sm, info = H.score_errors(sel, scores[h0, gt], tmin)
         worst = max(worst, se)
+        worst_unfloored = max(worst_unfloored, info.get("unfloored", 0.0))
+        worst_mand = max(worst_mand, sm)
         assert se <= H.SCORE_RTOL, (h0, gt, se, info)
         assert sm <= H.MANDATORY_SCORE_RTOL, (h0, gt, sm)
         assert np.all(scores[h0, gt, n_vis:] == -1.0)
         assert kept == sorted(kept) and len(set(kept)) == len(kept)
         assert set(sel.mandatory) <= set(kept)
-        nc, nm, bad = H.mask_agreement(sel, kept, tmin, tmin / n_vis, target=0.0)
+        nc, nm, bad = H.mask_agreement(sel, kept, tmin, tmin / n_vis, target=0.0, detail=detail)
         n_cand += nc
         n_match += nm
         assert not bad, (h0, gt, bad)
@@ -456,6 +464,8 @@ def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=No
                                           gpu_sparse[t.q_row0 + row, hh].astype(np.float64)))
                 assert ge <= b * (1 + 1e-3) + 2e-4, (h0, gt, j, ge, b)
         assert np.all(bounds[h0, gt, len(sel.rows):] == -1.0)
+    say("  worst candidate score error unfloored", worst_unfloored, "mandatory", worst_mand,
+        "mismatches under the score-only exemption", detail.get("score_only_bad", 0))
     return n_cand, n_match, worst
 
 
