@@ -24,7 +24,7 @@ STATUS_NAMES = {0: "POEM_OK", -1: "POEM_ERR_INVALID_ARG", -2: "POEM_ERR_UNSUPPOR
                 -4: "POEM_ERR_CAPACITY", -5: "POEM_ERR_HIP"}
 SYMBOLS = ["poem_num_tiles", "poem_csr_capacity", "poem_max_visible_blocks", "poem_select_workspace_bytes",
            "poem_sparse_workspace_bytes", "poem_select", "poem_select_mass", "poem_select_group", "poem_select_practical",
-           "poem_sparse_prefill", "poem_sparse_prefill_group", "poem_dense_prefill",
+           "poem_sparse_prefill", "poem_sparse_prefill_group", "poem_sparse_prefill_noalloc", "poem_dense_prefill",
            "poem_last_error", "poem_version"]
 
 
@@ -83,6 +83,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.poem_sparse_prefill.restype = ctypes.c_int
     lib.poem_sparse_prefill_group.argtypes = lib.poem_sparse_prefill.argtypes
     lib.poem_sparse_prefill_group.restype = ctypes.c_int
+    lib.poem_sparse_prefill_noalloc.argtypes = [P, vp, vp, vp, vp, vp, vp, i32, vp, vp]
+    lib.poem_sparse_prefill_noalloc.restype = ctypes.c_int
     lib.poem_dense_prefill.argtypes = [P, vp, vp, vp, vp, i32, vp, vp, ctypes.c_size_t, vp]
     lib.poem_dense_prefill.restype = ctypes.c_int
     lib.poem_last_error.restype = ctypes.c_char_p
@@ -325,6 +327,18 @@ def sparse_prefill_group(problem: Problem, q, k, v, row_ptr, block_idx, out_dtyp
                                             _ptr(block_idx), _ptr(out),
                                             POEM_FP32 if out_dtype == "fp32" else POEM_BF16, _ptr(lse), wp, wb,
                                             _stream_ptr(stream)))
+    return out, lse
+
+
+def sparse_prefill_noalloc(problem: Problem, q, k, v, row_ptr, block_idx, out, lse=None, out_dtype: str = "bf16",
+                           stream=None):
+    """Run poem_sparse_prefill_noalloc into caller-allocated out (and lse): the library
+    allocates nothing and uses its own per-device scratch. Returns (out, lse)."""
+    _check_qkv(problem, q, k, v)
+    _check(load().poem_sparse_prefill_noalloc(ctypes.byref(problem.c()), _ptr(q), _ptr(k), _ptr(v), _ptr(row_ptr),
+                                              _ptr(block_idx), _ptr(out),
+                                              POEM_FP32 if out_dtype == "fp32" else POEM_BF16, _ptr(lse),
+                                              _stream_ptr(stream)))
     return out, lse
 
 

@@ -16,9 +16,41 @@
 // block, longest first, with the KV head as the fastest-varying index of the
 // workgroup id, so with 8 KV heads and the round-robin dispatch over the 8 XCDs every
 // XCD streams one KV head's K/V through its own L2.
+#include <mutex>
+
+#include "poem.h"
 #include "poem_internal.hpp"
 
 namespace poem {
+
+// Scratch of poem_sparse_prefill_noalloc: the queue head (first 256 bytes) and the row
+// order of the persistent sparse schedule, in a device array the library owns. Host
+// code never passes `scratch` itself to a kernel (on the host the name stands for a
+// host-side shadow, not a device address): it uses the per-device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kNoAllocScratchBytes = 256 + sizeof(int32_t) * (size_t)POEM_NOALLOC_MAX_ROWS;
+static __device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
+  constexpr int kMaxDevices = 64;
+  static std::mutex mu;
+  static void* per_device[kMaxDevices] = {};
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(mu);
+  if (per_device[dev] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // this device's copy (the device is current)
+    if (e != hipSuccess) return e;
+    if (p == nullptr || ((uintptr_t)p & 255) != 0) return hipErrorInvalidValue;
+    per_device[dev] = p;
+  }
+  *ptr = per_device[dev];
+  *bytes = kNoAllocScratchBytes;
+  return hipSuccess;
+}
 
 // Two waves per SIMD (two workgroups per CU) when the LDS stages allow it: the MFMA
 // work of one wave overlaps the softmax of the other.

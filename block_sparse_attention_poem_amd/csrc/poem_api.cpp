@@ -404,6 +404,32 @@ poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q
                    true, true);
 }
 
+poem_status poem_sparse_prefill_noalloc(const poem_problem* problem, const void* q, const void* k, const void* v,
+                                        const int32_t* row_ptr, const int32_t* block_idx, void* out,
+                                        int32_t out_dtype, float* lse, void* stream) {
+  Geometry g;
+  poem_status s = build_geometry(problem, g);
+  if (s != POEM_OK) return s;
+  const int64_t rows = (int64_t)problem->num_heads_q * g.num_tiles;
+  if (rows > POEM_NOALLOC_MAX_ROWS)
+    return fail(POEM_ERR_UNSUPPORTED, "num_heads_q * num_tiles = %lld exceeds POEM_NOALLOC_MAX_ROWS (%d)",
+                (long long)rows, POEM_NOALLOC_MAX_ROWS);
+  if (q == nullptr || k == nullptr || v == nullptr) return fail(POEM_ERR_INVALID_ARG, "q, k or v is NULL");
+  if (out == nullptr) return fail(POEM_ERR_INVALID_ARG, "out is NULL");
+  if (row_ptr == nullptr || block_idx == nullptr) return fail(POEM_ERR_INVALID_ARG, "row_ptr or block_idx is NULL");
+  if (out_dtype != POEM_BF16 && out_dtype != POEM_FP32)
+    return fail(POEM_ERR_INVALID_ARG, "out_dtype %d is not a poem_dtype", out_dtype);
+  void* scratch = nullptr;
+  size_t scratch_bytes = 0;
+  s = hip_status(poem::noalloc_scratch(&scratch, &scratch_bytes), "poem_sparse_prefill_noalloc scratch lookup");
+  if (s != POEM_OK) return s;
+  if (sparse_ws_bytes(problem, g) > scratch_bytes)  // implied by the row limit above
+    return fail(POEM_ERR_UNSUPPORTED, "schedule needs %zu bytes, the scratch holds %zu", sparse_ws_bytes(problem, g),
+                scratch_bytes);
+  return attention(problem, q, k, v, row_ptr, block_idx, out, out_dtype, lse, scratch, scratch_bytes, stream, true,
+                   false);
+}
+
 poem_status poem_dense_prefill(const poem_problem* problem, const void* q, const void* k, const void* v, void* out,
                                int32_t out_dtype, float* lse, void* workspace, size_t workspace_bytes, void* stream) {
   return attention(problem, q, k, v, nullptr, nullptr, out, out_dtype, lse, workspace, workspace_bytes, stream, false,

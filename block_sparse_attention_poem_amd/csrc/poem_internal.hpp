@@ -30,6 +30,10 @@ struct AttnParams {
   SeqTable seqs;
 };
 
+// The device scratch of poem_sparse_prefill_noalloc on the current device (looked up
+// once per device): 256 bytes of queue head, then POEM_NOALLOC_MAX_ROWS int32 of row order.
+hipError_t noalloc_scratch(void** ptr, size_t* bytes);
+
 // in_dtype: 0 bf16, 1 fp32.
 hipError_t launch_attention(const AttnParams& p, int in_dtype, int head_dim, int block, bool sparse,
                             hipStream_t stream);

@@ -271,6 +271,29 @@ poem_status poem_sparse_prefill_group(const poem_problem* problem, const void* q
                                       void* out, int32_t out_dtype, float* lse, void* workspace,
                                       size_t workspace_bytes, void* stream);
 
+/* Most CSR rows (num_heads_q * num_tiles) poem_sparse_prefill_noalloc schedules. */
+#define POEM_NOALLOC_MAX_ROWS 1048576
+
+/*
+ * poem_sparse_prefill_noalloc: poem_sparse_prefill with its persistent, count-ordered
+ * schedule, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid allocation). It takes no
+ * workspace: the queue head and the row order live in a library-owned device array
+ * of 256 + 4 * POEM_NOALLOC_MAX_ROWS bytes (about 4 MiB), one per GPU, held from the
+ * first call on that GPU until the process ends. The call allocates nothing; its
+ * first call on a device looks up that device's copy of the array.
+ *
+ * Arguments, results and errors as for poem_sparse_prefill (the results are identical),
+ * except: num_heads_q * num_tiles above POEM_NOALLOC_MAX_ROWS is POEM_ERR_UNSUPPORTED,
+ * and the stream must belong to the current device. Every call on one GPU shares that
+ * GPU's array and it keeps the last call's contents (the schedule kernel resets the
+ * queue head on the stream before use), so calls that overlap on one GPU, on any
+ * streams, race: the caller must order them.
+ */
+poem_status poem_sparse_prefill_noalloc(const poem_problem* problem, const void* q, const void* k,
+                                        const void* v, const int32_t* row_ptr, const int32_t* block_idx,
+                                        void* out, int32_t out_dtype, float* lse, void* stream);
+
 /* Bytes of the optional device workspace poem_dense_prefill uses for its tile queue. */
 #define POEM_DENSE_WORKSPACE_BYTES 256
 

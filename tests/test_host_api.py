@@ -216,3 +216,25 @@ def test_error_is_thread_local(lib):
     th.join()
     assert seen["msg"] == ""
     assert "head_dim" in lib.poem_last_error().decode()
+
+
+def test_noalloc_validation(lib):
+    """poem_sparse_prefill_noalloc rejects, before any HIP call, what poem_sparse_prefill
+    rejects and more CSR rows than its scratch holds."""
+    src = open(os.path.join(ROOT, "include", "poem.h")).read()
+    max_rows = int(re.search(r"#define\s+POEM_NOALLOC_MAX_ROWS\s+(\d+)", src).group(1))
+    f = lib.poem_sparse_prefill_noalloc
+    cp = prob().c()
+    assert f(ctypes.byref(cp), None, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None) == L.POEM_ERR_INVALID_ARG
+    assert f(ctypes.byref(cp), FAKE, FAKE, FAKE, None, FAKE, FAKE, L.POEM_FP32, None, None) == L.POEM_ERR_INVALID_ARG
+    assert f(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, FAKE, None, L.POEM_FP32, None, None) == L.POEM_ERR_INVALID_ARG
+    assert f(ctypes.byref(cp), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 9, None, None) == L.POEM_ERR_INVALID_ARG
+    bad = prob(head_dim=96).c()
+    assert f(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None) == L.POEM_ERR_UNSUPPORTED
+    # 128 heads x 64 sequences x 129 tiles of 64 rows = 1056768 rows > POEM_NOALLOC_MAX_ROWS
+    n = 64 * 129
+    big = prob(seqlens_q=[n] * 64, seqlens_k=[n] * 64, num_heads_q=128, num_heads_kv=8)
+    assert L.num_tiles(big) * 128 > max_rows
+    assert f(ctypes.byref(big.c()), FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, L.POEM_FP32, None, None) == \
+        L.POEM_ERR_UNSUPPORTED
+    assert "POEM_NOALLOC_MAX_ROWS" in lib.poem_last_error().decode()
