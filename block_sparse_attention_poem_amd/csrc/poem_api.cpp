@@ -134,7 +134,7 @@ SelLayout sel_layout(const poem_problem* p, const Geometry& g, int cols) {
   SelLayout L;
   size_t off = 0;
   L.row_stats = off;
-  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (p->head_dim + 4));
+  off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (2 * p->head_dim + 4));
   L.blk_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.vis_per_head * cols * 2);
   L.counts = off;

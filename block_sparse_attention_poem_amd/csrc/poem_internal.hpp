@@ -65,7 +65,7 @@ struct SelectParams {
   float scale_log2;
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions
-  float* row_stats;          // [hkv][total_tiles][cols_rec][D + 4]: M2, l, pad, pad, normalised o
+  float* row_stats;          // [hkv][total_tiles][cols_rec][2 D + 4]: M2, l, L_rest / l, pad, o, R / l
   float* blk_stats;          // per (KV head, gtile, visible block): I[cols_rec] then m[cols_rec]
   int32_t* counts;           // [hq * total_tiles]
   int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets

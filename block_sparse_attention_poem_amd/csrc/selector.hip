@@ -8,30 +8,36 @@
 //
 // Pass 1 (sel_sweep_kernel<..., false>): per column, the dense softmax statistics
 //   over all visible keys (c = scale * log2 e): the final running max M2 of c s_j,
-//   l = sum_j 2^(c s_j - M2) and o = sum_j 2^(c s_j - M2) v_j / l.
+//   l = sum_j 2^(c s_j - M2) and o = sum_j 2^(c s_j - M2) v_j / l. bf16 inputs: block 0's
+//   sums are kept apart while they are formed, and the record also holds R / l and
+//   L_rest / l, with R = sum_j w_j v_j and L_rest = sum_j w_j over the keys after block 0.
 // Pass 2 (sel_sweep_kernel<..., true>): per column and visible block b, with the
 //   same weights w_j = 2^(c s_j - M2): L_b = sum_{j in b} w_j, U_b = sum_{j in b} w_j v_j,
 //   then m_b = L_b / l and I_b = ||U_b - L_b o|| / l (= ||u_b - m_b o||; a cross-lane
-//   sum of squares). Normalising only at the end keeps the weight of the row's
-//   maximum key exactly 1, so the block that dominates o (typically the sink) sees
-//   the same rounding in U_b as in o and u_b - m_b o does not lose its digits.
+//   sum of squares). For block 0 the vector is formed as (U_0 L_rest - L_0 R) / l, the
+//   same quantity since l = L_0 + L_rest and l o = U_0 + R: with a sink in block 0
+//   holding nearly all of a row's mass (1 - m_0 of a few 1e-4 at 128K tokens), U_0 and
+//   L_0 o agree to 1 - m_0 and their difference would lose that factor of fp32's
+//   precision; L_0 R and U_0 L_rest differ by L_0 L_rest (v_0 - v_rest), which does not.
 // Both passes stream the visible K/V blocks through the same LDS stages as the
 // attention kernel; a workgroup of eight waves (bf16) holds several tiles of one KV
 // head (one CU each: two waves per SIMD), so each fetch is shared by up to 256 columns
 // and the direct loads per MFMA are half those of four-wave workgroups (measured: the
 // selector's two passes run 6% faster at 128K).
 //
-// Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o and l: the row's
-// maximum key weighs exactly 1, the rounding of the other weights averages out over
-// every visible key, and o is the exact mean under the rounded weights. Pass 2 needs more: with bf16 weights (2^-9 relative rounding), a block
-// whose mass sits on a few keys would carry up to 2^-9 relative error in I_b. It runs
-// P V on fp16 instead (2^-11): v16_kernel first writes V as fp16, each (key block,
-// KV head) scaled by a power of two s_b that puts its largest |v| in [2^14, 2^15)
-// (exact for bf16 values, whose 8-bit significands fit fp16's 11, down to s_b |v| =
-// 2^-14); the weights are formed as 2^14 w_j, at most 2^14, so fp16 keeps 11 bits of
-// them down to w_j = 2^-28. U_b - L_b o is formed with L_b the sum of the same fp16
-// weights, so I_b sees each weight's rounding once, as a perturbation of the weight;
-// m_b = L_b / l comes from that sum too (at most 2^-12 relative per weight).
+// Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o, R, l and L_rest: the
+// row's maximum key weighs exactly 1, the rounding of the other weights averages out
+// over every visible key, and o is the exact mean under the rounded weights. Pass 2
+// needs more: with bf16 weights (2^-9 relative rounding), a block whose mass sits on a
+// few keys would carry up to 2^-9 relative error in I_b. It runs P V on fp16 instead
+// (2^-11): v16_kernel first writes V as fp16, each (key block, KV head) scaled by a
+// power of two s_b that puts its largest |v| in [2^14, 2^15) (exact for bf16 values,
+// whose 8-bit significands fit fp16's 11, down to s_b |v| = 2^-14); the weights are
+// formed as 2^14 w_j, at most 2^14, so fp16 keeps 11 bits of them down to w_j = 2^-28.
+// U_b - L_b o is formed with L_b the sum of the same fp16 weights, so I_b sees each
+// weight's rounding once, as a perturbation of the weight; m_b = L_b / l comes from that
+// sum too (at most 2^-12 relative per weight). Only a block other than block 0 that
+// holds nearly all of a row's mass would lose digits to the cancellation above.
 //
 // Threshold (sel_threshold_kernel): per (query head, tile), the tile score is the
 // mean of I over the sampled rows; candidates (visible, not mandatory) are sorted
@@ -47,6 +53,11 @@ namespace poem {
 // waves per SIMD leave, so fp32 keeps four waves (one per SIMD).
 template <typename T> constexpr int sel_threads() { return sizeof(T) == 2 ? 512 : 256; }
 template <bool B> struct BoolTag { static constexpr bool value = B; };
+constexpr int kMaxSeqBlocks = 4096;  // key blocks a tile may see (POEM_MAX_VISIBLE_BLOCKS)
+// Per-column record of pass 1: M2, l, L_rest / l, pad, o[D], R / l [D], where R and
+// L_rest sum w_j v_j and w_j over the keys after block 0 (bf16 inputs; pass 2 forms
+// block 0's I from them, see the file header).
+template <int D> constexpr int kRecordFloats = 2 * D + 4;
 // fp16 P V of pass 2: weights carry 2^14 (log2 and inverse)
 constexpr float kP16Log2 = 14.f;
 constexpr float kP16Inv = 1.f / 16384.f;
@@ -66,6 +77,8 @@ void sel_sweep_kernel(SelectParams p) {
   constexpr bool PIPE = St::ASYNC && !MASS && !PASS2;
   // bf16 pass 2 of the output-relative selectors: P V on fp16 (see the file header)
   constexpr bool F16PV = St::ASYNC && PASS2 && !MASS;
+  // bf16 pass 1 keeps block 0's sums apart from the rest (see the file header)
+  constexpr bool SPLIT0 = PIPE;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
@@ -130,8 +143,10 @@ void sel_sweep_kernel(SelectParams p) {
   using cfloat = const __attribute__((address_space(4))) float;
   cfloat* vsc = nullptr;
   if constexpr (F16PV) vsc = (cfloat*)p.vscale + (int64_t)gk * p.total_kb + kblocks_before(p.seqs, seq);
-  // per column: M2, l, two pad words, then o (16-byte aligned)
-  float* rs_col = p.row_stats + (((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + (in_range ? col : 0)) * (D + 4);
+  // per column: M2, l, L_rest / l, a pad word, then o and R / l (16-byte aligned); see
+  // kRecordFloats
+  float* rs_col = p.row_stats + (((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + (in_range ? col : 0)) *
+                                    kRecordFloats<D>;
   const float c = p.scale_log2;
 
   f32x16 O[D / 32];
@@ -139,28 +154,32 @@ void sel_sweep_kernel(SelectParams p) {
   for (int dt = 0; dt < D / 32; ++dt) O[dt] = f32x16{};
   // pass 1: running max and sum; pass 2: M2, l, dense output o, block weight sum
   float m_run = -INFINITY, l_run = 0.f;
-  float m2 = 0.f, inv_l = 0.f, mloc = 0.f;
+  float m_ref = 0.f;                 // bf16 pass 1: final exponent reference
+  float u0_ref = 0.f, l0_run = 0.f;  // bf16 pass 1: block 0's reference and weight sum
+  float m2 = 0.f, inv_l = 0.f, mloc = 0.f, lrest = 0.f;
   float lt = 0.f;  // fp16 P V: the block's sum of the fp16 weights
   f32x16 Od[D / 32];
   if constexpr (PASS2) {
     if (col_on) {
       m2 = rs_col[0];
       inv_l = 1.f / rs_col[1];
+      lrest = rs_col[2];
     }
   }
-  // the column's dense output o in the accumulator layout (pass 2)
-  auto load_o = [&](f32x16 (&o)[D / 32]) {
+  // a D-vector of the column's record (at float offset `at`) in the accumulator layout
+  auto load_vec = [&](f32x16 (&o)[D / 32], int at) {
 #pragma unroll
     for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
       for (int a = 0; a < 4; ++a) {
         f32x4 v4 = {0.f, 0.f, 0.f, 0.f};
-        if (col_on) v4 = *reinterpret_cast<const f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2);
+        if (col_on) v4 = *reinterpret_cast<const f32x4*>(rs_col + at + 32 * dt + 8 * a + 4 * g2);
 #pragma unroll
         for (int e = 0; e < 4; ++e) o[dt][4 * a + e] = v4[e];
       }
   };
-  if constexpr (PASS2 && !MASS && !PIPE) load_o(Od);
+  // pass 2 holds o, except that the bf16 pass holds R / l while it forms block 0
+  if constexpr (PASS2 && !MASS && !PIPE) load_vec(Od, F16PV ? 4 + D : 4);
   // per (KV head, tile, visible block): I of the record's columns, then m of them, so
   // a wave's per-block results are one coalesced store each per tile
   float* blk_I = nullptr;
@@ -170,6 +189,13 @@ void sel_sweep_kernel(SelectParams p) {
       blk_I = p.blk_stats + ((int64_t)gk * p.seqs.vis_per_head + vis_offset(p.seqs, seq, t)) * bstride + col;
   }
 
+  // fp16 passes: the V scale of every key block of the sweep, staged in LDS, so the reads
+  // inside the loop wait on LDS alone (a scalar load there makes the wait drain the LDS
+  // fragment reads in flight as well); the sweep's first barrier publishes it
+  __shared__ float vsc_sh[F16PV ? kMaxSeqBlocks : 1];
+  if constexpr (F16PV) {
+    for (int i = tid; i < nblk_wg; i += sel_threads<T>()) vsc_sh[i] = vsc[i];
+  }
   wait_vmem_all();
   const int total = nblk_wg * SUBS;
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
@@ -177,10 +203,13 @@ void sel_sweep_kernel(SelectParams p) {
   // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
   // U - L o is formed at that scale, with L the sum of the same fp16 weights (which
   // also gives m_b = L / l)
+  // For block 0 of the fp16 pass, o holds R / l and U - L o is formed as
+  // U L_rest / l - L R / l: the same vector (o = (U + R) / l, l = L + L_rest), without
+  // the cancellation between U and L o when block 0 holds nearly all of the mass.
   auto finalize_block = [&](int blk, const f32x16 (&o)[D / 32]) {
     float mt, lo_coef, i_scale = inv_l;
     if constexpr (F16PV) {
-      const float sb = vsc[blk];
+      const float sb = vsc_sh[blk];
       const float ltt = half_sum(lt);
       lo_coef = ltt * sb;
       i_scale = inv_l * kP16Inv / sb;
@@ -191,13 +220,18 @@ void sel_sweep_kernel(SelectParams p) {
     }
     float ss = 0.f;
     if constexpr (!MASS) {
+      auto norm = [&](auto block0_tag) {
 #pragma unroll
-      for (int dt = 0; dt < D / 32; ++dt)
+        for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float dv = __builtin_fmaf(-lo_coef, o[dt][r], O[dt][r]);
-          ss = __builtin_fmaf(dv, dv, ss);
-        }
+          for (int r = 0; r < 16; ++r) {
+            const float u = decltype(block0_tag)::value ? O[dt][r] * lrest : O[dt][r];
+            const float dv = __builtin_fmaf(-lo_coef, o[dt][r], u);
+            ss = __builtin_fmaf(dv, dv, ss);
+          }
+      };
+      if (F16PV && blk == 0) norm(BoolTag<true>{});
+      else norm(BoolTag<false>{});
       ss = half_sum(ss);
     }
     if (col_on && g2 == 0) {
@@ -300,6 +334,7 @@ void sel_sweep_kernel(SelectParams p) {
         }
         __builtin_amdgcn_sched_barrier(0);
       }
+      const int pst = it - 1;  // the stage whose P V this step runs
       // PV phase: O += V^T P with the packs one key step ahead (one bf16 P: see the
       // file header); l adds the same bf16 weights, two per dot instruction, so o is
       // their exact weighted mean
@@ -329,6 +364,23 @@ void sel_sweep_kernel(SelectParams p) {
       }
       __builtin_amdgcn_s_setprio(0);
       l_run += rs;
+      if (pst == SUBS - 1) {
+        // block 0 is complete: its sums U_0 (in the record's o slot) and L_0 are kept
+        // apart, at the reference they were formed with, and O and l restart for the
+        // blocks after it
+        u0_ref = m_use;
+        l0_run = l_run;
+        l_run = 0.f;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) {
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 u = {O[dt][4 * a], O[dt][4 * a + 1], O[dt][4 * a + 2], O[dt][4 * a + 3]};
+            if (col_on) *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2) = u;
+          }
+          O[dt] = f32x16{};
+        }
+      }
       if constexpr (MORE) {
         if (key0 + kStageKeys - 1 > wave_pos_min) {
           mask(Sn, key0);
@@ -354,6 +406,7 @@ void sel_sweep_kernel(SelectParams p) {
     }
     // it == total: the P V of the last stage, whose V sits in vb[(total - 1) & 1]
     if (total > 0) step(BoolTag<false>{}, it, nullptr, nullptr, ((total - 1) & 1) ? vb1 : vb0, nullptr);
+    m_ref = m_use;
   } else {
   __shared__ __attribute__((aligned(16))) char buf0[St::BYTES];
   __shared__ __attribute__((aligned(16))) char buf1[St::BYTES];
@@ -512,11 +565,43 @@ void sel_sweep_kernel(SelectParams p) {
     if constexpr (PASS2) {
       // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
       if (sub == SUBS - 1 && in_range && blk <= diag) finalize_block(blk, Od);
+      if constexpr (F16PV) {
+        if (sub == SUBS - 1 && blk == 0) load_vec(Od, 4);  // o for the other blocks
+      }
     }
   });
   }
 
-  if constexpr (!PASS2) {
+  if constexpr (!PASS2 && SPLIT0) {
+    // O and l hold R and L_rest (the blocks after block 0) at reference m_ref; U_0 (in the
+    // record) and L_0 were formed at reference u0_ref <= m_ref
+    const float f0 = __builtin_amdgcn_exp2f(u0_ref - m_ref);
+    const float l_rest = half_sum(l_run);
+    const float l_all = half_sum(l0_run) * f0 + l_rest;
+    const float r_coef = 1.f / l_all;  // R -> R / l
+    const float u_coef = f0 / l_all;   // U_0 -> U_0 / l
+    wait_vmem_all();  // this lane's U_0 stores have landed
+    if (col_on) {
+      if (g2 == 0) {
+        rs_col[0] = m_ref;
+        rs_col[1] = l_all;
+        rs_col[2] = l_rest / l_all;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          float* po = rs_col + 4 + 32 * dt + 8 * a + 4 * g2;
+          const f32x4 u = *reinterpret_cast<const f32x4*>(po);
+          const f32x4 rn = {O[dt][4 * a] * r_coef, O[dt][4 * a + 1] * r_coef, O[dt][4 * a + 2] * r_coef,
+                            O[dt][4 * a + 3] * r_coef};
+          const f32x4 o = {__builtin_fmaf(u[0], u_coef, rn[0]), __builtin_fmaf(u[1], u_coef, rn[1]),
+                           __builtin_fmaf(u[2], u_coef, rn[2]), __builtin_fmaf(u[3], u_coef, rn[3])};
+          *reinterpret_cast<f32x4*>(po) = o;
+          *reinterpret_cast<f32x4*>(po + D) = rn;
+        }
+    }
+  } else if constexpr (!PASS2) {
     const float l_tot = half_sum(l_run);
     if (col_on) {
       const float inv = 1.f / l_tot;
@@ -550,7 +635,7 @@ void sel_sweep_kernel(SelectParams p) {
 
 constexpr int kThrThreads = 256;
 constexpr int kThrWaves = kThrThreads / 64;
-constexpr int kMaxVis = 4096;
+constexpr int kMaxVis = kMaxSeqBlocks;
 constexpr int kStageVis = 1024;   // STAGED: visible blocks per tile
 constexpr int kStageVals = 8192;  // STAGED: visible blocks x sampled rows
 constexpr int kXcds = 8;
@@ -1205,7 +1290,9 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
   for (int i = 1; i < kV16Threads / 64; ++i) amax = max(amax, red[i]);
   // biased exponent E of the largest |v|: |v| in [2^(E-127), 2^(E-126)), so e = E - 126
   const int E = (int)(amax >> 7);
-  const int k = E >= 255 ? 0 : min(141 - E, 127);  // s_b = 2^(15 - e) = 2^(141 - E)
+  // s_b = 2^(15 - e) = 2^(141 - E); an all-zero block keeps s_b = 1, so the rescale of
+  // pass 1's accumulator between neighbouring blocks stays within the fp32 range
+  const int k = (E >= 255 || amax == 0) ? 0 : min(141 - E, 127);
   const float sb = __builtin_bit_cast(float, (uint32_t)(k + 127) << 23);
   uint16_t* dst = p.v16;
 #pragma unroll
@@ -1243,7 +1330,7 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
   } else {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
-    if (sizeof(T) == 2 && p.total_kb > 0)
+    if (sizeof(T) == 2 && p.total_kb > 0)  // the fp16 copy of V that pass 2 reads (bf16 inputs)
       hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
                          p);
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid), dim3(kSelThreads), 0, s, p);

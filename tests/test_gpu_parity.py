@@ -332,10 +332,11 @@ def test_selector_matches_oracle(case, sink, n_local):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
-def _scale_value_blocks(inp, w, lo, hi, seed):
+def _scale_value_blocks(inp, w, lo, hi, seed, p_zero=0.0):
     """V with each (key block, KV head) multiplied by 2^k, k uniform on lo..hi: exact in
     bf16, and it spans far more than fp16's range, so the fp16 copy of V that the
-    selector's second pass reads must take a scale per block."""
+    selector's passes read must take a scale per block. With p_zero, that share of the
+    blocks (never block 0) is all zeros instead."""
     import dataclasses
     rng = np.random.default_rng(seed)
     v = synth.bf16_bits_to_f32(inp.v) if inp.is_bf16 else inp.v.astype(np.float32)
@@ -345,7 +346,10 @@ def _scale_value_blocks(inp, w, lo, hi, seed):
     for nk in w.seqlens_k:
         for b0 in range(0, nk, B):
             for g in range(w.num_heads_kv):
-                out[k0 + b0:k0 + min(b0 + B, nk), g] *= np.float32(2.0 ** int(rng.integers(lo, hi + 1)))
+                f = np.float32(2.0 ** int(rng.integers(lo, hi + 1)))
+                if b0 > 0 and rng.uniform() < p_zero:
+                    f = np.float32(0.0)
+                out[k0 + b0:k0 + min(b0 + B, nk), g] *= f
         k0 += nk
     out_v = synth.round_to_bf16_bits(out) if inp.is_bf16 else out
     if inp.is_bf16:
@@ -354,21 +358,23 @@ def _scale_value_blocks(inp, w, lo, hi, seed):
 
 
 SCALES = [
-    # case, block scale exponents lo..hi
-    ((300, 428, 8, 2, 128, 128, "bf16", 1), 20, 20),
-    ((300, 428, 8, 2, 128, 128, "bf16", 1), -24, -24),
-    ((300, 428, 8, 2, 128, 128, "bf16", 1), -20, 20),
-    ((256, 4096, 8, 2, 128, 128, "bf16", 1), -20, 20),
-    ((257, 641, 10, 2, 128, 64, "bf16", 1), -12, 12),
+    # case, block scale exponents lo..hi, share of all-zero blocks
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 20, 20, 0.0),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), -24, -24, 0.0),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), -20, 20, 0.0),
+    ((256, 4096, 8, 2, 128, 128, "bf16", 1), -20, 20, 0.0),
+    ((257, 641, 10, 2, 128, 64, "bf16", 1), -12, 12, 0.0),
+    ((256, 4096, 8, 2, 128, 128, "bf16", 1), -16, 16, 0.3),
 ]
 
 
-@pytest.mark.parametrize("case,lo,hi", SCALES, ids=lambda x: str(x))
-def test_selector_value_scales(case, lo, hi):
-    """Scores and masks when V's blocks range from 2^-24 to 2^20 in scale (the second
-    pass's fp16 V carries one power-of-two scale per key block and KV head)."""
+@pytest.mark.parametrize("case,lo,hi,p_zero", SCALES, ids=lambda x: str(x))
+def test_selector_value_scales(case, lo, hi, p_zero):
+    """Scores and masks when V's blocks range from 2^-24 to 2^20 in scale, or are all
+    zero (both passes' fp16 V carries one power-of-two scale per key block and KV head,
+    and pass 1 moves its accumulator between the blocks' scales)."""
     w = _small(case, seed=11)
-    inp = _scale_value_blocks(synth.make(w), w, lo, hi, seed=3)
+    inp = _scale_value_blocks(synth.make(w), w, lo, hi, seed=3, p_zero=p_zero)
     gp, op = H.problems(w)
     qd, kd, vd = H.device_inputs(inp)
     say("selector with V block scales 2^", lo, "..", hi)
