@@ -669,6 +669,11 @@ def test_workload_full_size_sampled(wid):
     q, k, v = H.f64(inp)
     heads = sorted({0, w.num_heads_q - 1, w.num_heads_q // 2 + 1})
     which = H.stratified_tiles(op, heads, per_head=3, seed=wid)
+    if len(w.seqlens_q) > 1:  # chunked: every sequence's first and last tile, two heads
+        tl = O.tiles(op)
+        ends = sorted({i for s_ in range(len(w.seqlens_q)) for i in
+                       (min(t.gtile for t in tl if t.seq == s_), max(t.gtile for t in tl if t.seq == s_))})
+        which = sorted(set(which) | {(h, gt) for h in (0, w.num_heads_q - 1) for gt in ends})
     do, so = d_out.cpu().numpy(), s_out.cpu().numpy()
     del d_out, s_out
     torch.cuda.empty_cache()
@@ -676,7 +681,7 @@ def test_workload_full_size_sampled(wid):
     say("  sampled candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
     dl, sl = d_lse.cpu().numpy(), s_lse.cpu().numpy()
     T = L.num_tiles(gp)
-    for (h, gt) in which[:8]:
+    for (h, gt) in which:
         t = O.tiles(op)[gt]
         Od, ld = O.tile_attention(op, q, k, v, h, t)
         ids = H.retained(rp, bi, h * T + gt)
@@ -767,3 +772,87 @@ def test_practical_full_size_sampled():
     which = H.stratified_tiles(op, [0, w.num_heads_q - 1], per_head=3, seed=55)
     nc, nm = check_practical(w, eps_h, 0.5, 0.95, gp, op, r, which, q, k, v)
     say("  sampled candidates", nc, "agreement", nm / max(nc, 1))
+
+
+def test_workload3_every_tile_of_four_heads():
+    """The 128K layer in the benchmark's configuration. The selector on every tile of
+    query heads 0..3 (the KV head 0 group; 4 x 1,024 tiles): scores within 1e-3, masks
+    with exemptions, per-row bounds within tau, and at every sampled row the error of
+    the sparse output on the GPU's mask (fp64, and the GPU's own dense and sparse
+    outputs) within its bound. Then the dense and sparse outputs and LSE on every row
+    of 32 tiles of those heads, the three longest tiles of each head among them. The
+    oracle runs in spawned worker processes on the group's sub-problem."""
+    import torch
+    from . import oracle_pool as P
+    w = synth.WORKLOADS[3]
+    say("workload 3 every tile of four heads: generate")
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("workload 3 every tile of four heads: select + dense + sparse")
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    T = L.num_tiles(gp)
+    G = op.group
+    rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+    tl = O.tiles(op)
+    sub = O.Problem(tuple(w.seqlens_q), tuple(w.seqlens_k), G, 1, w.head_dim, w.block_size)
+    q_sub = synth.to_f64(inp.q[:, 0:G])
+    k_sub, v_sub = synth.to_f64(inp.k[:, 0:1]), synth.to_f64(inp.v[:, 0:1])
+    jobs = [(h, gt, float(inp.tau[h]), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
+             H.retained(rp, bi, h * T + gt)) for h in range(G) for gt in range(T)]
+    rng = np.random.default_rng(31)
+    out_tiles = []
+    for h in range(G):
+        picks = {0, T - 3, T - 2, T - 1} | set((1 + rng.choice(T - 4, size=4, replace=False)).tolist())
+        out_tiles += [(h, int(gt)) for gt in sorted(picks)]
+    say("  oracle on", len(jobs), "tiles and", len(out_tiles), "output tiles")
+    with P.GroupPool(sub, q_sub, k_sub, v_sub) as pool:
+        results = pool.select(jobs)
+        attn = pool.attention([(h, gt, H.retained(rp, bi, h * T + gt)) for (h, gt) in out_tiles])
+    scores = r["tile_scores"][:G].cpu().numpy()
+    bounds = r["row_bound"][:G].cpu().numpy()
+    # the sampled rows of every job, from the GPU's dense and sparse outputs
+    rows = torch.tensor([tl[j[1]].q_row0 + r_ for j, (sel, _, _) in zip(jobs, results) for r_ in sel.rows],
+                        device=d_out.device)
+    heads = torch.tensor([j[0] for j, (sel, _, _) in zip(jobs, results) for _ in sel.rows], device=d_out.device)
+    g_err = torch.linalg.vector_norm(d_out[rows, heads].double() - s_out[rows, heads].double(), dim=-1).cpu().numpy()
+    n_cand = n_match = 0
+    worst = worst_mand = worst_unf = 0.0
+    detail = {}
+    i = 0
+    for (h, gt, tau, _, _, _, kept), (sel, err, delta) in zip(jobs, results):
+        n_vis = tl[gt].diag + 1
+        se, sm, info = H.score_errors(sel, scores[h, gt], tau)
+        worst, worst_mand = max(worst, se), max(worst_mand, sm)
+        worst_unf = max(worst_unf, info.get("unfloored", 0.0))
+        assert se <= H.SCORE_RTOL, (h, gt, se, info)
+        assert sm <= H.MANDATORY_SCORE_RTOL, (h, gt, sm)
+        assert kept == sorted(kept) and set(sel.mandatory) <= set(kept)
+        nc, nm, bad = H.mask_agreement(sel, kept, tau, tau / n_vis, detail=detail)
+        n_cand, n_match = n_cand + nc, n_match + nm
+        assert not bad, (h, gt, bad)
+        for j in range(len(sel.rows)):
+            b = float(bounds[h, gt, j])
+            assert b <= tau * (1 + 1e-6), (h, gt, j, b)
+            assert err[j] <= b * (1 + 1e-3) + 1e-6, (h, gt, j, err[j], b)
+            assert g_err[i] <= b * (1 + 1e-3) + 2e-4, (h, gt, j, g_err[i], b)
+            i += 1
+        assert np.all(bounds[h, gt, len(sel.rows):] == -1.0)
+    say("  heads 0..3, tiles", len(jobs), "candidates", n_cand, "agreement", n_match / max(n_cand, 1),
+        "worst score", worst, "unfloored", worst_unf, "mandatory", worst_mand,
+        "score-only mismatches", detail.get("score_only_bad", 0))
+    worst_o = 0.0
+    for (h, gt), ((Od, ld), (Os, ls)) in zip(out_tiles, attn):
+        t = tl[gt]
+        r0, n = t.q_row0, t.n_rows
+        go_d = d_out[r0:r0 + n, h].cpu().numpy()
+        go_s = s_out[r0:r0 + n, h].cpu().numpy()
+        e = max(np.abs(go_d - Od).max(), np.abs(go_s - Os).max())
+        worst_o = max(worst_o, e)
+        assert e <= H.OUT_ATOL_BF16, (h, gt, e)
+        assert H.lse_close(d_lse[h, r0:r0 + n].cpu().numpy(), ld, H.LSE_ATOL_BF16), (h, gt)
+        assert H.lse_close(s_lse[h, r0:r0 + n].cpu().numpy(), ls, H.LSE_ATOL_BF16), (h, gt)
+    say("  outputs on", len(out_tiles), "tiles: worst max-abs error", worst_o)

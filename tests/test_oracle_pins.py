@@ -991,3 +991,29 @@ def test_planted_mistakes_are_caught(monkeypatch, toy, name, fn, pins):
     for pin in pins:
         with pytest.raises(AssertionError):
             runners[pin]()
+
+
+def test_oracle_pool_matches_direct_calls():
+    """The spawned oracle workers the large GPU parity tests use give exactly what the
+    oracle gives when called directly (selection, per-row errors on a given list, tile
+    attention)."""
+    from tests import oracle_pool as P
+    p, q, k, v = _tiny_problem(7, nq=256, nk=640, hq=4, hkv=1, B=32, sink=6.0)
+    tl = O.tiles(p)
+    jobs = [(h, t.gtile, 0.05, 1, 1, 8, list(range(0, t.diag + 1, 2)) + [t.diag]) for h in (1, 3) for t in tl]
+    with P.GroupPool(p, q, k, v, workers=2) as pool:
+        res = pool.select(jobs)
+        att = pool.attention([(1, 5, [0, 3, 5]), (2, 7, None)])
+    for (h, gt, tau, ns, nl, S, kept), (sel, err, delta) in zip(jobs, res):
+        ref = O.select_tile(p, q, k, v, h, tl[gt], tau, ns, nl, S)
+        assert sel.retained == ref.retained and sel.order == ref.order and np.array_equal(sel.score, ref.score)
+        assert np.array_equal(sel.curve, ref.curve)
+        kept = sorted(set(kept))
+        od, _ = O.tile_attention(p, q, k, v, h, tl[gt])
+        os_, _ = O.tile_attention(p, q, k, v, h, tl[gt], kept)
+        assert np.allclose(err, np.linalg.norm(od[ref.rows] - os_[ref.rows], axis=1), rtol=1e-12, atol=1e-15)
+        dropped = [b for b in range(tl[gt].diag + 1) if b not in set(kept)]
+        assert np.allclose(delta, ref.m[:, dropped].sum(axis=1), rtol=1e-12, atol=1e-15)
+    (d, s_), = [att[0]]
+    assert np.array_equal(d[0], O.tile_attention(p, q, k, v, 1, tl[5])[0])
+    assert np.array_equal(s_[0], O.tile_attention(p, q, k, v, 1, tl[5], [0, 3, 5])[0])
