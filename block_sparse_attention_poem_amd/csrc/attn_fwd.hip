@@ -6,7 +6,9 @@
 // stage are loaded into LDS once and shared by the tile's waves; the loop visits
 // only listed blocks, as BFLA's support-restricted kernel does (Section 3.4).
 // Online softmax runs in the log2 domain in fp32; QK^T and PV run on bf16 (or
-// fp32) MFMAs with fp32 accumulation. Only the diagonal block is masked.
+// fp32) MFMAs with fp32 accumulation. Only the diagonal block is masked. bf16 tiles
+// take the first stage's row max as the exponent reference for all stages and fall
+// back to the exact running max when later weights outgrow it (see attn_tile).
 //
 // Work order. Sparse rows: a persistent kernel pulls rows from a queue that a schedule
 // kernel sorts by retained count, one KV head after another (or, without a workspace,
@@ -79,8 +81,19 @@ struct AttnCfg {
   __shared__ __attribute__((aligned(16))) char vb0[AttnCfg<T, D, BLK>::VBUF];  \
   __shared__ __attribute__((aligned(16))) char vb1[AttnCfg<T, D, BLK>::VBUF];
 
+// Largest per-lane sum of one stage's weights the lazy reference accepts (see attn_tile).
+constexpr float kLazyCap = 4294967296.0f;  // 2^32
+
 // One (query head h, tile t of sequence seq): the whole workgroup, B rows. Sparse: the
 // list of h, or with p.shared that of h's GQA group's first head.
+//
+// Exponent reference (bf16): the tile is first computed with the first stage's row max
+// as the reference for every stage (no per-stage max or rescale), so later weights may
+// exceed 1. A stage whose per-lane weight sum exceeds kLazyCap, or is not finite, marks
+// the tile; a tile marked by any wave is computed again with the exact running max. The
+// rule depends only on the tile's data, so every schedule gives the same bits, and on
+// accepted tiles the weights stay below 2^32, far inside the range of the bf16 weights
+// and fp32 sums.
 template <typename T, int D, int BLK, bool SPARSE>
 __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* kb0, char* kb1,
                                           char* kb2, char* vb0, char* vb1) {
@@ -161,6 +174,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
   // sink is seen) the accumulated O and row sums are rescaled. exps(): the scores
   // become weights 2^(c s - m) and are added to the row sums.
   float m_use = 0.f;
+  bool ovf = false;  // a stage's weights outgrew the lazy reference
   auto update = [&](const f32x16 (&S)[2]) {
     float mx = -INFINITY;
 #pragma unroll
@@ -199,14 +213,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     //   QK phase : each QK^T MFMA of stage j with the next-but-one K fragment read and
     //              the exponentials (and bf16 packs) of stage j-1;
     //   mask     : only on stages that reach past a row;
-    //   PV phase : each P V MFMA of stage j-1 with the next-but-one V fragment read and
-    //              part of stage j's running max;
-    //   rescale  : only when some column's max grew.
+    //   PV phase : each P V MFMA of stage j-1 with the next-but-one V fragment read.
+    // The reference is the first stage's max (see above); a rejected tile is computed
+    // again one stage at a time with the exact running max.
     constexpr int NQK = 2 * (D / 16);  // QK^T MFMAs per stage (2 key tiles x d steps)
     constexpr int NDT = D / 32;        // d tiles of O
     constexpr int NPV = 4 * NDT;       // P V MFMAs per stage (4 key steps x d tiles)
     constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
-    constexpr int XPM = 32 / NPV;      // max candidates per P V MFMA
     // The row sums add the bf16 weights the P V MFMAs use (two per dot instruction), so
     // numerator and denominator see the same rounding.
     f32x16 Sp[2];
@@ -289,31 +302,20 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         __builtin_amdgcn_sched_barrier(0);
       }
       l_run += rs;
-      // PV phase (the max is taken over the raw scores; masked stages redo it below)
+      ovf |= !(rs <= kLazyCap);
+      // PV phase
       __builtin_amdgcn_s_setprio(0);
       bf16x8 va[3];
       va[0] = St::v_frag(vprev, 0, 0, lane);
       va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
-      float mx = -INFINITY;
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const int dt = i % NDT, st = i / NDT;
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], P[st], O[dt], 0, 0, 0);
         if (i + 2 < NPV) va[(i + 2) % 3] = St::v_frag(vprev, (i + 2) % NDT, (i + 2) / NDT, lane);
-#pragma unroll
-        for (int u = 0; u < XPM; ++u) {
-          const int e = i * XPM + u;
-          mx = fmaxf(mx, Sn[e >> 4][e & 15]);
-        }
         __builtin_amdgcn_sched_barrier(0);
       }
-      if (key0 + kStageKeys - 1 > wave_pos_min) {
-        mask(Sn, key0);
-        mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 32; ++e) mx = fmaxf(mx, Sn[e >> 4][e & 15]);
-      }
-      finish_max(mx);
+      if (key0 + kStageKeys - 1 > wave_pos_min) mask(Sn, key0);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
       __builtin_amdgcn_s_waitcnt(kWait);
@@ -350,10 +352,54 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         rs = row_sum_bf16(P[s4], rs);
       }
       l_run += rs;
+      ovf |= !(rs <= kLazyCap);
       St::pv_packed(((total - 1) & 1) ? vb1 : vb0, P, O, lane);
       // the last K prefetch (a repeat of the final stage) may still be in flight: it
       // lands before this workgroup's LDS can be reused
       wait_vmem_all();
+    }
+    // Did any wave mark the tile? Each wave writes its own word of the third K buffer,
+    // free once every wave has passed the barrier after its loads landed (the next user
+    // of those words, a persistent kernel's queue slot, writes them after a barrier).
+    lds_barrier();
+    int* flags = reinterpret_cast<int*>(kb2);
+    const int mine = __any(ovf) ? 1 : 0;
+    if (lane == 0) flags[wave] = mine;
+    lds_barrier();
+    int redo = 0;
+#pragma unroll
+    for (int w = 0; w < C::WAVES; ++w) redo |= flags[w];
+    if (__builtin_amdgcn_readfirstlane(redo) != 0) {
+      // the exact running max, one stage at a time in the first K and V buffers (rare)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x16{};
+      m_run = -INFINITY;
+      l_run = 0.f;
+      m_use = 0.f;
+      for (int it = 0; it < total; ++it) {
+        const int key0 = stage_key0(it);
+        St::load_k(kbase, row_stride, key0, n_k, tid, kb0, lo);
+        St::load_v(vbase, row_stride, key0, n_k, tid, vb0, lo);
+        wait_vmem_all();
+        lds_barrier();
+        f32x16 S[2];
+        S[0] = St::qk_tile(kb0, qf, 0, lane);
+        S[1] = St::qk_tile(kb0, qf, 1, lane);
+        mask(S, key0);
+        update(S);
+        bf16x8 P[4], unused;
+        float rs = 0.f;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) S[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -m_use));
+#pragma unroll
+        for (int s4 = 0; s4 < 4; ++s4) {
+          p_step<false>(S, s4, P[s4], unused);
+          rs = row_sum_bf16(P[s4], rs);
+        }
+        l_run += rs;
+        St::pv_packed(vb0, P, O, lane);
+        lds_barrier();  // every wave is done with the buffers before the next stage loads
+      }
     }
   } else {
     sweep<St>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, kb0, kb1, [&](int it, const char* cur) {
@@ -386,8 +432,10 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
           *reinterpret_cast<u32x2*>(orow + d * 2) = w;
         }
       }
+    // the weights are 2^(c s - m_use); with the lazy reference m_use stays at the first
+    // stage's max (0 if that stage was masked) while later stages add weight
     if (p.lse != nullptr && g2 == 0)
-      p.lse[(int64_t)h * p.total_q + qrow] = l_tot > 0.f ? (m_run + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
+      p.lse[(int64_t)h * p.total_q + qrow] = l_tot > 0.f ? (m_use + __builtin_log2f(l_tot)) * kLn2 : -INFINITY;
   }
 }
 

@@ -224,6 +224,62 @@ def test_empty_and_out_of_range_rows():
                 assert np.abs(out[r0:r0 + n, h] - Or).max() <= H.OUT_ATOL_BF16
 
 
+def test_lazy_reference_recomputes_spiked_tiles():
+    """Keys whose logit exceeds every logit of a tile's first stage by 60 and by 200 nats
+    (weights of 2^86 and, past fp32's range, 2^288 against the first stage's reference)
+    make the lazy reference reject the tile, which is then computed with the exact
+    running max. Dense and sparse outputs and LSE against the oracle on every tile; both
+    schedules bit-identical; the sparse kernel on full lists equal to dense bit for bit."""
+    import dataclasses
+    import torch
+    w = synth.small_workload(n_q=300, n_k=428, hq=4, hkv=2, d=128, block=128, dtype="bf16", seed=21)
+    inp = synth.make(w)
+    q = synth.bf16_bits_to_f32(inp.q).copy()
+    k = synth.bf16_bits_to_f32(inp.k).copy()
+    d = w.head_dim
+    q[:, :, d - 1] = 1.0
+    k[:, :, d - 1] = 0.0
+    k[300, 0, d - 1] = 60.0 * math.sqrt(d)   # KV head 0, key block 2
+    k[400, 1, d - 1] = 200.0 * math.sqrt(d)  # KV head 1, key block 3
+    inp = dataclasses.replace(inp, q=synth.round_to_bf16_bits(q), k=synth.round_to_bf16_bits(k))
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    tl = O.tiles(op)
+    rows = [list(range(t.diag + 1)) if (h + t.gtile) % 2 == 0 else [0, t.diag] + ([2] if t.diag > 2 else [])
+            for h in range(op.num_heads_q) for t in tl]
+    rows = [sorted(set(r)) for r in rows]
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    bi = np.array([b for r in rows for b in r] + [0], np.int32)
+    rpd, bid = torch.from_numpy(rp).cuda(), torch.from_numpy(bi).cuda()
+    say("lazy reference: spiked keys")
+    d_out, d_lse = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    d_out2, d_lse2 = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32", workspace=None)
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32")
+    s_out2, s_lse2 = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32", workspace=None)
+    full = [list(range(t.diag + 1)) for h in range(op.num_heads_q) for t in tl]
+    frp = torch.tensor(np.concatenate([[0], np.cumsum([len(r) for r in full])]), dtype=torch.int32, device="cuda")
+    fbi = torch.tensor([b for r in full for b in r], dtype=torch.int32, device="cuda")
+    f_out, f_lse = L.sparse_prefill(gp, qd, kd, vd, frp, fbi, out_dtype="fp32")
+    _sync()
+    assert torch.equal(d_out, d_out2) and torch.equal(d_lse, d_lse2)
+    assert torch.equal(s_out, s_out2) and torch.equal(s_lse, s_lse2)
+    assert torch.equal(f_out, d_out) and torch.equal(f_lse, d_lse)
+    qf, kf, vf = H.f64(inp)
+    ref_d = O.dense_prefill(op, qf, kf, vf)
+    ref_s = O.sparse_prefill(op, qf, kf, vf, rp.astype(np.int64), bi)
+    do, so, dl, sl = d_out.cpu().numpy(), s_out.cpu().numpy(), d_lse.cpu().numpy(), s_lse.cpu().numpy()
+    spiked = 0
+    for (h, gt), (Or, lr) in ref_d.items():
+        r0, n = H.tile_rows(op, gt)
+        assert np.abs(do[r0:r0 + n, h] - Or).max() <= H.OUT_ATOL_BF16, (h, gt)
+        assert H.lse_close(dl[h, r0:r0 + n], lr, H.LSE_ATOL_BF16), (h, gt)
+        Os, ls = ref_s[(h, gt)]
+        assert np.abs(so[r0:r0 + n, h] - Os).max() <= H.OUT_ATOL_BF16, (h, gt)
+        assert H.lse_close(sl[h, r0:r0 + n], ls, H.LSE_ATOL_BF16), (h, gt)
+        spiked += int(lr.max() > 50)
+    assert spiked >= 4  # the spikes reach several tiles of both KV heads
+
+
 def test_bf16_output_is_rounded_fp32_output():
     import torch
     w = _small(SMALL[1], seed=4)
