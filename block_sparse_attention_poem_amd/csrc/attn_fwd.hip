@@ -211,15 +211,20 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     // pipeline the dense tiles ran 0.3% faster than with one step of K lead). The step
     // is laid out by hand in short chunks fenced off from the scheduler:
     //   QK phase : each QK^T MFMA of stage j with the next-but-one K fragment read and
-    //              the exponentials (and bf16 packs) of stage j-1;
+    //              the exponentials (and bf16 packs) of key steps 0-1 of stage j-1;
     //   mask     : only on stages that reach past a row;
-    //   PV phase : each P V MFMA of stage j-1 with the next-but-one V fragment read.
+    //   PV phase : each P V MFMA of stage j-1 with the next-but-one V fragment read, the
+    //              first half also with the exponentials of key steps 2-3.
     // The reference is the first stage's max (see above); a rejected tile is computed
     // again one stage at a time with the exact running max.
     constexpr int NQK = 2 * (D / 16);  // QK^T MFMAs per stage (2 key tiles x d steps)
     constexpr int NDT = D / 32;        // d tiles of O
     constexpr int NPV = 4 * NDT;       // P V MFMAs per stage (4 key steps x d tiles)
-    constexpr int EPM = 32 / NQK;      // exponentials per QK MFMA
+    constexpr int EPQ = 16 / NQK;      // exponentials per QK MFMA (key steps 0-1)
+    constexpr int EPV = 16 / (NPV / 2);  // per P V MFMA of the first half (key steps 2-3)
+    // key step 2's pack is complete after PV MFMA NPV/4 - 1, step 3's after NPV/2 - 1,
+    // ahead of their first use at MFMAs 2 NDT = NPV/2 and 3 NDT
+    static_assert(16 % NQK == 0 && 16 % (NPV / 2) == 0, "exponential split");
     // The row sums add the bf16 weights the P V MFMAs use (two per dot instruction), so
     // numerator and denominator see the same rounding.
     f32x16 Sp[2];
@@ -284,12 +289,13 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
       for (int i = 0; i < NQK; ++i) {
         Sn[i & 1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[i % 3], qf.q[i >> 1], Sn[i & 1], 0, 0, 0);
         if (i + 2 < NQK) ka[(i + 2) % 3] = kfrag(kcur, i + 2);
+        // key steps 0 and 1 of stage j-1 here, steps 2 and 3 next to the first half of the
+        // PV MFMAs, which do not use them yet (measured at 128K against all four here:
+        // sparse -0.45%, dense -1.5%, the same bits)
 #pragma unroll
-        for (int u = 0; u < EPM; ++u) {
-          const int e = i * EPM + u;
+        for (int u = 0; u < EPQ; ++u) {
+          const int e = i * EPQ + u;
           Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
-          // bf16 packs and row sums of all four key steps in this phase (measured at
-          // 128K: packs next to the PV MFMAs make the sparse kernel 4.4% slower)
           if ((e & 7) == 7) {
             bf16x8 unused;
             p_step<false>(Sp, e >> 3, P[e >> 3], unused);
@@ -301,8 +307,6 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         }
         __builtin_amdgcn_sched_barrier(0);
       }
-      l_run += rs;
-      ovf |= !(rs <= kLazyCap);
       // PV phase
       __builtin_amdgcn_s_setprio(0);
       bf16x8 va[3];
@@ -313,8 +317,23 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
         const int dt = i % NDT, st = i / NDT;
         O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], P[st], O[dt], 0, 0, 0);
         if (i + 2 < NPV) va[(i + 2) % 3] = St::v_frag(vprev, (i + 2) % NDT, (i + 2) / NDT, lane);
+        if (i < NPV / 2) {  // exponentials, packs and sums of key steps 2 and 3
+#pragma unroll
+          for (int u = 0; u < EPV; ++u) {
+            const int e = 16 + i * EPV + u;
+            Sp[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(Sp[e >> 4][e & 15], c, -m_use));
+            if ((e & 7) == 7) {
+              bf16x8 unused;
+              p_step<false>(Sp, e >> 3, P[e >> 3], unused);
+              rs = row_sum_bf16(P[e >> 3], rs);
+              __asm__ volatile("" : "+v"(rs));
+            }
+          }
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
+      l_run += rs;
+      ovf |= !(rs <= kLazyCap);
       if (key0 + kStageKeys - 1 > wave_pos_min) mask(Sn, key0);
       Sp[0] = Sn[0];
       Sp[1] = Sn[1];
