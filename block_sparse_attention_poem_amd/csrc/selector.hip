@@ -743,6 +743,32 @@ __device__ __forceinline__ void sort_blocked(uint64_t (&x)[E], uint64_t* sh) {
   }
 }
 
+// Sampled rows i0 .. i0 + nr - 1 (nr <= kRowChunk, i0 a multiple of kRowChunk) of visible
+// block b, from the LDS copy (st) or the workspace (glob). A staged record holds a
+// block's S rows side by side, so with S a multiple of 4 they are read as 16-byte
+// vectors: one 32-bit read per row, with the lanes of a wave on records S floats
+// apart, would put the whole wave on a few LDS banks. Entries r >= nr are not set.
+template <bool STAGED>
+__device__ __forceinline__ void block_rows(const float* st, const float* glob, int64_t bstride, int S, int b, int i0,
+                                           int nr, float (&v)[kRowChunk]) {
+  if (STAGED && S % 4 == 0) {
+    const float* rec = st + b * S + i0;  // 16-byte aligned: st is, and b * S + i0 is a multiple of 4
+#pragma unroll
+    for (int r = 0; r < kRowChunk; r += 4)
+      if (r < nr) {  // rows up to r + 3 < S stay inside the record
+        const f32x4 q4 = *reinterpret_cast<const f32x4*>(rec + r);
+        v[r] = q4[0];
+        v[r + 1] = q4[1];
+        v[r + 2] = q4[2];
+        v[r + 3] = q4[3];
+      }
+  } else {
+#pragma unroll
+    for (int r = 0; r < kRowChunk; ++r)
+      if (r < nr) v[r] = STAGED ? st[b * S + i0 + r] : glob[(int64_t)b * bstride + i0 + r];
+  }
+}
+
 // One (query head, tile) of the threshold kernel after staging: scores, sort, cut,
 // row bounds and compaction, with E = padded candidates / 256 keys per thread.
 struct ThrTile {
@@ -764,13 +790,11 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
   const int S = w.S, s_t = w.s_t, n_vis = w.n_vis, diag = w.diag;
-  auto I_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_I[b * S + i];
-    else return w.Ib[(int64_t)b * w.bstride + i];
+  auto rows_I = [&](int b, int i0, int nr, float (&v)[kRowChunk]) {
+    block_rows<STAGED>(st_I, w.Ib, w.bstride, S, b, i0, nr, v);
   };
-  auto m_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_m[b * S + i];
-    else return w.Mb[(int64_t)b * w.bstride + i];
+  auto rows_m = [&](int b, int i0, int nr, float (&v)[kRowChunk]) {
+    block_rows<STAGED>(st_m, w.Mb, w.bstride, S, b, i0, nr, v);
   };
   auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
   const float inv_s = 1.f / (float)s_t;
@@ -778,9 +802,8 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
   const int64_t diag_row = ((int64_t)w.h0 * T + w.gtile) * p.max_vis;
   auto tau_of = [&](int i) { return p.tau[w.h0 + (w.tau_group ? i % w.tau_group : 0)]; };
 
-  // scores of blocks e * 256 + tid (consecutive lanes read consecutive records, so
-  // the staged reads stay off each other's banks), as sort keys (score bits, ~id);
-  // the sort does not care where a key starts
+  // scores of blocks e * 256 + tid as sort keys (score bits, ~id); the sort does not
+  // care where a key starts
   uint64_t x[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) {
@@ -788,9 +811,17 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
     x[e] = ~0ull;
     if (b < n_vis) {
       float si = 0.f, sm = 0.f;
-      for (int i = 0; i < s_t; ++i) {
-        if constexpr (POEM) si += I_of(b, i);
-        sm += m_of(b, i);
+      for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+        const int nr = min(kRowChunk, s_t - i0);
+        float vi[kRowChunk], vm[kRowChunk];
+        if constexpr (POEM) rows_I(b, i0, nr, vi);
+        rows_m(b, i0, nr, vm);
+#pragma unroll
+        for (int r = 0; r < kRowChunk; ++r)
+          if (r < nr) {
+            if constexpr (POEM) si += vi[r];
+            sm += vm[r];
+          }
       }
       const float mass = sm * inv_s;
       const float score = POEM ? si * inv_s : mass;
@@ -844,11 +875,14 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       if (tid * E + e < limit) {
+        float vi[kRowChunk], vm[kRowChunk];
+        if constexpr (POEM) rows_I(ids[e], i0, nr, vi);
+        rows_m(ids[e], i0, nr, vm);
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
           if (r < nr) {
-            if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
-            Dl[r] += (double)m_of(ids[e], i0 + r);
+            if constexpr (POEM) A[r] += (double)vi[r];
+            Dl[r] += (double)vm[r];
           }
       }
     }
@@ -858,11 +892,14 @@ __device__ __forceinline__ void threshold_tile(const SelectParams& p, const ThrT
       const int k = tid * E + e;
       if (k < limit) {
         bool over = false;
+        float vi[kRowChunk], vm[kRowChunk];
+        if constexpr (POEM) rows_I(ids[e], i0, nr, vi);
+        rows_m(ids[e], i0, nr, vm);
 #pragma unroll
         for (int r = 0; r < kRowChunk; ++r)
           if (r < nr) {
-            if constexpr (POEM) A[r] += (double)I_of(ids[e], i0 + r);
-            Dl[r] += (double)m_of(ids[e], i0 + r);
+            if constexpr (POEM) A[r] += (double)vi[r];
+            Dl[r] += (double)vm[r];
             if (find) over |= exceeds(A[r], Dl[r], (double)tau_of(i0 + r));
             if constexpr (KEEP)
               if (keep_bounds) kept_b[e][r] = (float)bound_of(A[r], Dl[r]);
@@ -974,14 +1011,6 @@ __device__ __forceinline__ void practical_tile(const SelectParams& p, const ThrT
   const int tid = threadIdx.x;
   const int T = p.seqs.total_tiles;
   const int S = w.S, s_t = w.s_t, n_vis = w.n_vis, diag = w.diag;
-  auto I_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_I[b * S + i];
-    else return w.Ib[(int64_t)b * w.bstride + i];
-  };
-  auto m_of = [&](int b, int i) -> float {
-    if constexpr (STAGED) return st_m[b * S + i];
-    else return w.Mb[(int64_t)b * w.bstride + i];
-  };
   auto mandatory = [&](int b) { return b < p.n_sink || b > diag - p.n_local; };
   const float inv_s = 1.f / (float)s_t;
   const float wt = p.prac_w;
@@ -1006,9 +1035,17 @@ __device__ __forceinline__ void practical_tile(const SelectParams& p, const ThrT
     x[e] = ~0ull;
     if (b < n_vis) {
       float si = 0.f, sm = 0.f;
-      for (int i = 0; i < s_t; ++i) {
-        si += I_of(b, i);
-        sm += m_of(b, i);
+      for (int i0 = 0; i0 < s_t; i0 += kRowChunk) {
+        const int nr = min(kRowChunk, s_t - i0);
+        float vi[kRowChunk], vm[kRowChunk];
+        block_rows<STAGED>(st_I, w.Ib, w.bstride, S, b, i0, nr, vi);
+        block_rows<STAGED>(st_m, w.Mb, w.bstride, S, b, i0, nr, vm);
+#pragma unroll
+        for (int r = 0; r < kRowChunk; ++r)
+          if (r < nr) {
+            si += vi[r];
+            sm += vm[r];
+          }
       }
       const float mb = sm * inv_s, ib = si * inv_s;
       bar_I[b] = ib;
@@ -1085,11 +1122,14 @@ __device__ __forceinline__ void practical_tile(const SelectParams& p, const ThrT
       double a[kRowChunk], d[kRowChunk], mine[kRowChunk];
 #pragma unroll
       for (int r = 0; r < kRowChunk; ++r) a[r] = d[r] = 0.0;
+      const int nr = min(kRowChunk, s_t - i0);
       for (int b = tid; b < n_vis; b += kThrThreads)
         if (!keep[b]) {
+          float vm[kRowChunk];
+          block_rows<STAGED>(st_m, w.Mb, w.bstride, S, b, i0, nr, vm);
 #pragma unroll
           for (int r = 0; r < kRowChunk; ++r)
-            if (i0 + r < s_t) a[r] += (double)m_of(b, i0 + r);
+            if (r < nr) a[r] += (double)vm[r];
         }
 #pragma unroll
       for (int r = 0; r < kRowChunk; ++r) mine[r] = a[r];
@@ -1125,9 +1165,9 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   constexpr int NK = STAGED ? kStageVis : kMaxVis;
   __shared__ uint64_t sh[NK];
   __shared__ uint8_t keep[NK];
-  __shared__ float st_I[STAGED && NEED_I ? kStageVals : 1];
+  __shared__ __attribute__((aligned(16))) float st_I[STAGED && NEED_I ? kStageVals : 1];
   __shared__ float bar_I[PRAC ? NK : 1], bar_m[PRAC ? NK : 1];  // practical: pooled estimates
-  __shared__ float st_m[STAGED ? kStageVals : 1];
+  __shared__ __attribute__((aligned(16))) float st_m[STAGED ? kStageVals : 1];
   __shared__ double shd[2 * kRowChunk * kThrWaves];
   __shared__ int shi[kThrWaves];
   const int tid = threadIdx.x;
