@@ -62,6 +62,7 @@ struct SelectParams {
   int32_t group_mode;
   int32_t cols_rec;
   int32_t tiles_per_wave;
+  int32_t p2_chunk_blocks, p2_chunks;  // pass 2 grid: blocks per chunk, chunks per tile group (set at launch)
   float scale_log2;
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions

@@ -87,7 +87,11 @@ void sel_sweep_kernel(SelectParams p) {
   const int TG = p.group_mode ? kSelWaves * TPW : max(1, kSelWaves / CT);
 
   const int gk = blockIdx.x % p.hkv;
-  const int rank = blockIdx.x / p.hkv;
+  // pass 2: the tile group's visible blocks in chunks of p2_chunk_blocks, one chunk per
+  // workgroup (a block's I and m need only pass 1's record, so chunks are independent);
+  // the chunks of a group are adjacent in the grid
+  const int chunk = PASS2 ? (int)(blockIdx.x / p.hkv) % p.p2_chunks : 0;
+  const int rank = PASS2 ? (int)(blockIdx.x / p.hkv) / p.p2_chunks : (int)(blockIdx.x / p.hkv);
   int seq, tile0;
   rank_to_item(p.seqs, TG, rank, seq, tile0);
   if (seq < 0) return;
@@ -95,6 +99,9 @@ void sel_sweep_kernel(SelectParams p) {
   const int diag0 = p.seqs.diag0[seq];
   const int t_last = min(tile0 + TG - 1, n_tiles - 1);
   const int nblk_wg = diag0 + t_last + 1;
+  const int blk_lo = PASS2 ? chunk * p.p2_chunk_blocks : 0;  // this workgroup's blocks: blk_lo .. blk_hi - 1
+  const int blk_hi = PASS2 ? min(nblk_wg, blk_lo + p.p2_chunk_blocks) : nblk_wg;
+  if (blk_lo >= blk_hi) return;
 
   // this lane's column: tile t, record column col, row jr of the tile's sample taken
   // from query head gk * G + hg
@@ -179,7 +186,7 @@ void sel_sweep_kernel(SelectParams p) {
       }
   };
   // pass 2 holds o, except that the bf16 pass holds R / l while it forms block 0
-  if constexpr (PASS2 && !MASS && !PIPE) load_vec(Od, F16PV ? 4 + D : 4);
+  if constexpr (PASS2 && !MASS && !PIPE) load_vec(Od, (F16PV && blk_lo == 0) ? 4 + D : 4);
   // per (KV head, tile, visible block): I of the record's columns, then m of them, so
   // a wave's per-block results are one coalesced store each per tile
   float* blk_I = nullptr;
@@ -194,10 +201,11 @@ void sel_sweep_kernel(SelectParams p) {
   // fragment reads in flight as well); the sweep's first barrier publishes it
   __shared__ float vsc_sh[F16PV ? kMaxSeqBlocks : 1];
   if constexpr (F16PV) {
-    for (int i = tid; i < nblk_wg; i += sel_threads<T>()) vsc_sh[i] = vsc[i];
+    for (int i = blk_lo + tid; i < blk_hi; i += sel_threads<T>()) vsc_sh[i] = vsc[i];
   }
   wait_vmem_all();
-  const int total = nblk_wg * SUBS;
+  const int total = (blk_hi - blk_lo) * SUBS;  // stages of this workgroup
+  const int it_base = blk_lo * SUBS;            // (pass 1: every block, from block 0)
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
   // pass 2: I and m of one block from its weight sum and U (O), for the pair's column
   // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
@@ -487,7 +495,9 @@ void sel_sweep_kernel(SelectParams p) {
       }
     }
   };
-  sweep<St, MASS>(total, stage_key0, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int it, const char* cur) {
+  auto key0_of = [&](int i) { return stage_key0(it_base + i); };
+  sweep<St, MASS>(total, key0_of, kbase, vbase, row_stride, n_k, tid, buf0, buf1, [&](int i, const char* cur) {
+    const int it = it_base + i;
     const int blk = it / SUBS, sub = it % SUBS;
     const int key0 = stage_key0(it);
     if (PASS2 && sub == 0) {
@@ -1351,6 +1361,10 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
   if (tid == 0) p.vscale[(int64_t)g * p.total_kb + kb] = sb;
 }
 
+constexpr int kP2MaxChunk = 1024;    // pass 2 chunk sizes tried, in key blocks
+constexpr int kP2MinChunk = 16;
+constexpr int kP2Workgroups = 1024;  // enough workgroups to balance 256 CUs
+
 template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   constexpr int kSelWaves = sel_threads<T>() / 64;
@@ -1364,16 +1378,40 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     return hipGetLastError();
   }
   const unsigned grid = (unsigned)((int64_t)items * p.hkv);
+  // Pass 2 chunks: the largest power-of-two chunk (of 16 .. 1024 blocks) that still
+  // gives kP2Workgroups non-empty workgroups. A tile group's sweep is as long as its
+  // last tile, so few long groups (short sequences, or chunks of many queries against
+  // long prefixes) would otherwise leave most CUs idle behind the longest group.
+  SelectParams p2 = p;
+  {
+    auto nonempty = [&](int C) {
+      int64_t n = 0;
+      for (int i = 0; i < p.seqs.num_seqs; ++i)
+        for (int t0 = 0; t0 < p.seqs.n_tiles[i]; t0 += TG) {
+          const int nblk = p.seqs.diag0[i] + min(t0 + TG, p.seqs.n_tiles[i]);
+          n += (nblk + C - 1) / C;
+        }
+      return n * p.hkv;
+    };
+    int C = kP2MaxChunk;
+    while (C > kP2MinChunk && nonempty(C) < kP2Workgroups) C >>= 1;
+    int max_nblk = 1;
+    for (int i = 0; i < p.seqs.num_seqs; ++i)
+      if (p.seqs.n_tiles[i] > 0) max_nblk = max(max_nblk, p.seqs.diag0[i] + p.seqs.n_tiles[i]);
+    p2.p2_chunk_blocks = C;
+    p2.p2_chunks = (max_nblk + C - 1) / C;
+  }
+  const unsigned grid2 = (unsigned)((int64_t)items * p.hkv * p2.p2_chunks);
   const bool mass = p.mode == kSelectMass;
   if (mass) {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid2), dim3(kSelThreads), 0, s, p2);
   } else {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
     if (sizeof(T) == 2 && p.total_kb > 0)  // the fp16 copy of V that pass 2 reads (bf16 inputs)
       hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
                          p);
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid2), dim3(kSelThreads), 0, s, p2);
   }
   // threshold grid: (KV-head unit, head in group) with the unit's XCD kept fixed
   const int64_t units = (int64_t)p.seqs.total_tiles * p.hkv;
