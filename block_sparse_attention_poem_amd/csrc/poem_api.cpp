@@ -113,7 +113,8 @@ poem_status build_geometry(const poem_problem* p, Geometry& g) {
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct SelLayout {
-  size_t row_stats = 0, blk_stats = 0, counts = 0, slots = 0, v16 = 0, vscale = 0, total = 0;
+  size_t row_stats = 0, p1_part = 0, blk_stats = 0, counts = 0, slots = 0, v16 = 0, vscale = 0, total = 0;
+  poem::SweepChunks p1 = {0, 1};  // pass 1 chunks (bf16 inputs)
 };
 
 // key blocks over all sequences (ceil(N_k / B) each)
@@ -130,11 +131,20 @@ int record_columns(const poem_problem* p, int S, bool group_mode) {
   return group_mode ? S : 32 * ((G * S + 31) / 32);
 }
 
-SelLayout sel_layout(const poem_problem* p, const Geometry& g, int cols) {
+SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S, bool group_mode) {
   SelLayout L;
+  const int cols = record_columns(p, S, group_mode);
+  const int G = p->num_heads_q / p->num_heads_kv;
   size_t off = 0;
   L.row_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (2 * p->head_dim + 4));
+  if (p->in_dtype == POEM_BF16) {  // pass 1 in chunks: partial records of the chunks after the first
+    const int TG = poem::sel_tile_group(true, (G * S + 31) / 32, group_mode, group_mode ? 32 / S : 1);
+    L.p1 = poem::sweep_chunks(g.st, p->num_heads_kv, TG, poem::kPass1MaxChunks, poem::kPass1Workgroups);
+    L.p1_part = off;
+    off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (L.p1.chunks - 1) *
+                    (p->head_dim + 4));
+  }
   L.blk_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.vis_per_head * cols * 2);
   L.counts = off;
@@ -203,9 +213,8 @@ int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_pe
   ok();
   // enough for every selector entry point the problem allows
   const int G = problem->num_heads_q / problem->num_heads_kv;
-  size_t bytes = sel_layout(problem, g, record_columns(problem, rows_per_tile, true)).total;
-  if ((int64_t)G * rows_per_tile <= 128)
-    bytes = std::max(bytes, sel_layout(problem, g, record_columns(problem, rows_per_tile, false)).total);
+  size_t bytes = sel_layout(problem, g, rows_per_tile, true).total;
+  if ((int64_t)G * rows_per_tile <= 128) bytes = std::max(bytes, sel_layout(problem, g, rows_per_tile, false).total);
   return (int64_t)bytes;
 }
 
@@ -239,7 +248,7 @@ static poem_status select_impl(int mode, bool group_mode, float prac_w, float pr
     return fail(POEM_ERR_CAPACITY, "block_idx capacity %lld < required %lld", (long long)block_idx_capacity,
                 (long long)g.capacity);
   const int cols = record_columns(problem, rows_per_tile, group_mode);
-  const SelLayout L = sel_layout(problem, g, cols);
+  const SelLayout L = sel_layout(problem, g, rows_per_tile, group_mode);
   if (workspace == nullptr) return fail(POEM_ERR_WORKSPACE, "workspace is NULL");
   if (workspace_bytes < L.total)
     return fail(POEM_ERR_WORKSPACE, "workspace has %zu bytes, %zu needed", workspace_bytes, L.total);
@@ -268,6 +277,9 @@ static poem_status select_impl(int mode, bool group_mode, float prac_w, float pr
   for (int h = 0; h < problem->num_heads_q; ++h) sp.tau[h] = tau_host[h];
   char* ws = static_cast<char*>(workspace);
   sp.row_stats = reinterpret_cast<float*>(ws + L.row_stats);
+  sp.p1_part = reinterpret_cast<float*>(ws + L.p1_part);
+  sp.p1_chunk_blocks = L.p1.blocks;
+  sp.p1_chunks = L.p1.chunks;
   sp.blk_stats = reinterpret_cast<float*>(ws + L.blk_stats);
   sp.counts = reinterpret_cast<int32_t*>(ws + L.counts);
   sp.slots = reinterpret_cast<int32_t*>(ws + L.slots);

@@ -62,11 +62,15 @@ struct SelectParams {
   int32_t group_mode;
   int32_t cols_rec;
   int32_t tiles_per_wave;
-  int32_t p2_chunk_blocks, p2_chunks;  // pass 2 grid: blocks per chunk, chunks per tile group (set at launch)
+  int32_t tile_group;                  // tiles per sweep workgroup (set at launch)
+  int32_t sweep_items;                 // tile groups (set at launch)
+  int32_t p1_chunk_blocks, p1_chunks;  // pass 1 grid: blocks per chunk, chunks per tile group
+  int32_t p2_chunk_blocks, p2_chunks;  // pass 2 grid (set at launch)
   float scale_log2;
   float tau[kMaxHeadsQ];     // per query head, passed by value
   // workspace regions
   float* row_stats;          // [hkv][total_tiles][cols_rec][2 D + 4]: M2, l, L_rest / l, pad, o, R / l
+  float* p1_part;            // pass 1 in chunks: [hkv][total_tiles][cols_rec][p1_chunks - 1][D + 4]
   float* blk_stats;          // per (KV head, gtile, visible block): I[cols_rec] then m[cols_rec]
   int32_t* counts;           // [hq * total_tiles]
   int32_t* slots;            // [hq * vis_per_head] retained ids at slot offsets
@@ -85,5 +89,47 @@ struct SelectParams {
 };
 
 hipError_t launch_select(const SelectParams& p, int in_dtype, int head_dim, int block, hipStream_t stream);
+
+// Selector sweeps, host side. A sweep workgroup walks the visible blocks of a tile
+// group (TG consecutive tiles of one sequence and KV head): eight waves for bf16 inputs,
+// four for fp32, each wave one 32-column tile, or tiles_per_wave tiles of group-shared
+// lists.
+inline int sel_tile_group(bool bf16, int col_tiles, bool group_mode, int tiles_per_wave) {
+  const int waves = bf16 ? 8 : 4;
+  if (group_mode) return waves * tiles_per_wave;
+  return waves / col_tiles > 1 ? waves / col_tiles : 1;
+}
+
+// A long group's blocks can be split into chunks of whole blocks, one workgroup each,
+// so that few long groups do not leave most CUs idle behind the longest: the largest
+// power-of-two chunk of kSweepMaxChunk .. kSweepMinChunk blocks that gives at least
+// `target` non-empty workgroups, then doubled while a group would need more than
+// max_chunks chunks.
+constexpr int kSweepMaxChunk = 1024;
+constexpr int kSweepMinChunk = 16;
+constexpr int64_t kPass1Workgroups = 1024;
+constexpr int64_t kPass2Workgroups = 1024;
+struct SweepChunks {
+  int blocks, chunks;
+};
+inline SweepChunks sweep_chunks(const SeqTable& st, int hkv, int TG, int max_chunks, int64_t target) {
+  int max_nblk = 1;
+  for (int s = 0; s < st.num_seqs; ++s)
+    if (st.n_tiles[s] > 0 && st.diag0[s] + st.n_tiles[s] > max_nblk) max_nblk = st.diag0[s] + st.n_tiles[s];
+  auto nonempty = [&](int C) {
+    int64_t n = 0;
+    for (int s = 0; s < st.num_seqs; ++s)
+      for (int t0 = 0; t0 < st.n_tiles[s]; t0 += TG) {
+        const int t1 = t0 + TG < st.n_tiles[s] ? t0 + TG : st.n_tiles[s];
+        n += (st.diag0[s] + t1 + C - 1) / C;
+      }
+    return n * hkv;
+  };
+  int C = kSweepMaxChunk;
+  while (C > kSweepMinChunk && nonempty(C) < target) C >>= 1;
+  while ((max_nblk + C - 1) / C > max_chunks) C <<= 1;
+  return {C, (max_nblk + C - 1) / C};
+}
+constexpr int kPass1MaxChunks = 8;  // bounds pass 1's partial records (workspace)
 
 }  // namespace poem

@@ -23,7 +23,12 @@
 // attention kernel; a workgroup of eight waves (bf16) holds several tiles of one KV
 // head (one CU each: two waves per SIMD), so each fetch is shared by up to 256 columns
 // and the direct loads per MFMA are half those of four-wave workgroups (measured: the
-// selector's two passes run 6% faster at 128K).
+// selector's two passes run 6% faster at 128K). When the tile groups are too few to
+// fill the chip with long ones among them (short sequences; chunks of a few thousand
+// queries against long prefixes), each group's blocks are split into chunks of whole
+// blocks, one workgroup per chunk, run chunk-major so that the workgroups of one XCD
+// read the same key range; pass 1's chunks leave partial sums at their own exponent
+// references that sel_merge_kernel combines (see there).
 //
 // Precision of P V (bf16 inputs). Pass 1 takes one bf16 P for o, R, l and L_rest: the
 // row's maximum key weighs exactly 1, the rounding of the other weights averages out
@@ -87,11 +92,16 @@ void sel_sweep_kernel(SelectParams p) {
   const int TG = p.group_mode ? kSelWaves * TPW : max(1, kSelWaves / CT);
 
   const int gk = blockIdx.x % p.hkv;
-  // pass 2: the tile group's visible blocks in chunks of p2_chunk_blocks, one chunk per
-  // workgroup (a block's I and m need only pass 1's record, so chunks are independent);
-  // the chunks of a group are adjacent in the grid
-  const int chunk = PASS2 ? (int)(blockIdx.x / p.hkv) % p.p2_chunks : 0;
-  const int rank = PASS2 ? (int)(blockIdx.x / p.hkv) / p.p2_chunks : (int)(blockIdx.x / p.hkv);
+  // the tile group's visible blocks in chunks of whole blocks, one chunk per workgroup.
+  // The grid runs chunk 0 of every group (longest groups first), then chunk 1, ...: the
+  // workgroups resident together on an XCD (one KV head each) then read the same range
+  // of key blocks, which its L2 serves once. Pass 2's chunks are independent (a block's
+  // I and m need only pass 1's record); pass 1's chunks leave partial sums that
+  // sel_merge_kernel combines.
+  const int n_chunks = PASS2 ? p.p2_chunks : p.p1_chunks;
+  const int chunk_blocks = PASS2 ? p.p2_chunk_blocks : p.p1_chunk_blocks;
+  const int chunk = (int)(blockIdx.x / p.hkv) / p.sweep_items;
+  const int rank = (int)(blockIdx.x / p.hkv) % p.sweep_items;
   int seq, tile0;
   rank_to_item(p.seqs, TG, rank, seq, tile0);
   if (seq < 0) return;
@@ -99,8 +109,8 @@ void sel_sweep_kernel(SelectParams p) {
   const int diag0 = p.seqs.diag0[seq];
   const int t_last = min(tile0 + TG - 1, n_tiles - 1);
   const int nblk_wg = diag0 + t_last + 1;
-  const int blk_lo = PASS2 ? chunk * p.p2_chunk_blocks : 0;  // this workgroup's blocks: blk_lo .. blk_hi - 1
-  const int blk_hi = PASS2 ? min(nblk_wg, blk_lo + p.p2_chunk_blocks) : nblk_wg;
+  const int blk_lo = chunk * chunk_blocks;  // this workgroup's blocks: blk_lo .. blk_hi - 1
+  const int blk_hi = min(nblk_wg, blk_lo + chunk_blocks);
   if (blk_lo >= blk_hi) return;
 
   // this lane's column: tile t, record column col, row jr of the tile's sample taken
@@ -205,7 +215,7 @@ void sel_sweep_kernel(SelectParams p) {
   }
   wait_vmem_all();
   const int total = (blk_hi - blk_lo) * SUBS;  // stages of this workgroup
-  const int it_base = blk_lo * SUBS;            // (pass 1: every block, from block 0)
+  const int it_base = blk_lo * SUBS;
   auto stage_key0 = [](int it) { return (it / SUBS) * BLK + (it % SUBS) * kStageKeys; };
   // pass 2: I and m of one block from its weight sum and U (O), for the pair's column
   // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
@@ -292,16 +302,17 @@ void sel_sweep_kernel(SelectParams p) {
       }
     };
     f32x16 Sp[2] = {f32x16{}, f32x16{}};
+    auto skey = [&](int i) { return stage_key0(it_base + i); };  // first key of the chunk's stage i
     {
-      St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0, lofs);
+      St::load_k(kbase, row_stride, skey(0), n_k, tid, kb0, lofs);
       wait_vmem_all();
       __syncthreads();
-      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lofs);
-      St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0, lofs);
+      St::load_k(kbase, row_stride, skey(min(1, total - 1)), n_k, tid, kb1, lofs);
+      St::load_v(vbase, row_stride, skey(0), n_k, tid, vb0, lofs);
       if (total > 0) {
         Sp[0] = St::qk_tile(kb0, qf, 0, lane);
         Sp[1] = St::qk_tile(kb0, qf, 1, lane);
-        if (kStageKeys - 1 > wave_pos_min) mask(Sp, 0);
+        if (skey(0) + kStageKeys - 1 > wave_pos_min) mask(Sp, skey(0));
         if constexpr (!PASS2) {
           float mx = -INFINITY;
 #pragma unroll
@@ -316,9 +327,9 @@ void sel_sweep_kernel(SelectParams p) {
     // softmax and P V of stage it - 1; the last step (it = total) has P V alone
     auto step = [&](auto more_tag, int it, const char* kcur, char* knext, const char* vprev, char* vcur) {
       constexpr bool MORE = decltype(more_tag)::value;
-      const int key0 = MORE ? stage_key0(it) : 0;
+      const int key0 = MORE ? skey(it) : 0;
       if constexpr (MORE) {
-        St::load_k(kbase, row_stride, stage_key0(min(it + 1, total - 1)), n_k, tid, knext, lofs);
+        St::load_k(kbase, row_stride, skey(min(it + 1, total - 1)), n_k, tid, knext, lofs);
         St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lofs);
       }
       f32x16 Sn[2] = {f32x16{}, f32x16{}};
@@ -372,7 +383,7 @@ void sel_sweep_kernel(SelectParams p) {
       }
       __builtin_amdgcn_s_setprio(0);
       l_run += rs;
-      if (pst == SUBS - 1) {
+      if (it_base + pst == SUBS - 1) {
         // block 0 is complete: its sums U_0 (in the record's o slot) and L_0 are kept
         // apart, at the reference they were formed with, and O and l restart for the
         // blocks after it
@@ -582,7 +593,42 @@ void sel_sweep_kernel(SelectParams p) {
   });
   }
 
-  if constexpr (!PASS2 && SPLIT0) {
+  if (!PASS2 && SPLIT0 && n_chunks > 1) {
+    // one chunk of the group's blocks: raw sums at this chunk's own reference m_ref, for
+    // sel_merge_kernel. Chunk 0 leaves in the record M2 <- m_ref, l <- L_rest of its
+    // blocks after block 0, then u0_ref and L_0, with U_0 already in the o slot and R in
+    // the R / l slot; a later chunk leaves (m_ref, or -inf when it saw no key, its weight
+    // sum, U) in its partial record.
+    const float l_c = half_sum(l_run);
+    const float l0 = half_sum(l0_run);
+    if (col_on) {
+      float* vdst;
+      if (chunk == 0) {
+        if (g2 == 0) {
+          rs_col[0] = m_ref;
+          rs_col[1] = l_c;
+          rs_col[2] = u0_ref;
+          rs_col[3] = l0;
+        }
+        vdst = rs_col + 4 + D;
+      } else {
+        float* part = p.p1_part + ((((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + col) * (n_chunks - 1) +
+                                   (chunk - 1)) * (D + 4);
+        if (g2 == 0) {
+          part[0] = l_c > 0.f ? m_ref : -INFINITY;
+          part[1] = l_c;
+        }
+        vdst = part + 4;
+      }
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 u = {O[dt][4 * a], O[dt][4 * a + 1], O[dt][4 * a + 2], O[dt][4 * a + 3]};
+          *reinterpret_cast<f32x4*>(vdst + 32 * dt + 8 * a + 4 * g2) = u;
+        }
+    }
+  } else if constexpr (!PASS2 && SPLIT0) {
     // O and l hold R and L_rest (the blocks after block 0) at reference m_ref; U_0 (in the
     // record) and L_0 were formed at reference u0_ref <= m_ref
     const float f0 = __builtin_amdgcn_exp2f(u0_ref - m_ref);
@@ -1361,9 +1407,58 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
   if (tid == 0) p.vscale[(int64_t)g * p.total_kb + kb] = sb;
 }
 
-constexpr int kP2MaxChunk = 1024;    // pass 2 chunk sizes tried, in key blocks
-constexpr int kP2MinChunk = 16;
-constexpr int kP2Workgroups = 1024;  // enough workgroups to balance 256 CUs
+// Pass 1 in chunks (bf16): one wave per record column combines the chunks' sums into
+// the record pass 2 reads. With M2 the largest chunk reference and f_k = 2^(m_k - M2):
+// L_rest = sum_k l_k f_k and R = sum_k U_k f_k over every chunk's blocks after block 0,
+// l = L_0 2^(u0_ref - M2) + L_rest, o = (U_0 2^(u0_ref - M2) + R) / l: the sums of the
+// unsplit sweep, each chunk's rescaled once to the common reference.
+template <int D>
+__global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
+  const int T = p.seqs.total_tiles;
+  const int64_t rec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (KV head * T + gtile) * cols_rec + col
+  const int lane = threadIdx.x & 63;
+  if (rec >= (int64_t)p.hkv * T * p.cols_rec) return;
+  const int col = (int)(rec % p.cols_rec);
+  const int gtile = (int)((rec / p.cols_rec) % T);
+  const int seq = find_seq(p.seqs, gtile);
+  const int t = gtile - p.seqs.tile_start[seq];
+  const int B = p.seqs.block;
+  const int s_t = min(p.S, min(B, p.seqs.n_q[seq] - t * B));
+  const bool on = p.group_mode ? col < s_t : (col / p.S < p.group && col % p.S < s_t);
+  if (!on) return;  // a column pass 1 did not write
+  const int TG = p.tile_group;
+  const int t_last = min((t / TG) * TG + TG - 1, p.seqs.n_tiles[seq] - 1);
+  const int nblk = p.seqs.diag0[seq] + t_last + 1;
+  const int nch = (nblk + p.p1_chunk_blocks - 1) / p.p1_chunk_blocks;  // chunks the group ran
+  float* r = p.row_stats + rec * kRecordFloats<D>;
+  const float* part = p.p1_part + rec * (int64_t)(p.p1_chunks - 1) * (D + 4);
+  const float m0 = r[0], l0rest = r[1], u0_ref = r[2], L0 = r[3];
+  float M2 = m0;
+  for (int k = 1; k < nch; ++k) M2 = fmaxf(M2, part[(k - 1) * (D + 4)]);
+  float f[kPass1MaxChunks];
+  f[0] = __builtin_amdgcn_exp2f(m0 - M2);
+  float l_rest = l0rest * f[0];
+  for (int k = 1; k < nch; ++k) {
+    const float* pk = part + (k - 1) * (D + 4);
+    f[k] = pk[1] > 0.f ? __builtin_amdgcn_exp2f(pk[0] - M2) : 0.f;
+    l_rest += pk[1] * f[k];
+  }
+  const float fu = __builtin_amdgcn_exp2f(u0_ref - M2);
+  const float l_all = L0 * fu + l_rest;
+  const float r_coef = 1.f / l_all, u_coef = fu / l_all;
+  for (int d = lane; d < D; d += 64) {
+    float R = r[4 + D + d] * f[0];
+    for (int k = 1; k < nch; ++k) R += part[(k - 1) * (D + 4) + 4 + d] * f[k];
+    const float rn = R * r_coef;
+    r[4 + d] = __builtin_fmaf(r[4 + d], u_coef, rn);
+    r[4 + D + d] = rn;
+  }
+  if (lane == 0) {  // after every lane has read them
+    r[0] = M2;
+    r[1] = l_all;
+    r[2] = l_rest / l_all;
+  }
+}
 
 template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
@@ -1377,41 +1472,34 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.row_ptr, 0);
     return hipGetLastError();
   }
-  const unsigned grid = (unsigned)((int64_t)items * p.hkv);
-  // Pass 2 chunks: the largest power-of-two chunk (of 16 .. 1024 blocks) that still
-  // gives kP2Workgroups non-empty workgroups. A tile group's sweep is as long as its
-  // last tile, so few long groups (short sequences, or chunks of many queries against
-  // long prefixes) would otherwise leave most CUs idle behind the longest group.
-  SelectParams p2 = p;
-  {
-    auto nonempty = [&](int C) {
-      int64_t n = 0;
-      for (int i = 0; i < p.seqs.num_seqs; ++i)
-        for (int t0 = 0; t0 < p.seqs.n_tiles[i]; t0 += TG) {
-          const int nblk = p.seqs.diag0[i] + min(t0 + TG, p.seqs.n_tiles[i]);
-          n += (nblk + C - 1) / C;
-        }
-      return n * p.hkv;
-    };
-    int C = kP2MaxChunk;
-    while (C > kP2MinChunk && nonempty(C) < kP2Workgroups) C >>= 1;
-    int max_nblk = 1;
-    for (int i = 0; i < p.seqs.num_seqs; ++i)
-      if (p.seqs.n_tiles[i] > 0) max_nblk = max(max_nblk, p.seqs.diag0[i] + p.seqs.n_tiles[i]);
-    p2.p2_chunk_blocks = C;
-    p2.p2_chunks = (max_nblk + C - 1) / C;
-  }
-  const unsigned grid2 = (unsigned)((int64_t)items * p.hkv * p2.p2_chunks);
   const bool mass = p.mode == kSelectMass;
+  SelectParams pp = p;
+  pp.tile_group = TG;
+  pp.sweep_items = items;
+  // pass 1 runs in the chunks the workspace was sized for only in its pipelined form
+  // (bf16, output-relative); pass 2 in chunks of its own choosing
+  if (sizeof(T) != 2 || mass) {
+    pp.p1_chunks = 1;
+    pp.p1_chunk_blocks = kMaxSeqBlocks;
+  }
+  const SweepChunks c2 = sweep_chunks(p.seqs, p.hkv, TG, kMaxSeqBlocks, kPass2Workgroups);
+  pp.p2_chunk_blocks = c2.blocks;
+  pp.p2_chunks = c2.chunks;
+  const unsigned grid1 = (unsigned)((int64_t)items * p.hkv * pp.p1_chunks);
+  const unsigned grid2 = (unsigned)((int64_t)items * p.hkv * pp.p2_chunks);
   if (mass) {
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, true>), dim3(grid), dim3(kSelThreads), 0, s, p);
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid2), dim3(kSelThreads), 0, s, p2);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, true>), dim3(grid1), dim3(kSelThreads), 0, s, pp);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid2), dim3(kSelThreads), 0, s, pp);
   } else {
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid), dim3(kSelThreads), 0, s, p);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid1), dim3(kSelThreads), 0, s, pp);
+    if (pp.p1_chunks > 1) {
+      const int64_t recs = (int64_t)p.hkv * p.seqs.total_tiles * p.cols_rec;
+      hipLaunchKernelGGL(sel_merge_kernel<D>, dim3((unsigned)((recs + 3) / 4)), dim3(256), 0, s, pp);
+    }
     if (sizeof(T) == 2 && p.total_kb > 0)  // the fp16 copy of V that pass 2 reads (bf16 inputs)
       hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
                          p);
-    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid2), dim3(kSelThreads), 0, s, p2);
+    hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, false>), dim3(grid2), dim3(kSelThreads), 0, s, pp);
   }
   // threshold grid: (KV-head unit, head in group) with the unit's XCD kept fixed
   const int64_t units = (int64_t)p.seqs.total_tiles * p.hkv;

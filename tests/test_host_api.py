@@ -63,17 +63,60 @@ def test_geometry_queries(lib):
     assert ws > 0 and ws % 256 == 0
 
 
-def test_select_workspace_holds_fp16_values():
-    """bf16 inputs add an fp16 copy of V (2 bytes per element) and one fp32 scale per
-    (key block, KV head) to the select workspace; fp32 inputs need neither."""
+def _sweep_chunks(seqs, hkv, TG, max_chunks):
+    """The selector's chunking of a sweep: the largest power-of-two chunk of 1024 .. 16
+    blocks giving at least 1024 non-empty workgroups, doubled while a tile group would
+    need more than max_chunks chunks. seqs: [(diag0, n_tiles)]."""
+    mx = max([1] + [d + n for d, n in seqs if n > 0])
+    nonempty = lambda C: hkv * sum(-(-(d + min(t0 + TG, n)) // C) for d, n in seqs for t0 in range(0, n, TG))
+    C = 1024
+    while C > 16 and nonempty(C) < 1024:
+        C //= 2
+    while -(-mx // C) > max_chunks:
+        C *= 2
+    return C, -(-mx // C)
+
+
+def _select_layout_bytes(p, S, group_mode):
+    """Per (KV head, tile) records of 2 d + 4 floats per column; bf16: partial records
+    of pass 1's later chunks (d + 4 floats), the fp16 copy of V and its block scales;
+    per visible (tile, block) I and m per column; per query head counts and slots."""
     a256 = lambda x: -(-x // 256) * 256
-    for kw in (dict(), dict(seqlens_q=[64, 0, 100], seqlens_k=[128, 64, 100]),
-               dict(seqlens_q=[100], seqlens_k=[4196], head_dim=128, block_size=128)):
-        pb, pf = prob(**kw), prob(dtype="fp32", **kw)
-        nk = sum(pb.seqlens_k)
-        kblocks = sum(-(-n // pb.block_size) for n in pb.seqlens_k)
-        extra = a256(2 * nk * pb.num_heads_kv * pb.head_dim) + a256(4 * pb.num_heads_kv * kblocks)
-        assert L.select_workspace_bytes(pb, 8) - L.select_workspace_bytes(pf, 8) == extra, kw
+    B, d, hkv = p.block_size, p.head_dim, p.num_heads_kv
+    G = p.num_heads_q // hkv
+    seqs = [((nk - nq) // B, -(-nq // B)) for nq, nk in zip(p.seqlens_q, p.seqlens_k)]
+    T = sum(n for _, n in seqs)
+    vis = sum(sum(d0 + t + 1 for t in range(n)) for d0, n in seqs)
+    cols = S if group_mode else 32 * (-(-(G * S) // 32))
+    total = a256(4 * hkv * T * cols * (2 * d + 4))
+    if p.dtype == "bf16":
+        TG = 8 * (32 // S) if group_mode else max(1, 8 // (-(-(G * S) // 32)))
+        _, nch = _sweep_chunks(seqs, hkv, TG, 8)
+        total += a256(4 * hkv * T * cols * (nch - 1) * (d + 4))
+    total += a256(4 * hkv * vis * cols * 2) + a256(4 * p.num_heads_q * T) + a256(4 * p.num_heads_q * vis)
+    if p.dtype == "bf16":
+        nk = sum(p.seqlens_k)
+        kblocks = sum(-(-n // B) for n in p.seqlens_k)
+        total += a256(2 * nk * hkv * d) + a256(4 * hkv * kblocks)
+    return total
+
+
+def test_select_workspace_layout():
+    """The select workspace is the larger of the per-head and group-shared layouts; bf16
+    inputs add pass 1's partial records (when its tile groups are split into chunks), an
+    fp16 copy of V and one fp32 scale per (key block, KV head)."""
+    cases = (dict(), dict(seqlens_q=[64, 0, 100], seqlens_k=[128, 64, 100]),
+             dict(seqlens_q=[100], seqlens_k=[4196], head_dim=128, block_size=128),
+             dict(seqlens_q=[128], seqlens_k=[66048], head_dim=64, block_size=64),
+             dict(seqlens_q=[8192] * 2, seqlens_k=[16384, 131072], num_heads_q=32, num_heads_kv=8, head_dim=128,
+                  block_size=128))
+    for kw in cases:
+        for dt in ("bf16", "fp32"):
+            p = prob(dtype=dt, **kw)
+            want = max(_select_layout_bytes(p, 8, True), _select_layout_bytes(p, 8, False))
+            assert L.select_workspace_bytes(p, 8) == want, (kw, dt)
+    # the long-prefix case runs pass 1 in chunks: five of 256 blocks (1032 blocks, one group)
+    assert _sweep_chunks([(1030, 2)], 1, 8, 8) == (256, 5)
 
 
 @pytest.mark.parametrize("kw,status", [
