@@ -77,10 +77,10 @@ def measured_traffic(workload_id):
                    for f in ("poem_device.hpp", "poem_internal.hpp", "attn_fwd.hip"))
     if hashlib.sha256(src).hexdigest() != rec.get("attn_source_sha256"):
         return None
-    k = rec["kernels"].get("void poem::attn_sparse_persistent_kernel<unsigned short, 128, 128>")
-    if k is None:
+    ks = [v for name, v in rec["kernels"].items() if "attn_sparse_persistent_kernel<" in name]
+    if len(ks) != 1:
         return None
-    return k["read_bytes"] + k["write_bytes"]
+    return ks[0]["read_bytes"] + ks[0]["write_bytes"]
 
 
 def unique_bytes(gp, rp, bi, in_bytes, out_bytes):

@@ -77,13 +77,45 @@ def cmd_kernels(d, title, command):
               f"{k['share']:.2f}%")
 
 
+SIMDS = 1024  # 256 CUs x 4 SIMDs
+XCDS = 8      # GRBM_GUI_ACTIVE sums the XCDs' busy cycles
+
+
+def derived(v, dur_ns):
+    """From one dispatch's SQ/GRBM counters: elapsed cycles (GRBM_GUI_ACTIVE / 8), clock
+    (elapsed cycles / the dispatch's own duration), MFMA FLOP (512 per MOPS unit), MFMA
+    busy share (SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x elapsed cycles))."""
+    out = {}
+    el = v.get("GRBM_GUI_ACTIVE", 0.0) / XCDS
+    if el > 0:
+        out["elapsed cycles"] = f"{el:.4g}"
+        if dur_ns > 0:
+            out["clock GHz"] = f"{el / dur_ns:.2f}"
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in v:
+            out["MFMA busy"] = f"{100.0 * v['SQ_VALU_MFMA_BUSY_CYCLES'] / (SIMDS * el):.1f}%"
+    mops = sum(x for c, x in v.items() if c.startswith("SQ_INSTS_VALU_MFMA_MOPS_"))
+    if mops > 0:
+        out["MFMA FLOP"] = f"{512.0 * mops:.4g}"
+        if dur_ns > 0:
+            out["MFMA TFLOP/s"] = f"{512.0 * mops / dur_ns / 1e3:.0f}"
+    return out
+
+
 def cmd_counters(d, title, command):
     per, dur = last_dispatch_counters(d)
     names = sorted({c for v in per.values() for c in v})
-    print(f"# rocprofv3 counters: {title}\n\ncommand: {command}\n\nThe last dispatch of each kernel.\n")
-    print("kernel | dispatch_us | " + " | ".join(names) + "\n" + "---|" * (len(names) + 2))
+    der = {k: derived(v, dur.get(k, 0.0)) for k, v in per.items()}
+    dnames = [n for n in ("MFMA FLOP", "MFMA TFLOP/s", "elapsed cycles", "MFMA busy", "clock GHz")
+              if any(n in x for x in der.values())]
+    print(f"# rocprofv3 counters: {title}\n\ncommand: {command}\n\nThe last dispatch of each kernel "
+          f"(counters serialize the dispatches). Derived: elapsed cycles = GRBM_GUI_ACTIVE / {XCDS}; clock = "
+          f"elapsed cycles / dispatch duration; MFMA FLOP = 512 x MOPS; MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / "
+          f"({SIMDS} SIMDs x elapsed cycles).\n")
+    cols = ["dispatch_us"] + dnames + names
+    print("kernel | " + " | ".join(cols) + "\n" + "---|" * (len(cols) + 1))
     for k, v in per.items():
-        print(f"{k} | {dur.get(k, 0) / 1e3:.1f} | " + " | ".join(f"{v.get(c, 0):.4g}" for c in names))
+        vals = [f"{dur.get(k, 0) / 1e3:.1f}"] + [der[k].get(n, "") for n in dnames] + [f"{v.get(c, 0):.4g}" for c in names]
+        print(f"{k} | " + " | ".join(vals))
 
 
 def _copy_factor(d, counter, nbytes):
