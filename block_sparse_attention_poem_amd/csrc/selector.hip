@@ -1259,30 +1259,61 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   if constexpr (STAGED) {
     // the head's s_t values of I (not for the mass-only ranking) and m per visible block, read with every
     // load of a batch in flight before the first LDS store
-    const int per_tensor = w.n_vis * w.s_t;
-    const int total = NEED_I ? 2 * per_tensor : per_tensor;
-    constexpr int BATCH = 16;
-    for (int base = 0; base < total; base += BATCH * kThrThreads) {
-      float val[BATCH];
+    if (w.S % 4 == 0 && w.s_t % 4 == 0) {
+      // 16-byte pieces: four rows of a block are adjacent in the record and in LDS
+      const int q_per_blk = w.s_t / 4;
+      const int per_tensor = w.n_vis * q_per_blk;
+      const int total = NEED_I ? 2 * per_tensor : per_tensor;
+      constexpr int BATCH = 8;
+      for (int base = 0; base < total; base += BATCH * kThrThreads) {
+        f32x4 val[BATCH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int idx = base + u * kThrThreads + tid;
-        val[u] = 0.f;
-        if (idx < total) {
-          const bool is_m = !NEED_I || idx >= per_tensor;
-          const int r = is_m && NEED_I ? idx - per_tensor : idx;
-          const int b = r / w.s_t, i = r % w.s_t;
-          val[u] = (is_m ? w.Mb : w.Ib)[(int64_t)b * w.bstride + i];
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = base + u * kThrThreads + tid;
+          if (idx < total) {
+            const bool is_m = !NEED_I || idx >= per_tensor;
+            const int r = is_m && NEED_I ? idx - per_tensor : idx;
+            const int b = r / q_per_blk, i = 4 * (r % q_per_blk);
+            val[u] = *reinterpret_cast<const f32x4*>((is_m ? w.Mb : w.Ib) + (int64_t)b * w.bstride + i);
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = base + u * kThrThreads + tid;
+          if (idx < total) {
+            const bool is_m = !NEED_I || idx >= per_tensor;
+            const int r = is_m && NEED_I ? idx - per_tensor : idx;
+            const int b = r / q_per_blk, i = 4 * (r % q_per_blk);
+            *reinterpret_cast<f32x4*>((is_m ? st_m : st_I) + b * w.S + i) = val[u];
+          }
         }
       }
+    } else {
+      const int per_tensor = w.n_vis * w.s_t;
+      const int total = NEED_I ? 2 * per_tensor : per_tensor;
+      constexpr int BATCH = 16;
+      for (int base = 0; base < total; base += BATCH * kThrThreads) {
+        float val[BATCH];
 #pragma unroll
-      for (int u = 0; u < BATCH; ++u) {
-        const int idx = base + u * kThrThreads + tid;
-        if (idx < total) {
-          const bool is_m = !NEED_I || idx >= per_tensor;
-          const int r = is_m && NEED_I ? idx - per_tensor : idx;
-          const int b = r / w.s_t, i = r % w.s_t;
-          (is_m ? st_m : st_I)[b * w.S + i] = val[u];
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = base + u * kThrThreads + tid;
+          val[u] = 0.f;
+          if (idx < total) {
+            const bool is_m = !NEED_I || idx >= per_tensor;
+            const int r = is_m && NEED_I ? idx - per_tensor : idx;
+            const int b = r / w.s_t, i = r % w.s_t;
+            val[u] = (is_m ? w.Mb : w.Ib)[(int64_t)b * w.bstride + i];
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < BATCH; ++u) {
+          const int idx = base + u * kThrThreads + tid;
+          if (idx < total) {
+            const bool is_m = !NEED_I || idx >= per_tensor;
+            const int r = is_m && NEED_I ? idx - per_tensor : idx;
+            const int b = r / w.s_t, i = r % w.s_t;
+            (is_m ? st_m : st_I)[b * w.S + i] = val[u];
+          }
         }
       }
     }
