@@ -353,23 +353,27 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
         del e_m
 
     # practical POEM: latency at a fixed budget, then errors at POEM's per-head keep counts
-    pk = dict(weight=args.practical_weight, presel_fraction=args.practical_presel)
-    r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "practical", steps, **pk)
-    res_p = {"eps": args.mass_eps, "weight": pk["weight"], "presel_fraction": pk["presel_fraction"],
-             "select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
-    eps_p, rpr = matched("practical", **pk)
-    e_pr = errors(rpr)
-    res_p["matched_keep"] = {"keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
-                             "keep_fraction_blocks_practical": float(rpr["row_ptr"][-1].item()) / cap,
-                             "err_poem": out["err_poem"], "err_practical": _err_stats(e_pr, si, tau)}
-    del e_pr
+    res_p = {}
+    if not args.no_practical:
+        pk = dict(weight=args.practical_weight, presel_fraction=args.practical_presel)
+        r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, [args.mass_eps] * H, "practical", steps,
+                                             **pk)
+        res_p = {"eps": args.mass_eps, "weight": pk["weight"], "presel_fraction": pk["presel_fraction"],
+                 "select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap}
+        eps_p, rpr = matched("practical", **pk)
+        e_pr = errors(rpr)
+        res_p["matched_keep"] = {"keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
+                                 "keep_fraction_blocks_practical": float(rpr["row_ptr"][-1].item()) / cap,
+                                 "err_poem": out["err_poem"], "err_practical": _err_stats(e_pr, si, tau)}
+        del e_pr
 
     r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, inp.tau, "group", steps)
     e_g = errors(r, group=True)
     res_g = {"select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap,
              "err_group": _err_stats(e_g, si, tau), "err_poem": out["err_poem"],
              "note": "same per-head thresholds as the headline step; one list per (KV head, tile) from the "
-                     "group's 8 sampled rows, run by poem_sparse_prefill_group; sampled_rows_within_tau is taken "
+                     "group's 8 sampled rows, run by poem_sparse_prefill_group (G even: two heads per workgroup, each "
+                     "K/V stage loaded once for both); sampled_rows_within_tau is taken "
                      "on the per-head selector's rows"}
     del od, e_g
     torch.cuda.empty_cache()
@@ -389,6 +393,7 @@ def main():
     ap.add_argument("--no-legs", action="store_true", help="skip the mass-only and group-shared selector legs")
     ap.add_argument("--no-probe", action="store_true", help="skip the on-card MFMA rate probe")
     ap.add_argument("--no-mass", action="store_true", help="skip the mass-only selector leg")
+    ap.add_argument("--no-practical", action="store_true", help="skip the practical POEM leg")
     ap.add_argument("--mass-eps", type=float, default=0.002,
                     help="omitted-mass budget of the mass-only and practical legs")
     ap.add_argument("--practical-weight", type=float, default=0.5, help="deviation weight of the practical leg")
@@ -559,7 +564,8 @@ def main():
         if res_m:
             res["mass_only"] = res_m
         res["group_shared"] = res_g
-        res["practical"] = res_p
+        if res_p:
+            res["practical"] = res_p
     if not args.no_cpu_baseline:
         log(f"[bench] cpu baseline ({args.cpu_seconds:.0f} s)")
         # the GPU's scores for the parity sample (one more selection, outside the timed steps)

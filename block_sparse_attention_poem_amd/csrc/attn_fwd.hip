@@ -59,9 +59,12 @@ hipError_t noalloc_scratch(void** ptr, size_t* bytes) {
 template <typename T, int D>
 constexpr int attn_waves_per_eu() { return (sizeof(T) == 4 && D == 128) ? 1 : 2; }
 
-template <typename T, int D, int BLK>
+// HEADS: query heads per workgroup (2: two heads of one GQA group walk one list, and
+// each K/V stage is loaded once for both)
+template <typename T, int D, int BLK, int HEADS = 1>
 struct AttnCfg {
-  static constexpr int WAVES = BLK / 32;
+  static constexpr int WAVES_PER_HEAD = BLK / 32;
+  static constexpr int WAVES = HEADS * WAVES_PER_HEAD;
   static constexpr int NT = WAVES * 64;
   using St = Stage<T, D, NT>;
   static constexpr int SUBS = BLK / kStageKeys;
@@ -94,24 +97,27 @@ constexpr float kLazyCap = 4294967296.0f;  // 2^32
 // rule depends only on the tile's data, so every schedule gives the same bits, and on
 // accepted tiles the weights stay below 2^32, far inside the range of the bf16 weights
 // and fp32 sums.
-template <typename T, int D, int BLK, bool SPARSE>
-__device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, int t, char* kb0, char* kb1,
+template <typename T, int D, int BLK, bool SPARSE, int HEADS = 1>
+__device__ __forceinline__ void attn_tile(const AttnParams& p, int h0, int seq, int t, char* kb0, char* kb1,
                                           char* kb2, char* vb0, char* vb1) {
-  using C = AttnCfg<T, D, BLK>;
+  using C = AttnCfg<T, D, BLK, HEADS>;
   using St = typename C::St;
   constexpr int SUBS = C::SUBS;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: the head and the CSR row below are too
   const int jcol = lane & 31, g2 = lane >> 5;
+  const int hw = wave % C::WAVES_PER_HEAD;    // the wave's 32 rows within its head's tile
+  const int h = h0 + wave / C::WAVES_PER_HEAD;  // its query head
   const int gk = h / p.group;
   const int n_q = p.seqs.n_q[seq], n_k = p.seqs.n_k[seq];
   const int diag = p.seqs.diag0[seq] + t;
   const int row0 = t * BLK;
   const int n_rows = min(BLK, n_q - row0);
   const int pos0 = (n_k - n_q) + row0;  // absolute position of the tile's first row
-  const int wrow = 32 * wave + jcol;
+  const int wrow = 32 * hw + jcol;
   const bool row_ok = wrow < n_rows;
   const int my_pos = pos0 + wrow;
-  const int wave_pos_min = pos0 + 32 * wave, wave_pos_max = wave_pos_min + 31;
+  const int wave_pos_min = pos0 + 32 * hw, wave_pos_max = wave_pos_min + 31;
 
   const int64_t qrow = (int64_t)p.seqs.q_start[seq] + row0 + wrow;
   QFrag<T, D> qf;
@@ -385,38 +391,50 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h, int seq, i
     const int mine = __any(ovf) ? 1 : 0;
     if (lane == 0) flags[wave] = mine;
     lds_barrier();
-    int redo = 0;
+    // The decision is per query head (its own waves' marks), so a tile's bits do not
+    // depend on the other head sharing the workgroup; every wave takes part in the
+    // redo's loads and barriers.
+    int redo = 0, redo_any = 0;
 #pragma unroll
-    for (int w = 0; w < C::WAVES; ++w) redo |= flags[w];
-    if (__builtin_amdgcn_readfirstlane(redo) != 0) {
+    for (int w = 0; w < C::WAVES; ++w) {
+      redo_any |= flags[w];
+      if (w / C::WAVES_PER_HEAD == wave / C::WAVES_PER_HEAD) redo |= flags[w];
+    }
+    if (__builtin_amdgcn_readfirstlane(redo_any) != 0) {
       // the exact running max, one stage at a time in the first K and V buffers (rare)
+      const bool mine_redo = HEADS == 1 || __builtin_amdgcn_readfirstlane(redo) != 0;
+      if (mine_redo) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x16{};
-      m_run = -INFINITY;
-      l_run = 0.f;
-      m_use = 0.f;
+        for (int dt = 0; dt < NDT; ++dt) O[dt] = f32x16{};
+        m_run = -INFINITY;
+        l_run = 0.f;
+        m_use = 0.f;
+      }
       for (int it = 0; it < total; ++it) {
         const int key0 = stage_key0(it);
         St::load_k(kbase, row_stride, key0, n_k, tid, kb0, lo);
         St::load_v(vbase, row_stride, key0, n_k, tid, vb0, lo);
         wait_vmem_all();
         lds_barrier();
-        f32x16 S[2];
-        S[0] = St::qk_tile(kb0, qf, 0, lane);
-        S[1] = St::qk_tile(kb0, qf, 1, lane);
-        mask(S, key0);
-        update(S);
-        bf16x8 P[4], unused;
-        float rs = 0.f;
+        if (mine_redo) {
+          f32x16 S[2];
+          S[0] = St::qk_tile(kb0, qf, 0, lane);
+          S[1] = St::qk_tile(kb0, qf, 1, lane);
+          mask(S, key0);
+          update(S);
+          bf16x8 P[4], unused;
+          float rs = 0.f;
 #pragma unroll
-        for (int e = 0; e < 32; ++e) S[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -m_use));
+          for (int e = 0; e < 32; ++e)
+            S[e >> 4][e & 15] = __builtin_amdgcn_exp2f(__builtin_fmaf(S[e >> 4][e & 15], c, -m_use));
 #pragma unroll
-        for (int s4 = 0; s4 < 4; ++s4) {
-          p_step<false>(S, s4, P[s4], unused);
-          rs = row_sum_bf16(P[s4], rs);
+          for (int s4 = 0; s4 < 4; ++s4) {
+            p_step<false>(S, s4, P[s4], unused);
+            rs = row_sum_bf16(P[s4], rs);
+          }
+          l_run += rs;
+          St::pv_packed(vb0, P, O, lane);
         }
-        l_run += rs;
-        St::pv_packed(vb0, P, O, lane);
         lds_barrier();  // every wave is done with the buffers before the next stage loads
       }
     }
@@ -555,9 +573,39 @@ void attn_sparse_persistent_kernel(AttnParams p) {
   }
 }
 
+// Group-shared lists (bf16, G even): one workgroup of eight waves per (KV head, tile,
+// pair of the group's query heads), both heads walking the group's one list, so each
+// K/V stage is loaded into LDS once for the two heads' rows (the heads of a BFLA group
+// share one selection, Section 3.3, and with it the blocks each stage reads). Items
+// come from a queue over (KV head, tile) units that the schedule kernel sorted by list
+// length, longest first, each unit followed by its G / 2 pairs.
+template <typename T, int D, int BLK>
+__global__ __launch_bounds__(BLK * 4) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void attn_sparse_pair_kernel(AttnParams p) {
+  POEM_ATTN_LDS(T, D, BLK)
+  int* item_sh = reinterpret_cast<int*>(kb2);  // as in the kernel above
+  const int n_tiles = p.seqs.total_tiles;
+  const int pairs = p.group / 2;
+  const int n_items = p.hkv * n_tiles * pairs;
+  for (;;) {
+    __syncthreads();
+    if (threadIdx.x == 0) *item_sh = atomicAdd(p.queue, 1);
+    __syncthreads();
+    const int item = __builtin_amdgcn_readfirstlane(*item_sh);
+    __syncthreads();
+    if (item >= n_items) break;
+    const int r = p.order[item / pairs];  // the unit's first-head row, g G T + gtile
+    const int gtile = r % n_tiles;
+    const int h0 = r / n_tiles + 2 * (item % pairs);
+    const int seq = find_seq(p.seqs, gtile);
+    attn_tile<T, D, BLK, true, 2>(p, h0, seq, gtile - p.seqs.tile_start[seq], kb0, kb1, kb2, vb0, vb1);
+  }
+}
+
 // Orders the CSR rows of each KV head by retained count, descending (a counting sort
 // in LDS; one workgroup per KV head, whose rows h*T .. are contiguous), KV heads one
-// after another, and resets the queue head. Pulling rows in this order keeps the
+// after another, and resets the queue head (group_stride: rows from one KV head's first
+// row to the next one's; rows_per_group of them are ordered). Pulling rows in this order keeps the
 // running workgroups on one KV head's K/V at a time (64 MiB at 128K tokens), which
 // the 256 MiB memory-side cache can hold while the rows re-read it. shared_tiles > 0
 // (shared lists): row i of a KV head's block takes the count of its group's first-head
@@ -565,15 +613,16 @@ void attn_sparse_persistent_kernel(AttnParams p) {
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 4097;  // counts are clamped to 4096 for ordering only
 __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const int32_t* __restrict__ row_ptr,
-                                                                       int rows_per_group, int shared_tiles,
+                                                                       int rows_per_group, int group_stride,
+                                                                       int shared_tiles,
                                                                        int32_t* __restrict__ order_all,
                                                                        int32_t* __restrict__ queue) {
   __shared__ int hist[kSchedBins];
   __shared__ int sh[16];
   const int tid = threadIdx.x;
-  const int first = blockIdx.x * rows_per_group;
+  const int first = blockIdx.x * group_stride;  // the KV head's first row
   const int rows = rows_per_group;
-  int32_t* order = order_all + first;
+  int32_t* order = order_all + blockIdx.x * rows_per_group;
   for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
   __syncthreads();
   auto bin = [&](int i) {
@@ -605,13 +654,36 @@ __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const in
   if (blockIdx.x == 0 && tid == 0) *queue = 0;
 }
 
+// Group-shared lists with G even (bf16): (KV head, tile) units ordered by the first
+// head's count, two heads of the group per workgroup.
+template <typename T, int D, int BLK>
+static hipError_t launch_pairs(const AttnParams& p, int64_t rows, hipStream_t stream) {
+  hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
+                     p.seqs.total_tiles, p.num_rows / p.hkv, 0, p.order, p.queue);
+  int dev = 0, cus = 0, per_cu = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e == hipSuccess)
+    e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_sparse_pair_kernel<T, D, BLK>, BLK * 4, 0);
+  if (e != hipSuccess) return e;
+  const int64_t items = rows / 2;
+  const int64_t slots = (int64_t)cus * (per_cu > 0 ? per_cu : 1);
+  hipLaunchKernelGGL((attn_sparse_pair_kernel<T, D, BLK>), dim3((unsigned)(slots < items ? slots : items)),
+                     dim3(BLK * 4), 0, stream, p);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int BLK, bool SPARSE>
 static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   const int64_t grid = (int64_t)p.seqs.total_tiles * p.hq;
   if (grid == 0) return hipSuccess;
+  if constexpr (SPARSE && sizeof(T) == 2) {
+    if (p.queue != nullptr && p.shared && p.group % 2 == 0)
+      return launch_pairs<T, D, BLK>(p, grid, stream);
+  }
   if (SPARSE && p.queue != nullptr) {
     hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
-                       p.num_rows / p.hkv, p.shared ? p.seqs.total_tiles : 0, p.order, p.queue);
+                       p.num_rows / p.hkv, p.num_rows / p.hkv, p.shared ? p.seqs.total_tiles : 0, p.order, p.queue);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
