@@ -10,6 +10,12 @@ from oracle import poem_oracle as O
 # Gates (stated by the method's acceptance criteria; fp32 ones derived in the design doc)
 SCORE_RTOL = 1e-3        # selector scores, relative, floored at tau / n_vis
 MANDATORY_SCORE_RTOL = SCORE_RTOL  # mandatory blocks too (never ranked, but reported)
+SCORE_RTOL_FP32 = 1e-4   # candidate scores with fp32 inputs (fp32 products and weights)
+
+
+def score_rtol(dtype):
+    """The candidate-score gate for an input dtype."""
+    return SCORE_RTOL_FP32 if dtype == "fp32" else SCORE_RTOL
 OUT_ATOL_BF16 = 1e-2     # max-abs output error, bf16 inputs, fp32 accumulation
 OUT_ATOL_FP32 = 1e-4     # fp32 inputs
 LSE_ATOL_BF16 = 1e-3

@@ -334,7 +334,7 @@ def check_selection(w, inp, gp, op, r, which, q, k, v, gpu_dense=None, gpu_spars
         worst_score = max(worst_score, se)
         worst_unfloored = max(worst_unfloored, info.get("unfloored", 0.0))
         worst_mand = max(worst_mand, sm)
-        assert se <= H.SCORE_RTOL, (h, gt, se, info)
+        assert se <= H.score_rtol(w.dtype), (h, gt, se, info)
         assert sm <= H.MANDATORY_SCORE_RTOL, (h, gt, sm)
         assert np.all(scores[h, gt, n_vis:] == -1.0)
         kept = H.retained(rp, bi, h * T + gt)
@@ -505,7 +505,7 @@ def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=No
         worst = max(worst, se)
         worst_unfloored = max(worst_unfloored, info.get("unfloored", 0.0))
         worst_mand = max(worst_mand, sm)
-        assert se <= H.SCORE_RTOL, (h0, gt, se, info)
+        assert se <= H.score_rtol(w.dtype), (h0, gt, se, info)
         assert sm <= H.MANDATORY_SCORE_RTOL, (h0, gt, sm)
         assert np.all(scores[h0, gt, n_vis:] == -1.0)
         assert kept == sorted(kept) and len(set(kept)) == len(kept)
