@@ -300,8 +300,9 @@ poem_status poem_sparse_prefill_noalloc(const poem_problem* problem, const void*
 #define POEM_DENSE_WORKSPACE_BYTES 256
 
 /*
- * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t
- * (dense causal attention, the speedup baseline). out, lse and errors as for
+ * poem_dense_prefill: the same kernel with every tile's full causal list 0 .. T_t:
+ * dense causal attention, the output o the POEM note's deletion error is measured
+ * against (Section 4.1), and the speedup baseline. out, lse and errors as for
  * poem_sparse_prefill.
  *
  *   workspace        nullable device buffer of >= POEM_DENSE_WORKSPACE_BYTES bytes,
