@@ -351,6 +351,29 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
             "eps_per_head": [float("%.4g" % e) for e in eps_m],
             "err_poem": out["err_poem"], "err_mass": _err_stats(e_m, si, tau)}
         del e_m
+        # matched guarantee: each head's budget bisected to the largest for which every
+        # sampled row's output error stays within the head's tau (POEM's guarantee by
+        # construction), then the blocks mass-only needs for it
+        lo, hi = np.full(H, -9.0), np.zeros(H)
+        for _ in range(16):
+            mid = 0.5 * (lo + hi)
+            rr = L.select(gp, q, k, v, list(10.0 ** mid), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
+                          workspace=ws, mode="mass")
+            e = errors(rr)
+            ok = (e[si] <= tau[None, :]).all(dim=0).cpu().numpy()
+            del e
+            lo = np.where(ok, mid, lo)
+            hi = np.where(ok, hi, mid)
+        rg = L.select(gp, q, k, v, list(10.0 ** lo), w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile,
+                      workspace=ws, mode="mass")
+        e_g = errors(rg)
+        res_m["matched_guarantee"] = {
+            "keep_fraction_blocks_poem": float(rp_poem[-1]) / cap,
+            "keep_fraction_blocks_mass": float(rg["row_ptr"][-1].item()) / cap,
+            "eps_per_head": [float("%.4g" % e) for e in 10.0 ** lo],
+            "err_mass": _err_stats(e_g, si, tau),
+            "note": "per head, the largest mass budget (bisected) whose sampled rows all stay within tau"}
+        del e_g
 
     # practical POEM: latency at a fixed budget, then errors at POEM's per-head keep counts
     res_p = {}
@@ -387,6 +410,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", type=int, default=3, help="synthetic workload id (1..5); 3 is the 128K layer")
     ap.add_argument("--sink-offset", type=float, default=None, help="L_s - ln N (default 6)")
+    ap.add_argument("--near-output", type=float, default=0.0,
+                    help="fraction of clusters whose values equal the sink's (default 0: the workload as defined)")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -428,6 +453,8 @@ def main():
     w = synth.WORKLOADS[args.workload]
     if args.sink_offset is not None:
         w = w.with_(sink_offset=args.sink_offset)
+    if args.near_output > 0:
+        w = w.with_(near_output=args.near_output)
     log(f"[bench] generating workload {args.workload}: {w.name}")
     inp = synth.make(w)
     if inp.is_bf16:
@@ -534,6 +561,7 @@ def main():
         "config": {"workload": w.name, "heads_q": w.num_heads_q, "heads_kv": w.num_heads_kv,
                    "head_dim": w.head_dim, "seqlens_k": list(w.seqlens_k), "seqlens_q": list(w.seqlens_q),
                    "block": w.block_size, "rows_per_tile": w.rows_per_tile, "sink_offset": w.sink_offset,
+                   "near_output": w.near_output,
                    "tau": list(w.tau), "mandatory": {"sink_blocks": w.n_sink_blocks,
                                                      "local_blocks": w.n_local_blocks}},
         "latency_ms": {"select": sel_ms, "sparse_attn": sp_ms, "select_plus_sparse": sel_ms + sp_ms,

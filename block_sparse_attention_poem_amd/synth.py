@@ -20,6 +20,11 @@ shapes):
   is ``L_s * sqrt(d) * e_{d-1}`` (zero elsewhere), so with the default
   1/sqrt(d) softmax scale every query gives the sink the logit L_s.
   L_s = ln(N_k) + ``sink_offset`` (default 6).
+* Near-output clusters (``near_output`` = p > 0, off by default): the value offset of
+  the first round(p * n_centers) centres of each KV head is replaced by the sink key's
+  value vector, so their blocks' values sit near the outputs the sink dominates (the
+  situation of the POEM note's three-block example, where a heavy block whose value
+  equals the output costs nothing to drop). Default inputs do not change.
 * Per-head thresholds tau: a fixed value, or uniform on a range per query head.
 * Values are drawn in fp32 and rounded once to bf16 (round to nearest even)
   for bf16 workloads.
@@ -62,6 +67,7 @@ class Workload:
     rows_per_tile: int = 8
     sink_offset: float = 6.0
     seed: int = 0
+    near_output: float = 0.0
 
     def with_(self, **kw) -> "Workload":
         d = dict(self.__dict__)
@@ -149,6 +155,12 @@ def _seq_kv(w: Workload, s: int, g: int, n_k: int):
     k = _rng(w.seed, wid, s, _T_KNOISE, g).standard_normal((n_k, d), dtype=np.float32)
     k += np.float32(3.0) * centers[cj]
     v = _rng(w.seed, wid, s, _T_VNOISE, g).standard_normal((n_k, d), dtype=np.float32)
+    n_near = int(round(w.near_output * w.n_centers))
+    if n_near > 0:  # value offsets of the first n_near centres <- the sink key's value
+        sink_v = v[0] + voff[cj[0]]
+        voff = voff.copy()
+        voff[:n_near] = sink_v
+        v[0] = sink_v - voff[cj[0]]  # the sink's own value is unchanged
     v += voff[cj]
     # sink key at token 0: logit L_s for every query under the 1/sqrt(d) scale
     ls = math.log(n_k) + w.sink_offset
