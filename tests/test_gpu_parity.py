@@ -388,6 +388,36 @@ def test_selector_matches_oracle(case, sink, n_local):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
+NEAR = [
+    # case, share of clusters whose values equal the sink's
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 0.5),
+    ((256, 4096, 8, 2, 128, 128, "bf16", 1), 1.0),
+    ((300, 428, 2, 1, 64, 64, "fp32", 1), 0.5),
+]
+
+
+@pytest.mark.parametrize("case,near", NEAR, ids=lambda x: str(x))
+def test_selector_near_output_values(case, near):
+    """The selector where blocks' values sit at the output (the regime the note's
+    three-block example describes): U_b - L_b o then cancels for heavy blocks, and
+    their small scores must still meet the gate; masks, bounds and errors as above."""
+    w = _small(case, seed=13).with_(near_output=near)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("selector near-output", case, near)
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    if len(which) > 96:
+        which = H.stratified_tiles(op, sorted({0, op.num_heads_q - 1}), per_head=24, seed=13)
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy())
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
 def _scale_value_blocks(inp, w, lo, hi, seed, p_zero=0.0):
     """V with each (key block, KV head) multiplied by 2^k, k uniform on lo..hi: exact in
     bf16, and it spans far more than fp16's range, so the fp16 copy of V that the
