@@ -124,22 +124,21 @@ int64_t total_key_blocks(const Geometry& g) {
   return n;
 }
 
-// Record columns per (KV head, tile): per-head lists pack the G heads' S rows into
-// 32-column tiles; a group-shared list has S columns.
+// Record columns per (KV head, tile): per-head lists hold the G heads' S rows; a
+// group-shared list has S columns.
 int record_columns(const poem_problem* p, int S, bool group_mode) {
   const int G = p->num_heads_q / p->num_heads_kv;
-  return group_mode ? S : 32 * ((G * S + 31) / 32);
+  return group_mode ? S : G * S;
 }
 
 SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S, bool group_mode) {
   SelLayout L;
   const int cols = record_columns(p, S, group_mode);
-  const int G = p->num_heads_q / p->num_heads_kv;
   size_t off = 0;
   L.row_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (2 * p->head_dim + 4));
   if (p->in_dtype == POEM_BF16) {  // pass 1 in chunks: partial records of the chunks after the first
-    const int TG = poem::sel_tile_group(true, (G * S + 31) / 32, group_mode, group_mode ? 32 / S : 1);
+    const int TG = poem::sel_tile_group(true, cols, group_mode, group_mode ? 32 / S : 1);
     L.p1 = poem::sweep_chunks(g.st, p->num_heads_kv, TG, poem::kPass1MaxChunks, poem::kPass1Workgroups);
     L.p1_part = off;
     off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (L.p1.chunks - 1) *
@@ -263,7 +262,6 @@ static poem_status select_impl(int mode, bool group_mode, float prac_w, float pr
   sp.hkv = problem->num_heads_kv;
   sp.group = problem->num_heads_q / problem->num_heads_kv;
   sp.S = rows_per_tile;
-  sp.col_tiles = (sp.group * rows_per_tile + 31) / 32;
   sp.group_mode = group_mode ? 1 : 0;
   sp.cols_rec = cols;
   sp.tiles_per_wave = group_mode ? 32 / rows_per_tile : 1;

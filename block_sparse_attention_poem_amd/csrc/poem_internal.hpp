@@ -50,15 +50,15 @@ struct SelectParams {
   const void* v;
   int32_t hq, hkv, group;
   int32_t S;                 // sampled rows per tile
-  int32_t col_tiles;         // 32-column tiles per (KV head, tile)
   int32_t n_sink, n_local;
   int32_t max_vis;
   int32_t mode;              // kSelectOutputRelative, kSelectMass or kSelectPractical
   float prac_w, prac_rho;    // practical POEM: deviation weight, preselected mass fraction
   // column layout of the per-(KV head, tile) records. Per-head lists: column
-  // f = hg * S + j (row j of head g G + hg), cols_rec = 32 * col_tiles, one tile per
-  // wave. Group-shared lists (group_mode): column j is row j of head g G + j mod G,
-  // cols_rec = S and a wave holds tiles_per_wave = 32 / S tiles.
+  // f = hg * S + j (row j of head g G + hg), cols_rec = G S, the tiles of a sweep
+  // workgroup's group laid end to end over its waves' 32-column tiles. Group-shared
+  // lists (group_mode): column j is row j of head g G + j mod G, cols_rec = S and a
+  // wave holds tiles_per_wave = 32 / S tiles.
   int32_t group_mode;
   int32_t cols_rec;
   int32_t tiles_per_wave;
@@ -92,12 +92,14 @@ hipError_t launch_select(const SelectParams& p, int in_dtype, int head_dim, int 
 
 // Selector sweeps, host side. A sweep workgroup walks the visible blocks of a tile
 // group (TG consecutive tiles of one sequence and KV head): eight waves for bf16 inputs,
-// four for fp32, each wave one 32-column tile, or tiles_per_wave tiles of group-shared
-// lists.
-inline int sel_tile_group(bool bf16, int col_tiles, bool group_mode, int tiles_per_wave) {
+// four for fp32, of 32 columns each. Per-head lists: the group's cols = G S columns per
+// tile, laid end to end over the waves (a wave's 32 columns may span two tiles), so
+// TG = floor(32 waves / cols) tiles and at most cols - 1 columns of the workgroup are
+// idle. Group-shared lists: each wave holds tiles_per_wave tiles of S columns.
+inline int sel_tile_group(bool bf16, int cols, bool group_mode, int tiles_per_wave) {
   const int waves = bf16 ? 8 : 4;
   if (group_mode) return waves * tiles_per_wave;
-  return waves / col_tiles > 1 ? waves / col_tiles : 1;
+  return 32 * waves / cols > 1 ? 32 * waves / cols : 1;
 }
 
 // A long group's blocks can be split into chunks of whole blocks, one workgroup each,

@@ -87,9 +87,8 @@ void sel_sweep_kernel(SelectParams p) {
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
-  const int CT = p.col_tiles;
   const int TPW = p.tiles_per_wave;
-  const int TG = p.group_mode ? kSelWaves * TPW : max(1, kSelWaves / CT);
+  const int TG = p.tile_group;  // tiles per workgroup (sel_tile_group)
 
   const int gk = blockIdx.x % p.hkv;
   // the tile group's visible blocks in chunks of whole blocks, one chunk per workgroup.
@@ -125,13 +124,19 @@ void sel_sweep_kernel(SelectParams p) {
     hg = jr % p.group;
     in_range = jcol < TPW * p.S && t < n_tiles;
   } else {
-    tw0 = tw1 = t = tile0 + wave / CT;
-    col = 32 * (wave % CT) + jcol;
+    // the group's tiles end to end: flattened column F = (t - tile0) C + col, 32 per wave
+    const int C = p.cols_rec;
+    const int F = 32 * wave + jcol;
+    const int F_end = TG * C;  // columns of the workgroup's tiles
+    t = tile0 + F / C;
+    col = F % C;
     hg = col / p.S;
     jr = col % p.S;
-    in_range = wave < TG * CT && t < n_tiles && hg < p.group;
+    in_range = F < F_end && t < n_tiles;
+    tw0 = tile0 + (32 * wave) / C;
+    tw1 = min(tile0 + min(32 * wave + 31, F_end - 1) / C, n_tiles - 1);
   }
-  const bool wave_on = tw0 < n_tiles && (p.group_mode || wave < TG * CT);
+  const bool wave_on = tw0 < n_tiles && (p.group_mode || 32 * wave < TG * p.cols_rec);
   const int diag = diag0 + t;
   const int n_rows_t = in_range ? min(BLK, n_q - t * BLK) : 1;
   const int s_t = min(p.S, n_rows_t);
@@ -1495,7 +1500,7 @@ template <typename T, int D, int BLK>
 static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   constexpr int kSelWaves = sel_threads<T>() / 64;
   constexpr int kSelThreads = sel_threads<T>();
-  const int TG = p.group_mode ? kSelWaves * p.tiles_per_wave : max(1, kSelWaves / p.col_tiles);
+  const int TG = sel_tile_group(sizeof(T) == 2, p.cols_rec, p.group_mode, p.tiles_per_wave);
   int items = 0;
   for (int i = 0; i < p.seqs.num_seqs; ++i) items += (p.seqs.n_tiles[i] + TG - 1) / TG;
   const int64_t rows = (int64_t)p.hq * p.seqs.total_tiles;

@@ -87,10 +87,10 @@ def _select_layout_bytes(p, S, group_mode):
     seqs = [((nk - nq) // B, -(-nq // B)) for nq, nk in zip(p.seqlens_q, p.seqlens_k)]
     T = sum(n for _, n in seqs)
     vis = sum(sum(d0 + t + 1 for t in range(n)) for d0, n in seqs)
-    cols = S if group_mode else 32 * (-(-(G * S) // 32))
+    cols = S if group_mode else G * S
     total = a256(4 * hkv * T * cols * (2 * d + 4))
     if p.dtype == "bf16":
-        TG = 8 * (32 // S) if group_mode else max(1, 8 // (-(-(G * S) // 32)))
+        TG = 8 * (32 // S) if group_mode else max(1, 256 // cols)
         _, nch = _sweep_chunks(seqs, hkv, TG, 8)
         total += a256(4 * hkv * T * cols * (nch - 1) * (d + 4))
     total += a256(4 * hkv * vis * cols * 2) + a256(4 * p.num_heads_q * T) + a256(4 * p.num_heads_q * vis)
