@@ -602,33 +602,47 @@ void attn_sparse_pair_kernel(AttnParams p) {
   }
 }
 
-// Orders the CSR rows of each KV head by retained count, descending (a counting sort
-// in LDS; one workgroup per KV head, whose rows h*T .. are contiguous), KV heads one
-// after another, and resets the queue head (group_stride: rows from one KV head's first
-// row to the next one's; rows_per_group of them are ordered). Pulling rows in this order keeps the
-// running workgroups on one KV head's K/V at a time (64 MiB at 128K tokens), which
-// the 256 MiB memory-side cache can hold while the rows re-read it. shared_tiles > 0
-// (shared lists): row i of a KV head's block takes the count of its group's first-head
-// row, i mod shared_tiles.
+// Orders the CSR rows of each KV head by sequence, longest sequence first, and within
+// a sequence by retained count, descending (a counting sort in LDS; one workgroup per
+// KV head, whose rows h*T .. are contiguous), KV heads one after another, and resets
+// the queue head (group_stride: rows from one KV head's first row to the next one's;
+// rows_per_group of them are ordered). Pulling rows in this order keeps the running
+// workgroups on one KV head's K/V of one sequence at a time (64 MiB at 128K tokens),
+// which the 256 MiB memory-side cache can hold while the rows re-read it (measured on
+// four chunked sequences of 16K-128K keys: 9.51 -> 9.38 ms against the count order
+// alone). shared_tiles > 0 (shared lists): row i of a KV head's block takes the count
+// of its group's first-head row, i mod shared_tiles. Counts are clamped to the bins
+// each sequence gets (4097 / sequences), for ordering only.
 constexpr int kSchedThreads = 1024;
 constexpr int kSchedBins = 4097;  // counts are clamped to 4096 for ordering only
 __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const int32_t* __restrict__ row_ptr,
                                                                        int rows_per_group, int group_stride,
                                                                        int shared_tiles,
                                                                        int32_t* __restrict__ order_all,
-                                                                       int32_t* __restrict__ queue) {
+                                                                       int32_t* __restrict__ queue, SeqTable seqs) {
   __shared__ int hist[kSchedBins];
   __shared__ int sh[16];
+  __shared__ int seq_rank[kMaxSeqs];  // position of each sequence, longest N_k first
   const int tid = threadIdx.x;
   const int first = blockIdx.x * group_stride;  // the KV head's first row
   const int rows = rows_per_group;
   int32_t* order = order_all + blockIdx.x * rows_per_group;
+  const int nseq = seqs.num_seqs;
+  const int per_seq = kSchedBins / nseq;  // count bins of one sequence
   for (int i = tid; i < kSchedBins; i += kSchedThreads) hist[i] = 0;
+  if (tid < nseq) {
+    int rk = 0;
+    for (int s = 0; s < nseq; ++s)
+      rk += (seqs.n_k[s] > seqs.n_k[tid] || (seqs.n_k[s] == seqs.n_k[tid] && s < tid)) ? 1 : 0;
+    seq_rank[tid] = rk;
+  }
   __syncthreads();
   auto bin = [&](int i) {
-    const int r = first + (shared_tiles > 0 ? i % shared_tiles : i);
-    const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), kSchedBins - 1);
-    return kSchedBins - 1 - c;  // longest first
+    const int local = shared_tiles > 0 ? i % shared_tiles : i;
+    const int r = first + local;
+    const int c = min(max(row_ptr[r + 1] - row_ptr[r], 0), per_seq - 1);
+    const int sq = nseq > 1 ? seq_rank[find_seq(seqs, local % seqs.total_tiles)] : 0;
+    return sq * per_seq + (per_seq - 1 - c);  // longest first
   };
   for (int r = tid; r < rows; r += kSchedThreads) atomicAdd(&hist[bin(r)], 1);
   __syncthreads();
@@ -659,7 +673,7 @@ __global__ __launch_bounds__(kSchedThreads) void sparse_schedule_kernel(const in
 template <typename T, int D, int BLK>
 static hipError_t launch_pairs(const AttnParams& p, int64_t rows, hipStream_t stream) {
   hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
-                     p.seqs.total_tiles, p.num_rows / p.hkv, 0, p.order, p.queue);
+                     p.seqs.total_tiles, p.num_rows / p.hkv, 0, p.order, p.queue, p.seqs);
   int dev = 0, cus = 0, per_cu = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
@@ -683,7 +697,8 @@ static hipError_t launch_one(const AttnParams& p, hipStream_t stream) {
   }
   if (SPARSE && p.queue != nullptr) {
     hipLaunchKernelGGL(sparse_schedule_kernel, dim3(p.hkv), dim3(kSchedThreads), 0, stream, p.row_ptr,
-                       p.num_rows / p.hkv, p.num_rows / p.hkv, p.shared ? p.seqs.total_tiles : 0, p.order, p.queue);
+                       p.num_rows / p.hkv, p.num_rows / p.hkv, p.shared ? p.seqs.total_tiles : 0, p.order, p.queue,
+                       p.seqs);
     int dev = 0, cus = 0, per_cu = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
