@@ -11,8 +11,9 @@
 // back to the exact running max when later weights outgrow it (see attn_tile).
 //
 // Work order. Sparse rows: a persistent kernel pulls rows from a queue that a schedule
-// kernel sorts by retained count, one KV head after another (or, without a workspace,
-// one workgroup per row in the static order below). Dense tiles: a persistent kernel
+// kernel sorts one KV head after another, by sequence and then by retained count (or,
+// without a workspace, one workgroup per row in the static order below); lists shared
+// by a GQA group run two heads per workgroup (attn_sparse_pair_kernel). Dense tiles: a persistent kernel
 // walks one KV head after another, longest tile first, pulling from a queue when the
 // caller gives a workspace. Static order: workgroups ranked by the tile's diagonal
 // block, longest first, with the KV head as the fastest-varying index of the

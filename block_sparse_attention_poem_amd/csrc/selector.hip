@@ -2,9 +2,10 @@
 //
 // Columns. For a KV head g and query tile t, the selector's query columns are the
 // sampled rows of the G query heads that share g (BFLA Section 3.3): column
-// f = hg * S + j is row r_j of head g*G + hg. They are packed 32 to a wave, so one
-// K/V fetch serves every head of the group and the MFMA is fully used when
-// G * S = 32 (Llama-3-8B shapes: G = 4, S = 8).
+// f = hg * S + j is row r_j of head g*G + hg. The G S columns of consecutive tiles are
+// laid end to end over a workgroup's waves, 32 to a wave, so one K/V fetch serves every
+// head of the group and at most G S - 1 of a workgroup's columns are idle (none when
+// G S divides 256: Llama-3-8B shapes, G = 4 and S = 8, put one tile on each wave).
 //
 // Pass 1 (sel_sweep_kernel<..., false>): per column, the dense softmax statistics
 //   over all visible keys (c = scale * log2 e): the final running max M2 of c s_j,
