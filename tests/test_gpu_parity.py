@@ -280,6 +280,55 @@ def test_lazy_reference_recomputes_spiked_tiles():
     assert spiked >= 4  # the spikes reach several tiles of both KV heads
 
 
+def test_pair_kernel_redo_is_per_head():
+    """Group-shared lists run two heads of a group per workgroup. A key whose logit
+    exceeds every logit of the first stage by 60 nats for one head of each pair only
+    (that head's queries carry the spike channel, the other's do not) makes that head
+    alone recompute with the exact running max: the two-head kernel's output equals the
+    one-head kernel's bit for bit, under both schedules, and the oracle's."""
+    import dataclasses
+    import torch
+    w = synth.small_workload(n_q=300, n_k=428, hq=4, hkv=2, d=128, block=128, dtype="bf16", seed=23)
+    inp = synth.make(w)
+    q = synth.bf16_bits_to_f32(inp.q).copy()
+    k = synth.bf16_bits_to_f32(inp.k).copy()
+    d = w.head_dim
+    q[:, :, d - 1] = 0.0
+    q[:, 0, d - 1] = 1.0   # group 0: head 0 sees the spike, head 1 does not
+    q[:, 3, d - 1] = 1.0   # group 1: head 3 sees it, head 2 does not
+    k[:, :, d - 1] = 0.0
+    k[300, 0, d - 1] = 60.0 * math.sqrt(d)
+    k[400, 1, d - 1] = 60.0 * math.sqrt(d)
+    inp = dataclasses.replace(inp, q=synth.round_to_bf16_bits(q), k=synth.round_to_bf16_bits(k))
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    tl = O.tiles(op)
+    G = op.group
+    first = {t.gtile: (list(range(t.diag + 1)) if t.gtile % 2 == 0 else sorted({0, 2, t.diag} & set(range(t.diag + 1))))
+             for t in tl}
+    rows = [first[t.gtile] for h in range(op.num_heads_q) for t in tl]
+    rp = np.concatenate([[0], np.cumsum([len(r) for r in rows])]).astype(np.int32)
+    bi = np.array([b for r in rows for b in r] + [0], np.int32)
+    rpd, bid = torch.from_numpy(rp).cuda(), torch.from_numpy(bi).cuda()
+    say("two-head kernel: per-head lazy-reference decisions")
+    g_out, g_lse = L.sparse_prefill_group(gp, qd, kd, vd, rpd, bid, out_dtype="fp32")
+    g_out2, g_lse2 = L.sparse_prefill_group(gp, qd, kd, vd, rpd, bid, out_dtype="fp32", workspace=None)
+    s_out, s_lse = L.sparse_prefill(gp, qd, kd, vd, rpd, bid, out_dtype="fp32")
+    _sync()
+    assert torch.equal(g_out, s_out) and torch.equal(g_lse, s_lse)
+    assert torch.equal(g_out2, s_out) and torch.equal(g_lse2, s_lse)
+    qf, kf, vf = H.f64(inp)
+    ref = O.sparse_prefill(op, qf, kf, vf, rp.astype(np.int64), bi)
+    go, gl = g_out.cpu().numpy(), g_lse.cpu().numpy()
+    spiked = {h: 0 for h in range(op.num_heads_q)}
+    for (h, gt), (Os, ls) in ref.items():
+        r0, n = H.tile_rows(op, gt)
+        assert np.abs(go[r0:r0 + n, h] - Os).max() <= H.OUT_ATOL_BF16, (h, gt)
+        assert H.lse_close(gl[h, r0:r0 + n], ls, H.LSE_ATOL_BF16), (h, gt)
+        spiked[h] += int(ls.max() > 50)
+    assert spiked[0] >= 1 and spiked[3] >= 1 and spiked[1] == 0 and spiked[2] == 0, spiked
+
+
 def test_bf16_output_is_rounded_fp32_output():
     import torch
     w = _small(SMALL[1], seed=4)
