@@ -1444,16 +1444,18 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
   if (tid == 0) p.vscale[(int64_t)g * p.total_kb + kb] = sb;
 }
 
-// Pass 1 in chunks (bf16): one wave per record column combines the chunks' sums into
+// Pass 1 in chunks (bf16): 16 lanes per record column combine the chunks' sums into
 // the record pass 2 reads. With M2 the largest chunk reference and f_k = 2^(m_k - M2):
 // L_rest = sum_k l_k f_k and R = sum_k U_k f_k over every chunk's blocks after block 0,
 // l = L_0 2^(u0_ref - M2) + L_rest, o = (U_0 2^(u0_ref - M2) + R) / l: the sums of the
 // unsplit sweep, each chunk's rescaled once to the common reference.
 template <int D>
 __global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
+  constexpr int kLanes = 16;  // lanes per record column: four columns per wave
   const int T = p.seqs.total_tiles;
-  const int64_t rec = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);  // (KV head * T + gtile) * cols_rec + col
-  const int lane = threadIdx.x & 63;
+  // (KV head * T + gtile) * cols_rec + col
+  const int64_t rec = ((int64_t)blockIdx.x * 256 + threadIdx.x) / kLanes;
+  const int l16 = threadIdx.x % kLanes;
   if (rec >= (int64_t)p.hkv * T * p.cols_rec) return;
   const int col = (int)(rec % p.cols_rec);
   const int gtile = (int)((rec / p.cols_rec) % T);
@@ -1470,27 +1472,36 @@ __global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
   float* r = p.row_stats + rec * kRecordFloats<D>;
   const float* part = p.p1_part + rec * (int64_t)(p.p1_chunks - 1) * (D + 4);
   const float m0 = r[0], l0rest = r[1], u0_ref = r[2], L0 = r[3];
+  // every chunk's (reference, weight sum), loaded together; unrolled so f stays in registers
+  float mk[kPass1MaxChunks], lk[kPass1MaxChunks], f[kPass1MaxChunks];
+#pragma unroll
+  for (int k = 1; k < kPass1MaxChunks; ++k) {
+    mk[k] = k < nch ? part[(k - 1) * (D + 4)] : -INFINITY;
+    lk[k] = k < nch ? part[(k - 1) * (D + 4) + 1] : 0.f;
+  }
   float M2 = m0;
-  for (int k = 1; k < nch; ++k) M2 = fmaxf(M2, part[(k - 1) * (D + 4)]);
-  float f[kPass1MaxChunks];
+#pragma unroll
+  for (int k = 1; k < kPass1MaxChunks; ++k) M2 = fmaxf(M2, mk[k]);
   f[0] = __builtin_amdgcn_exp2f(m0 - M2);
   float l_rest = l0rest * f[0];
-  for (int k = 1; k < nch; ++k) {
-    const float* pk = part + (k - 1) * (D + 4);
-    f[k] = pk[1] > 0.f ? __builtin_amdgcn_exp2f(pk[0] - M2) : 0.f;
-    l_rest += pk[1] * f[k];
+#pragma unroll
+  for (int k = 1; k < kPass1MaxChunks; ++k) {
+    f[k] = lk[k] > 0.f ? __builtin_amdgcn_exp2f(mk[k] - M2) : 0.f;
+    l_rest += lk[k] * f[k];
   }
   const float fu = __builtin_amdgcn_exp2f(u0_ref - M2);
   const float l_all = L0 * fu + l_rest;
   const float r_coef = 1.f / l_all, u_coef = fu / l_all;
-  for (int d = lane; d < D; d += 64) {
+  for (int d = l16; d < D; d += kLanes) {
     float R = r[4 + D + d] * f[0];
-    for (int k = 1; k < nch; ++k) R += part[(k - 1) * (D + 4) + 4 + d] * f[k];
+#pragma unroll
+    for (int k = 1; k < kPass1MaxChunks; ++k)
+      if (k < nch) R += part[(k - 1) * (D + 4) + 4 + d] * f[k];
     const float rn = R * r_coef;
     r[4 + d] = __builtin_fmaf(r[4 + d], u_coef, rn);
     r[4 + D + d] = rn;
   }
-  if (lane == 0) {  // after every lane has read them
+  if (l16 == 0) {  // after the column's lanes have read them (they run in one wave)
     r[0] = M2;
     r[1] = l_all;
     r[2] = l_rest / l_all;
@@ -1531,7 +1542,7 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid1), dim3(kSelThreads), 0, s, pp);
     if (pp.p1_chunks > 1) {
       const int64_t recs = (int64_t)p.hkv * p.seqs.total_tiles * p.cols_rec;
-      hipLaunchKernelGGL(sel_merge_kernel<D>, dim3((unsigned)((recs + 3) / 4)), dim3(256), 0, s, pp);
+      hipLaunchKernelGGL(sel_merge_kernel<D>, dim3((unsigned)((recs + 15) / 16)), dim3(256), 0, s, pp);
     }
     if (sizeof(T) == 2 && p.total_kb > 0)  // the fp16 copy of V that pass 2 reads (bf16 inputs)
       hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
