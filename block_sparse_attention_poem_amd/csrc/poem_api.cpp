@@ -114,7 +114,7 @@ size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 struct SelLayout {
   size_t row_stats = 0, p1_part = 0, blk_stats = 0, counts = 0, slots = 0, v16 = 0, vscale = 0, total = 0;
-  poem::SweepChunks p1 = {0, 1};  // pass 1 chunks (bf16 inputs)
+  poem::SweepChunks p1 = {0, 1};  // pass 1 chunks
 };
 
 // key blocks over all sequences (ceil(N_k / B) each)
@@ -137,8 +137,8 @@ SelLayout sel_layout(const poem_problem* p, const Geometry& g, int S, bool group
   size_t off = 0;
   L.row_stats = off;
   off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (2 * p->head_dim + 4));
-  if (p->in_dtype == POEM_BF16) {  // pass 1 in chunks: partial records of the chunks after the first
-    const int TG = poem::sel_tile_group(true, cols, group_mode, group_mode ? 32 / S : 1);
+  {  // pass 1 in chunks: partial records of the chunks after the first
+    const int TG = poem::sel_tile_group(p->in_dtype == POEM_BF16, cols, group_mode, group_mode ? 32 / S : 1);
     L.p1 = poem::sweep_chunks(g.st, p->num_heads_kv, TG, poem::kPass1MaxChunks, poem::kPass1Workgroups);
     L.p1_part = off;
     off += align256(sizeof(float) * (size_t)p->num_heads_kv * g.num_tiles * cols * (L.p1.chunks - 1) *

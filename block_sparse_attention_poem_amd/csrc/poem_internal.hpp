@@ -108,7 +108,7 @@ inline int sel_tile_group(bool bf16, int cols, bool group_mode, int tiles_per_wa
 // `target` non-empty workgroups, then doubled while a group would need more than
 // max_chunks chunks.
 constexpr int kSweepMaxChunk = 1024;
-constexpr int kSweepMinChunk = 16;
+constexpr int kSweepMinChunk = 1;
 constexpr int64_t kPass1Workgroups = 1024;
 constexpr int64_t kPass2Workgroups = 1024;
 struct SweepChunks {

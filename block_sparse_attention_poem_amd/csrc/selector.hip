@@ -663,6 +663,46 @@ void sel_sweep_kernel(SelectParams p) {
           *reinterpret_cast<f32x4*>(po + D) = rn;
         }
     }
+  } else if (!PASS2 && n_chunks > 1) {
+    // one chunk, without block 0 split off: the chunk's raw sums at its own reference,
+    // in the layout of the split sweep's chunks with L_0 = 0 and U_0 = 0 (chunk 0's
+    // record: reference, L, u0_ref = the reference, L_0, U_0 in the o slot, U in the
+    // R / l slot; a later chunk's partial record: reference or -inf, L, U)
+    const float l_c = half_sum(l_run);
+    if (col_on) {
+      float* vdst;
+      if (chunk == 0) {
+        if (g2 == 0) {
+          rs_col[0] = m_run;
+          rs_col[1] = l_c;
+          rs_col[2] = m_run;
+          rs_col[3] = 0.f;
+        }
+        if constexpr (!MASS) {
+#pragma unroll
+          for (int e = 0; e < D / 32 * 4; ++e)
+            *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * (e / 4) + 8 * (e % 4) + 4 * g2) = f32x4{0.f, 0.f, 0.f, 0.f};
+        }
+        vdst = rs_col + 4 + D;
+      } else {
+        float* part = p.p1_part + ((((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + col) * (n_chunks - 1) +
+                                   (chunk - 1)) * (D + 4);
+        if (g2 == 0) {
+          part[0] = l_c > 0.f ? m_run : -INFINITY;
+          part[1] = l_c;
+        }
+        vdst = part + 4;
+      }
+      if constexpr (!MASS) {
+#pragma unroll
+        for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+          for (int a = 0; a < 4; ++a) {
+            const f32x4 u = {O[dt][4 * a], O[dt][4 * a + 1], O[dt][4 * a + 2], O[dt][4 * a + 3]};
+            *reinterpret_cast<f32x4*>(vdst + 32 * dt + 8 * a + 4 * g2) = u;
+          }
+      }
+    }
   } else if constexpr (!PASS2) {
     const float l_tot = half_sum(l_run);
     if (col_on) {
@@ -1444,11 +1484,13 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
   if (tid == 0) p.vscale[(int64_t)g * p.total_kb + kb] = sb;
 }
 
-// Pass 1 in chunks (bf16): 16 lanes per record column combine the chunks' sums into
-// the record pass 2 reads. With M2 the largest chunk reference and f_k = 2^(m_k - M2):
+// Pass 1 in chunks: 16 lanes per record column combine the chunks' sums into the
+// record pass 2 reads. With M2 the largest chunk reference and f_k = 2^(m_k - M2):
 // L_rest = sum_k l_k f_k and R = sum_k U_k f_k over every chunk's blocks after block 0,
 // l = L_0 2^(u0_ref - M2) + L_rest, o = (U_0 2^(u0_ref - M2) + R) / l: the sums of the
-// unsplit sweep, each chunk's rescaled once to the common reference.
+// unsplit sweep, each chunk's rescaled once to the common reference. Sweeps that do not
+// split off block 0 (fp32, mass-only) leave L_0 = 0 and U_0 = 0; mass-only records hold
+// no vectors.
 template <int D>
 __global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
   constexpr int kLanes = 16;  // lanes per record column: four columns per wave
@@ -1492,7 +1534,8 @@ __global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
   const float fu = __builtin_amdgcn_exp2f(u0_ref - M2);
   const float l_all = L0 * fu + l_rest;
   const float r_coef = 1.f / l_all, u_coef = fu / l_all;
-  for (int d = l16; d < D; d += kLanes) {
+  const int dv = p.mode == kSelectMass ? 0 : D;
+  for (int d = l16; d < dv; d += kLanes) {
     float R = r[4 + D + d] * f[0];
 #pragma unroll
     for (int k = 1; k < kPass1MaxChunks; ++k)
@@ -1524,26 +1567,22 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   SelectParams pp = p;
   pp.tile_group = TG;
   pp.sweep_items = items;
-  // pass 1 runs in the chunks the workspace was sized for only in its pipelined form
-  // (bf16, output-relative); pass 2 in chunks of its own choosing
-  if (sizeof(T) != 2 || mass) {
-    pp.p1_chunks = 1;
-    pp.p1_chunk_blocks = kMaxSeqBlocks;
-  }
+  // pass 1 runs in the chunks the workspace was sized for, pass 2 in chunks of its own
+  // choosing
   const SweepChunks c2 = sweep_chunks(p.seqs, p.hkv, TG, kMaxSeqBlocks, kPass2Workgroups);
   pp.p2_chunk_blocks = c2.blocks;
   pp.p2_chunks = c2.chunks;
   const unsigned grid1 = (unsigned)((int64_t)items * p.hkv * pp.p1_chunks);
   const unsigned grid2 = (unsigned)((int64_t)items * p.hkv * pp.p2_chunks);
+  const int64_t recs = (int64_t)p.hkv * p.seqs.total_tiles * p.cols_rec;
+  const dim3 merge_grid((unsigned)((recs + 15) / 16));
   if (mass) {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, true>), dim3(grid1), dim3(kSelThreads), 0, s, pp);
+    if (pp.p1_chunks > 1) hipLaunchKernelGGL(sel_merge_kernel<D>, merge_grid, dim3(256), 0, s, pp);
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, true, true>), dim3(grid2), dim3(kSelThreads), 0, s, pp);
   } else {
     hipLaunchKernelGGL((sel_sweep_kernel<T, D, BLK, false, false>), dim3(grid1), dim3(kSelThreads), 0, s, pp);
-    if (pp.p1_chunks > 1) {
-      const int64_t recs = (int64_t)p.hkv * p.seqs.total_tiles * p.cols_rec;
-      hipLaunchKernelGGL(sel_merge_kernel<D>, dim3((unsigned)((recs + 15) / 16)), dim3(256), 0, s, pp);
-    }
+    if (pp.p1_chunks > 1) hipLaunchKernelGGL(sel_merge_kernel<D>, merge_grid, dim3(256), 0, s, pp);
     if (sizeof(T) == 2 && p.total_kb > 0)  // the fp16 copy of V that pass 2 reads (bf16 inputs)
       hipLaunchKernelGGL((v16_kernel<D, BLK>), dim3((unsigned)((int64_t)p.total_kb * p.hkv)), dim3(kV16Threads), 0, s,
                          p);

@@ -64,13 +64,13 @@ def test_geometry_queries(lib):
 
 
 def _sweep_chunks(seqs, hkv, TG, max_chunks):
-    """The selector's chunking of a sweep: the largest power-of-two chunk of 1024 .. 16
+    """The selector's chunking of a sweep: the largest power-of-two chunk of 1024 .. 1
     blocks giving at least 1024 non-empty workgroups, doubled while a tile group would
     need more than max_chunks chunks. seqs: [(diag0, n_tiles)]."""
     mx = max([1] + [d + n for d, n in seqs if n > 0])
     nonempty = lambda C: hkv * sum(-(-(d + min(t0 + TG, n)) // C) for d, n in seqs for t0 in range(0, n, TG))
     C = 1024
-    while C > 16 and nonempty(C) < 1024:
+    while C > 1 and nonempty(C) < 1024:
         C //= 2
     while -(-mx // C) > max_chunks:
         C *= 2
@@ -78,9 +78,10 @@ def _sweep_chunks(seqs, hkv, TG, max_chunks):
 
 
 def _select_layout_bytes(p, S, group_mode):
-    """Per (KV head, tile) records of 2 d + 4 floats per column; bf16: partial records
-    of pass 1's later chunks (d + 4 floats), the fp16 copy of V and its block scales;
-    per visible (tile, block) I and m per column; per query head counts and slots."""
+    """Per (KV head, tile) records of 2 d + 4 floats per column; partial records of
+    pass 1's later chunks (d + 4 floats); per visible (tile, block) I and m per column;
+    per query head counts and slots; bf16: the fp16 copy of V and its block scales.
+    Selector workgroups hold 8 waves of 32 columns for bf16, 4 for fp32."""
     a256 = lambda x: -(-x // 256) * 256
     B, d, hkv = p.block_size, p.head_dim, p.num_heads_kv
     G = p.num_heads_q // hkv
@@ -89,10 +90,10 @@ def _select_layout_bytes(p, S, group_mode):
     vis = sum(sum(d0 + t + 1 for t in range(n)) for d0, n in seqs)
     cols = S if group_mode else G * S
     total = a256(4 * hkv * T * cols * (2 * d + 4))
-    if p.dtype == "bf16":
-        TG = 8 * (32 // S) if group_mode else max(1, 256 // cols)
-        _, nch = _sweep_chunks(seqs, hkv, TG, 8)
-        total += a256(4 * hkv * T * cols * (nch - 1) * (d + 4))
+    waves = 8 if p.dtype == "bf16" else 4
+    TG = waves * (32 // S) if group_mode else max(1, 32 * waves // cols)
+    _, nch = _sweep_chunks(seqs, hkv, TG, 8)
+    total += a256(4 * hkv * T * cols * (nch - 1) * (d + 4))
     total += a256(4 * hkv * vis * cols * 2) + a256(4 * p.num_heads_q * T) + a256(4 * p.num_heads_q * vis)
     if p.dtype == "bf16":
         nk = sum(p.seqlens_k)
@@ -102,9 +103,9 @@ def _select_layout_bytes(p, S, group_mode):
 
 
 def test_select_workspace_layout():
-    """The select workspace is the larger of the per-head and group-shared layouts; bf16
-    inputs add pass 1's partial records (when its tile groups are split into chunks), an
-    fp16 copy of V and one fp32 scale per (key block, KV head)."""
+    """The select workspace is the larger of the per-head and group-shared layouts, with
+    pass 1's partial records when its tile groups are split into chunks; bf16 inputs add
+    an fp16 copy of V and one fp32 scale per (key block, KV head)."""
     cases = (dict(), dict(seqlens_q=[64, 0, 100], seqlens_k=[128, 64, 100]),
              dict(seqlens_q=[100], seqlens_k=[4196], head_dim=128, block_size=128),
              dict(seqlens_q=[128], seqlens_k=[66048], head_dim=64, block_size=64),
@@ -117,6 +118,11 @@ def test_select_workspace_layout():
             assert L.select_workspace_bytes(p, 8) == want, (kw, dt)
     # the long-prefix case runs pass 1 in chunks: five of 256 blocks (1032 blocks, one group)
     assert _sweep_chunks([(1030, 2)], 1, 8, 8) == (256, 5)
+    # a small problem goes down to one-block chunks for pass 2 (the single-head 2K
+    # workload: 32 tiles of 64 rows, 16 tiles per fp32 workgroup), four-block chunks
+    # for pass 1 (at most eight chunks per group)
+    assert _sweep_chunks([(0, 32)], 1, 16, 4096) == (1, 32)
+    assert _sweep_chunks([(0, 32)], 1, 16, 8) == (4, 8)
 
 
 @pytest.mark.parametrize("kw,status", [
