@@ -186,7 +186,9 @@ def parity_sample(sels, inp, gp, rp, bi, gpu_scores):
 
 
 def mfma_probe():
-    """On-card bf16 MFMA rate (libpoem_probe.so): MFMA-only waves, two per SIMD."""
+    """On-card bf16 MFMA rate (libpoem_probe.so): MFMA-only waves, two per SIMD, on
+    constant few-bit operands and on random operands that change from one MFMA to the
+    next (as a kernel streaming real K and V sees them)."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "block_sparse_attention_poem_amd", "libpoem_probe.so")
@@ -195,26 +197,41 @@ def mfma_probe():
     lib = ctypes.CDLL(path)
     lib.poem_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_void_p]
     lib.poem_probe_mfma_bf16.restype = ctypes.c_double
+    lib.poem_probe_mfma_bf16_random.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_uint32,
+                                                ctypes.c_void_p]
+    lib.poem_probe_mfma_bf16_random.restype = ctypes.c_double
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    blocks, iters = 2 * cus, 40000
+    blocks = 2 * cus
     sink = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
     st = torch.cuda.current_stream()
-    best = 0.0
-    for i in range(4):
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(st)
-        flop = lib.poem_probe_mfma_bf16(ctypes.c_void_p(sink.data_ptr()), blocks, iters,
-                                        ctypes.c_void_p(st.cuda_stream))
-        e1.record(st)
-        torch.cuda.synchronize()
-        if flop < 0:
-            return None
-        if i > 0:  # the first launch warms the clock up
-            best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+
+    def rate(launch):
+        best = 0.0
+        for i in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(st)
+            flop = launch()
+            e1.record(st)
+            torch.cuda.synchronize()
+            if flop < 0:
+                return None
+            if i > 0:  # the first launch warms the clock up
+                best = max(best, flop / (e0.elapsed_time(e1) * 1e-3) / 1e12)
+        return best
+
+    sp, sv = ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st.cuda_stream)
+    const = rate(lambda: lib.poem_probe_mfma_bf16(sp, blocks, 40000, sv))
+    rand = rate(lambda: lib.poem_probe_mfma_bf16_random(sp, blocks, 20000, 12345, sv))
     del sink
-    return {"achieved_tflops": best, "quoted_peak_tflops": PEAK_BF16_TFLOPS, "frac_of_quoted": best / PEAK_BF16_TFLOPS,
-            "implied_clock_ghz": best * 1e12 / (cus * 4096) / 1e9, "compute_units": cus,
-            "kernel": "v_mfma_f32_32x32x16_bf16 chains on registers, 2 waves per SIMD, no memory traffic"}
+    if const is None or rand is None:
+        return None
+    clock = lambda tf: tf * 1e12 / (cus * 4096) / 1e9
+    return {"achieved_tflops": const, "quoted_peak_tflops": PEAK_BF16_TFLOPS, "frac_of_quoted": const / PEAK_BF16_TFLOPS,
+            "implied_clock_ghz": clock(const), "compute_units": cus,
+            "kernel": "v_mfma_f32_32x32x16_bf16 chains on registers, 2 waves per SIMD, no memory traffic",
+            "random_operands": {"achieved_tflops": rand, "frac_of_quoted": rand / PEAK_BF16_TFLOPS,
+                                "implied_clock_ghz": clock(rand),
+                                "operands": "8 pairs per wave of random sign and mantissa, rotated every MFMA"}}
 
 
 def selector_streaming(gp, w, t_sel_ms, workload_id):
