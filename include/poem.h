@@ -90,11 +90,11 @@ int64_t poem_max_visible_blocks(const poem_problem* problem);
 
 /* Bytes of device workspace the selectors need (256-byte aligned start): enough for
  * poem_select, poem_select_mass, poem_select_practical and poem_select_group at this
- * rows_per_tile; < 0 on error. It holds per-row softmax statistics, per-block masses
- * and scores, retained-id slots and, for bf16 inputs, an fp16 copy of V (the size of
- * V) with one scale per (key block, KV head) for the second pass, and partial
- * statistics when the first pass splits long tile groups into block chunks (problems
- * with too few tile groups to fill the GPU otherwise). */
+ * rows_per_tile; < 0 on error. It holds per-row softmax statistics, partial
+ * statistics when the first pass splits tile groups into block chunks (problems with
+ * too few tile groups to fill the GPU otherwise), per-block masses and scores,
+ * retained-id slots and, for bf16 inputs, an fp16 copy of V (the size of V) with one
+ * scale per (key block, KV head) for the second pass. */
 int64_t poem_select_workspace_bytes(const poem_problem* problem, int32_t rows_per_tile);
 
 /*
