@@ -556,6 +556,31 @@ def test_mass_selector_matches_oracle(case, sink, n_local, eps):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst mass rel err", ws)
 
 
+@pytest.mark.parametrize("dt,d", [("fp32", 64), ("bf16", 128)])
+def test_selector_unsplit_sweeps(dt, d):
+    """64 one-tile sequences x 16 KV heads: 1024 tile groups, enough that no sweep is
+    split into block chunks, so the single-chunk epilogues of pass 1 run (small problems
+    otherwise always split). POEM and mass-only selectors against the oracle."""
+    case = (64, 128, 16, 16, d, 64, dt, 1)
+    w = _small(case, seed=11).with_(seqlens_q=tuple([64] * 64),
+                                    seqlens_k=tuple(64 + 64 * (i % 4) for i in range(64)), sink_offset=6.0)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    for mode, taus in (("poem", None), ("mass", [0.002 * (1 + 0.5 * (h % 3)) for h in range(w.num_heads_q)])):
+        say("unsplit sweeps", dt, d, mode)
+        r = L.select(gp, qd, kd, vd, inp.tau if taus is None else taus, w.n_sink_blocks, w.n_local_blocks,
+                     w.rows_per_tile, diagnostics=True, mode=mode)
+        s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+        _sync()
+        nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy(),
+                                     mode=mode, taus=taus)
+        say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
 def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=None, gpu_sparse=None):
     """poem_select_group against the oracle's group selection on (KV head, gtile) units:
     group scores, the shared list under every head, masks with exemptions, and for
