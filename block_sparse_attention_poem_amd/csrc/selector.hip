@@ -9,9 +9,9 @@
 //
 // Pass 1 (sel_sweep_kernel<..., false>): per column, the dense softmax statistics
 //   over all visible keys (c = scale * log2 e): the final running max M2 of c s_j,
-//   l = sum_j 2^(c s_j - M2) and o = sum_j 2^(c s_j - M2) v_j / l. bf16 inputs: block 0's
-//   sums are kept apart while they are formed, and the record also holds R / l and
-//   L_rest / l, with R = sum_j w_j v_j and L_rest = sum_j w_j over the keys after block 0.
+//   l = sum_j 2^(c s_j - M2) and o = sum_j 2^(c s_j - M2) v_j / l. Block 0's sums are
+//   kept apart while they are formed, and the record also holds R / l and L_rest / l,
+//   with R = sum_j w_j v_j and L_rest = sum_j w_j over the keys after block 0.
 // Pass 2 (sel_sweep_kernel<..., true>): per column and visible block b, with the
 //   same weights w_j = 2^(c s_j - M2): L_b = sum_{j in b} w_j, U_b = sum_{j in b} w_j v_j,
 //   then m_b = L_b / l and I_b = ||U_b - L_b o|| / l (= ||u_b - m_b o||; a cross-lane
@@ -61,8 +61,8 @@ template <typename T> constexpr int sel_threads() { return sizeof(T) == 2 ? 512 
 template <bool B> struct BoolTag { static constexpr bool value = B; };
 constexpr int kMaxSeqBlocks = 4096;  // key blocks a tile may see (POEM_MAX_VISIBLE_BLOCKS)
 // Per-column record of pass 1: M2, l, L_rest / l, pad, o[D], R / l [D], where R and
-// L_rest sum w_j v_j and w_j over the keys after block 0 (bf16 inputs; pass 2 forms
-// block 0's I from them, see the file header).
+// L_rest sum w_j v_j and w_j over the keys after block 0 (output-relative selectors;
+// pass 2 forms block 0's I from them, see the file header).
 template <int D> constexpr int kRecordFloats = 2 * D + 4;
 // fp16 P V of pass 2: weights carry 2^14 (log2 and inverse)
 constexpr float kP16Log2 = 14.f;
@@ -83,8 +83,9 @@ void sel_sweep_kernel(SelectParams p) {
   constexpr bool PIPE = St::ASYNC && !MASS && !PASS2;
   // bf16 pass 2 of the output-relative selectors: P V on fp16 (see the file header)
   constexpr bool F16PV = St::ASYNC && PASS2 && !MASS;
-  // bf16 pass 1 keeps block 0's sums apart from the rest (see the file header)
-  constexpr bool SPLIT0 = PIPE;
+  // pass 1 of the output-relative selectors keeps block 0's sums apart from the rest
+  // (see the file header)
+  constexpr bool SPLIT0 = !MASS && !PASS2;
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int jcol = lane & 31, g2 = lane >> 5;
@@ -201,8 +202,8 @@ void sel_sweep_kernel(SelectParams p) {
         for (int e = 0; e < 4; ++e) o[dt][4 * a + e] = v4[e];
       }
   };
-  // pass 2 holds o, except that the bf16 pass holds R / l while it forms block 0
-  if constexpr (PASS2 && !MASS && !PIPE) load_vec(Od, (F16PV && blk_lo == 0) ? 4 + D : 4);
+  // pass 2 holds o, except that it holds R / l while it forms block 0
+  if constexpr (PASS2 && !MASS && !PIPE) load_vec(Od, blk_lo == 0 ? 4 + D : 4);
   // per (KV head, tile, visible block): I of the record's columns, then m of them, so
   // a wave's per-block results are one coalesced store each per tile
   float* blk_I = nullptr;
@@ -227,7 +228,7 @@ void sel_sweep_kernel(SelectParams p) {
   // fp16 P V: the weights and U carry 2^14 and U also the block's V scale s_b;
   // U - L o is formed at that scale, with L the sum of the same fp16 weights (which
   // also gives m_b = L / l)
-  // For block 0 of the fp16 pass, o holds R / l and U - L o is formed as
+  // For block 0, o holds R / l and U - L o is formed as
   // U L_rest / l - L R / l: the same vector (o = (U + R) / l, l = L + L_rest), without
   // the cancellation between U and L o when block 0 holds nearly all of the mass.
   auto finalize_block = [&](int blk, const f32x16 (&o)[D / 32]) {
@@ -254,7 +255,7 @@ void sel_sweep_kernel(SelectParams p) {
             ss = __builtin_fmaf(dv, dv, ss);
           }
       };
-      if (F16PV && blk == 0) norm(BoolTag<true>{});
+      if (blk == 0) norm(BoolTag<true>{});
       else norm(BoolTag<false>{});
       ss = half_sum(ss);
     }
@@ -588,15 +589,36 @@ void sel_sweep_kernel(SelectParams p) {
           }
       }
       if constexpr (!MASS) St::template pv<SPLIT>(cur, S, O, lane);
+      if constexpr (SPLIT0) {
+        if (it == SUBS - 1) {
+          // block 0 is complete (every wave computes it): its sums U_0 (in the record's
+          // o slot) and L_0 are kept apart, at the reference they were formed with, and
+          // O and l restart for the blocks after it, as in the pipelined sweep
+          u0_ref = (m_run == -INFINITY) ? 0.f : m_run;
+          l0_run = l_run;
+          l_run = 0.f;
+#pragma unroll
+          for (int dt = 0; dt < D / 32; ++dt) {
+#pragma unroll
+            for (int a = 0; a < 4; ++a) {
+              const f32x4 u = {O[dt][4 * a], O[dt][4 * a + 1], O[dt][4 * a + 2], O[dt][4 * a + 3]};
+              if (col_on) *reinterpret_cast<f32x4*>(rs_col + 4 + 32 * dt + 8 * a + 4 * g2) = u;
+            }
+            O[dt] = f32x16{};
+          }
+        }
+      }
     }
     if constexpr (PASS2) {
       // lanes l and l ^ 32 hold the same column, so the pair takes the branch together
       if (sub == SUBS - 1 && in_range && blk <= diag) finalize_block(blk, Od);
-      if constexpr (F16PV) {
+      if constexpr (!MASS) {
         if (sub == SUBS - 1 && blk == 0) load_vec(Od, 4);  // o for the other blocks
       }
     }
   });
+  // the reference O and l were last formed at
+  if constexpr (!PASS2) m_ref = (m_run == -INFINITY) ? 0.f : m_run;
   }
 
   if (!PASS2 && SPLIT0 && n_chunks > 1) {
@@ -664,18 +686,17 @@ void sel_sweep_kernel(SelectParams p) {
         }
     }
   } else if (!PASS2 && n_chunks > 1) {
-    // one chunk, without block 0 split off: the chunk's raw sums at its own reference,
-    // in the layout of the split sweep's chunks with L_0 = 0 and U_0 = 0 (chunk 0's
-    // record: reference, L, u0_ref = the reference, L_0, U_0 in the o slot, U in the
-    // R / l slot; a later chunk's partial record: reference or -inf, L, U)
+    // mass-only, one chunk: the chunk's raw weight sum at its own reference, in the
+    // layout of the split sweep's chunks with L_0 = 0 (chunk 0's record: reference, L,
+    // u0_ref = the reference, L_0; a later chunk's partial record: reference or -inf, L)
     const float l_c = half_sum(l_run);
     if (col_on) {
       float* vdst;
       if (chunk == 0) {
         if (g2 == 0) {
-          rs_col[0] = m_run;
+          rs_col[0] = m_ref;
           rs_col[1] = l_c;
-          rs_col[2] = m_run;
+          rs_col[2] = m_ref;
           rs_col[3] = 0.f;
         }
         if constexpr (!MASS) {
@@ -688,7 +709,7 @@ void sel_sweep_kernel(SelectParams p) {
         float* part = p.p1_part + ((((int64_t)gk * p.seqs.total_tiles + gtile) * p.cols_rec + col) * (n_chunks - 1) +
                                    (chunk - 1)) * (D + 4);
         if (g2 == 0) {
-          part[0] = l_c > 0.f ? m_run : -INFINITY;
+          part[0] = l_c > 0.f ? m_ref : -INFINITY;
           part[1] = l_c;
         }
         vdst = part + 4;
@@ -1488,9 +1509,8 @@ __global__ __launch_bounds__(kV16Threads) void v16_kernel(SelectParams p) {
 // record pass 2 reads. With M2 the largest chunk reference and f_k = 2^(m_k - M2):
 // L_rest = sum_k l_k f_k and R = sum_k U_k f_k over every chunk's blocks after block 0,
 // l = L_0 2^(u0_ref - M2) + L_rest, o = (U_0 2^(u0_ref - M2) + R) / l: the sums of the
-// unsplit sweep, each chunk's rescaled once to the common reference. Sweeps that do not
-// split off block 0 (fp32, mass-only) leave L_0 = 0 and U_0 = 0; mass-only records hold
-// no vectors.
+// unsplit sweep, each chunk's rescaled once to the common reference. The mass-only
+// sweeps, which do not split off block 0, leave L_0 = 0 and hold no vectors.
 template <int D>
 __global__ __launch_bounds__(256) void sel_merge_kernel(SelectParams p) {
   constexpr int kLanes = 16;  // lanes per record column: four columns per wave

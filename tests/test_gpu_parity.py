@@ -581,6 +581,36 @@ def test_selector_unsplit_sweeps(dt, d):
         say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
+LIMITS = [
+    # case, rows_per_tile: the C ABI's maxima
+    ((64, 262144, 2, 1, 64, 64, "bf16", 1), 8),    # POEM_MAX_VISIBLE_BLOCKS: 4096 blocks of 64 keys
+    ((64, 262144, 2, 1, 64, 64, "fp32", 1), 8),
+    ((300, 428, 8, 2, 128, 128, "bf16", 1), 32),   # POEM_MAX_ROWS_PER_TILE with G = 4 (128 columns)
+    ((100, 228, 128, 32, 64, 64, "bf16", 1), 8),   # POEM_MAX_HEADS_Q
+]
+
+
+@pytest.mark.parametrize("case,S", LIMITS, ids=lambda x: str(x))
+def test_selector_at_limits(case, S):
+    """The selector (and the attention on its lists) at the largest sizes the C ABI
+    accepts: a tile seeing 4096 key blocks (pass 1 in eight chunks of 512, the threshold
+    reading its records from the workspace), 32 sampled rows per tile, 128 query heads."""
+    w = _small(case, seed=13).with_(sink_offset=7.0, rows_per_tile=S)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    say("selector at limits", case, S)
+    r = L.select(gp, qd, kd, vd, inp.tau, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+    d_out, _ = L.dense_prefill(gp, qd, kd, vd, out_dtype="fp32")
+    s_out, _ = L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32")
+    _sync()
+    assert L.max_visible_blocks(gp) <= 4096
+    q, k, v = H.f64(inp)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in O.tiles(op)]
+    nc, nm, ws = check_selection(w, inp, gp, op, r, which, q, k, v, d_out.cpu().numpy(), s_out.cpu().numpy())
+    say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
+
+
 def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=None, gpu_sparse=None):
     """poem_select_group against the oracle's group selection on (KV head, gtile) units:
     group scores, the shared list under every head, masks with exemptions, and for
