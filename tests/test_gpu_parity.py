@@ -611,6 +611,51 @@ def test_selector_at_limits(case, S):
     say("  candidates", nc, "agreement", nm / max(nc, 1), "worst score rel err", ws)
 
 
+@pytest.mark.parametrize("dt", ["bf16", "fp32"])
+def test_selector_degenerate(dt):
+    """A batch whose middle sequence has no queries, at tau = 0 (any discard has a
+    positive bound, so every visible block is kept) and tau = 1e30 (every candidate is
+    discarded, only the mandatory blocks stay): the kept sets equal the oracle's, the
+    retained-block attention equals the oracle's on them, the empty sequence writes
+    nothing and its tiles do not exist in the CSR."""
+    import torch
+    B, d = (128, 128) if dt == "bf16" else (64, 64)
+    w = _small((100, 356, 4, 1, d, B, dt, 1), seed=17).with_(
+        seqlens_q=(100, 0, 66), seqlens_k=(100 + 6 * B, B, 66 + 6 * B), sink_offset=6.0)
+    inp = synth.make(w)
+    gp, op = H.problems(w)
+    qd, kd, vd = H.device_inputs(inp)
+    q, k, v = H.f64(inp)
+    T = L.num_tiles(gp)
+    tl = O.tiles(op)
+    assert T == len(tl) and all(t.seq != 1 for t in tl)
+    which = [(h, t.gtile) for h in range(op.num_heads_q) for t in tl]
+    for tau in (0.0, 1e30):
+        taus = [tau] * w.num_heads_q
+        say("degenerate", dt, "tau", tau)
+        r = L.select(gp, qd, kd, vd, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, diagnostics=True)
+        sentinel = 123.0
+        out = torch.full((gp.total_q, gp.num_heads_q, d), sentinel, dtype=torch.float32, device="cuda")
+        lse = torch.full((gp.num_heads_q, gp.total_q), sentinel, dtype=torch.float32, device="cuda")
+        L.sparse_prefill(gp, qd, kd, vd, r["row_ptr"], r["block_idx"], out_dtype="fp32", out=out, lse=lse)
+        _sync()
+        assert gp.total_q == 166
+        rp, bi = H.csr_rows(r["row_ptr"], r["block_idx"])
+        out = out.cpu().numpy()
+        sels = O.select(op, q, k, v, taus, w.n_sink_blocks, w.n_local_blocks, w.rows_per_tile, which=which)
+        for (h, gt), sel in sels.items():
+            kept = H.retained(rp, bi, h * T + gt)
+            t = sel.tile
+            want = list(range(t.diag + 1)) if tau == 0.0 else sorted(sel.mandatory)
+            assert sel.retained == want, (tau, h, gt, sel.retained, want)
+            assert kept == want, (tau, h, gt, kept, want)
+            Or, _ = O.tile_attention(op, q, k, v, h, t, kept)
+            atol = H.OUT_ATOL_FP32 if dt == "fp32" else H.OUT_ATOL_BF16
+            assert np.abs(out[t.q_row0:t.q_row0 + t.n_rows, h] - Or).max() <= atol, (tau, h, gt)
+        # every output row belongs to a tile of sequence 0 or 2 and was written
+        assert not np.any(out == sentinel)
+
+
 def check_group_selection(w, taus, gp, op, r, which_units, q, k, v, gpu_dense=None, gpu_sparse=None):
     """poem_select_group against the oracle's group selection on (KV head, gtile) units:
     group scores, the shared list under every head, masks with exemptions, and for
