@@ -456,20 +456,32 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h0, int seq, 
   const float l_tot = half_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (row_ok) {
-    char* orow = reinterpret_cast<char*>(p.out) + (qrow * p.hq + h) * D * (p.out_f32 ? 4 : 2);
+    // a per-lane base pointer (the lane's half of each 8-column group) with the d tile
+    // and column group as constant offsets, which fold into the stores' immediate
+    // offsets; offsets kept as values of their own would be loop-invariant in the
+    // persistent kernels, hoisted out of the row loop and spilled
+    const int64_t e0 = (qrow * p.hq + h) * D + 4 * g2;
+    if (p.out_f32) {
+      float* orow = reinterpret_cast<float*>(p.out) + e0;
 #pragma unroll
-    for (int dt = 0; dt < D / 32; ++dt)
+      for (int dt = 0; dt < D / 32; ++dt)
 #pragma unroll
-      for (int a = 0; a < 4; ++a) {
-        const int d = 32 * dt + 8 * a + 4 * g2;
-        f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv};
-        if (p.out_f32) {
-          *reinterpret_cast<f32x4*>(orow + d * 4) = o;
-        } else {
-          u32x2 w = {pack_bf16(o[0], o[1]), pack_bf16(o[2], o[3])};
-          *reinterpret_cast<u32x2*>(orow + d * 2) = w;
+        for (int a = 0; a < 4; ++a) {
+          const f32x4 o = {O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv, O[dt][4 * a + 2] * inv,
+                           O[dt][4 * a + 3] * inv};
+          *reinterpret_cast<f32x4*>(orow + 32 * dt + 8 * a) = o;
         }
-      }
+    } else {
+      uint16_t* orow = reinterpret_cast<uint16_t*>(p.out) + e0;
+#pragma unroll
+      for (int dt = 0; dt < D / 32; ++dt)
+#pragma unroll
+        for (int a = 0; a < 4; ++a) {
+          const u32x2 w = {pack_bf16(O[dt][4 * a] * inv, O[dt][4 * a + 1] * inv),
+                           pack_bf16(O[dt][4 * a + 2] * inv, O[dt][4 * a + 3] * inv)};
+          *reinterpret_cast<u32x2*>(orow + 32 * dt + 8 * a) = w;
+        }
+    }
     // the weights are 2^(c s - m_use); with the lazy reference m_use stays at the first
     // stage's max (0 if that stage was masked) while later stages add weight
     if (p.lse != nullptr && g2 == 0)
