@@ -1281,16 +1281,22 @@ __device__ __forceinline__ void practical_tile(const SelectParams& p, const ThrT
   if (tid == 0) p.counts[w.h0 * T + w.gtile] = total;
 }
 
-template <int MODE, bool STAGED>
+// SMALL (staged only): the launch for tiles of at most kStageVis / 2 visible blocks,
+// whose LDS is half the size, so twice as many workgroups share a CU; each launch
+// skips the tiles of the other.
+template <int MODE, bool STAGED, bool SMALL = false>
 __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams p) {
   constexpr bool NEED_I = MODE != kSelectMass;  // the mass-only ranking reads m alone
   constexpr bool PRAC = MODE == kSelectPractical;
-  constexpr int NK = STAGED ? kStageVis : kMaxVis;
+  static_assert(STAGED || !SMALL, "the small launch is staged");
+  constexpr int VIS = SMALL ? kStageVis / 2 : kStageVis;     // staged blocks per tile
+  constexpr int VALS = SMALL ? kStageVals / 2 : kStageVals;  // staged blocks x sampled rows
+  constexpr int NK = STAGED ? VIS : kMaxVis;
   __shared__ uint64_t sh[NK];
   __shared__ uint8_t keep[NK];
-  __shared__ __attribute__((aligned(16))) float st_I[STAGED && NEED_I ? kStageVals : 1];
+  __shared__ __attribute__((aligned(16))) float st_I[STAGED && NEED_I ? VALS : 1];
   __shared__ float bar_I[PRAC ? NK : 1], bar_m[PRAC ? NK : 1];  // practical: pooled estimates
-  __shared__ __attribute__((aligned(16))) float st_m[STAGED ? kStageVals : 1];
+  __shared__ __attribute__((aligned(16))) float st_m[STAGED ? VALS : 1];
   __shared__ double shd[2 * kRowChunk * kThrWaves];
   __shared__ int shi[kThrWaves];
   const int tid = threadIdx.x;
@@ -1311,6 +1317,9 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
   const int B = p.seqs.block;
   w.diag = p.seqs.diag0[seq] + t;
   w.n_vis = w.diag + 1;
+  if constexpr (STAGED) {
+    if ((w.n_vis <= kStageVis / 2 && w.n_vis * p.S <= kStageVals / 2) != SMALL) return;  // the other launch's tile
+  }
   const int n_rows_t = min(B, p.seqs.n_q[seq] - t * B);
   w.S = p.S;
   w.s_t = min(p.S, n_rows_t);
@@ -1393,8 +1402,8 @@ __global__ __launch_bounds__(kThrThreads) void sel_threshold_kernel(SelectParams
     if constexpr (PRAC) practical_tile<STAGED, E>(p, w, st_I, st_m, bar_I, bar_m, sh, keep, shd, shi);
     else threshold_tile<MODE, STAGED, E>(p, w, st_I, st_m, sh, keep, shd, shi);
   };
-  // keys per thread; staged tiles hold at most kStageVis blocks
-  constexpr int EMAX = STAGED ? kStageVis / kThrThreads : kMaxVis / kThrThreads;
+  // keys per thread; staged tiles hold at most VIS blocks
+  constexpr int EMAX = STAGED ? VIS / kThrThreads : kMaxVis / kThrThreads;
   switch (n_pad / kThrThreads) {
     case 1: run(IntTag<1>{}); break;
     case 2: if constexpr (EMAX >= 2) run(IntTag<2>{}); break;
@@ -1629,21 +1638,20 @@ static hipError_t launch_sel(const SelectParams& p, hipStream_t s) {
   const int64_t units = (int64_t)p.seqs.total_tiles * p.hkv;
   const unsigned tgrid = (unsigned)(((units + kXcds - 1) / kXcds) * kXcds * (p.group_mode ? 1 : p.group));
   const bool staged = p.max_vis <= kStageVis && (int64_t)p.max_vis * p.S <= kStageVals;
-  if (mass) {
-    if (staged) hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
-    else hipLaunchKernelGGL((sel_threshold_kernel<kSelectMass, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
-  } else if (p.mode == kSelectPractical) {
-    if (staged)
-      hipLaunchKernelGGL((sel_threshold_kernel<kSelectPractical, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((sel_threshold_kernel<kSelectPractical, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
-  } else {
-    if (staged)
-      hipLaunchKernelGGL((sel_threshold_kernel<kSelectOutputRelative, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
-    else
-      hipLaunchKernelGGL((sel_threshold_kernel<kSelectOutputRelative, false>), dim3(tgrid), dim3(kThrThreads), 0, s,
-                         p);
-  }
+  // staged: the tiles of at most half the staging size in a launch of their own with half
+  // the LDS (twice the workgroups per CU), then the others
+  auto thr = [&](auto mode_tag) {
+    constexpr int M = decltype(mode_tag)::value;
+    if (staged) {
+      hipLaunchKernelGGL((sel_threshold_kernel<M, true, true>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+      hipLaunchKernelGGL((sel_threshold_kernel<M, true, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+    } else {
+      hipLaunchKernelGGL((sel_threshold_kernel<M, false>), dim3(tgrid), dim3(kThrThreads), 0, s, p);
+    }
+  };
+  if (mass) thr(IntTag<kSelectMass>{});
+  else if (p.mode == kSelectPractical) thr(IntTag<kSelectPractical>{});
+  else thr(IntTag<kSelectOutputRelative>{});
   hipLaunchKernelGGL(csr_scan_kernel, dim3(1), dim3(1024), 0, s, p.counts, p.row_ptr, (int)rows);
   hipLaunchKernelGGL(csr_scatter_kernel, dim3((unsigned)rows), dim3(64), 0, s, p);
   return hipGetLastError();
