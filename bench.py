@@ -409,7 +409,11 @@ def selector_legs(args, w, inp, gp, L, q, k, v, ws, sws, rp_poem, steps):
 
     r, t_sel, t_sp = _time_select_sparse(gp, L, w, q, k, v, ws, sws, inp.tau, "group", steps)
     e_g = errors(r, group=True)
+    # retained-pair rate of the two-heads-per-workgroup kernel on the shared lists
+    p_g, _ = pair_counts(gp, r["row_ptr"].cpu().numpy().astype(np.int64), r["block_idx"].cpu().numpy())
+    tf_g = 4.0 * w.head_dim * p_g / (t_sp * 1e-3) / 1e12
     res_g = {"select_ms": t_sel, "sparse_ms": t_sp, "keep_fraction_blocks": int(r["row_ptr"][-1].item()) / cap,
+             "sparse_tflops": tf_g, "sparse_frac_of_bf16_peak": tf_g / 2500.0,
              "err_group": _err_stats(e_g, si, tau), "err_poem": out["err_poem"],
              "note": "same per-head thresholds as the headline step; one list per (KV head, tile) from the "
                      "group's 8 sampled rows, run by poem_sparse_prefill_group (G even: two heads per workgroup, each "
