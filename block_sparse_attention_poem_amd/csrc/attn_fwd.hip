@@ -256,16 +256,19 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h0, int seq, 
     // s_waitcnt vmcnt(LOADS): every direct load but this wave's newest K stage has landed
     constexpr int kWait = C::LOADS | 0x0F70;
     static_assert(C::LOADS < 16, "vmcnt field");
+    // A K load past the row's last stage still issues its instructions (the waits count
+    // them), but with no valid keys: its buffer descriptor covers no bytes, so the loads
+    // write zeros without a memory access and the row's last waits do not sit on them.
     auto first = [&]() {
       // the waits count this wave's loads in issue order, which the fences keep
       St::load_k(kbase, row_stride, stage_key0(0), n_k, tid, kb0, lo);
       __builtin_amdgcn_sched_barrier(0);
-      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), n_k, tid, kb1, lo);
+      St::load_k(kbase, row_stride, stage_key0(min(1, total - 1)), total > 1 ? n_k : 0, tid, kb1, lo);
       __builtin_amdgcn_s_waitcnt(kWait);
       lds_barrier();
       St::load_v(vbase, row_stride, stage_key0(0), n_k, tid, vb0, lo);
       __builtin_amdgcn_sched_barrier(0);
-      St::load_k(kbase, row_stride, stage_key0(min(2, total - 1)), n_k, tid, kb2, lo);
+      St::load_k(kbase, row_stride, stage_key0(min(2, total - 1)), total > 2 ? n_k : 0, tid, kb2, lo);
       Sp[0] = St::qk_tile(kb0, qf, 0, lane);
       Sp[1] = St::qk_tile(kb0, qf, 1, lane);
       mask(Sp, stage_key0(0));
@@ -281,7 +284,7 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h0, int seq, 
       // V(it) first, then K(it + 2): the wait below leaves only the K loads in flight
       St::load_v(vbase, row_stride, key0, n_k, tid, vcur, lo);
       __builtin_amdgcn_sched_barrier(0);
-      St::load_k(kbase, row_stride, stage_key0(min(it + 2, total - 1)), n_k, tid, knext, lo);
+      St::load_k(kbase, row_stride, stage_key0(min(it + 2, total - 1)), it + 2 < total ? n_k : 0, tid, knext, lo);
       // QK phase at raised wave priority (s_setprio): its issue slots go ahead of the PV
       // phase of the other wave on the SIMD (measured at 128K: -1.8% for the sparse
       // kernel against raising the PV phase instead)
@@ -380,8 +383,8 @@ __device__ __forceinline__ void attn_tile(const AttnParams& p, int h0, int seq, 
       l_run += rs;
       ovf |= !(rs <= kLazyCap);
       St::pv_packed(((total - 1) & 1) ? vb1 : vb0, P, O, lane);
-      // the last K prefetch (a repeat of the final stage) may still be in flight: it
-      // lands before this workgroup's LDS can be reused
+      // the last K prefetches (empty ones past the row's end) may still be in flight:
+      // they land before this workgroup's LDS can be reused
       wait_vmem_all();
     }
     // Did any wave mark the tile? Each wave writes its own word of the third K buffer,
