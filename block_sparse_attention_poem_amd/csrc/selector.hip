@@ -368,13 +368,14 @@ void sel_sweep_kernel(SelectParams p) {
       bf16x8 ph[2], unused;
       p_step<false>(Sp, 0, ph[0], unused);
       float rs = row_sum_bf16(ph[0], 0.f);
-      bf16x8 va[2];
+      bf16x8 va[3];  // V fragments read two MFMAs ahead of their use
       va[0] = St::v_frag(vprev, 0, 0, lane);
+      va[1] = St::v_frag(vprev, 1 % NDT, 1 / NDT, lane);
 #pragma unroll
       for (int i = 0; i < NPV; ++i) {
         const int dt = i % NDT, st = i / NDT;
-        if (i + 1 < NPV) va[(i + 1) & 1] = St::v_frag(vprev, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i & 1], ph[st & 1], O[dt], 0, 0, 0);
+        if (i + 2 < NPV) va[(i + 2) % 3] = St::v_frag(vprev, (i + 2) % NDT, (i + 2) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[i % 3], ph[st & 1], O[dt], 0, 0, 0);
         if (dt == 0 && st + 1 < 4) {
           p_step<false>(Sp, st + 1, ph[(st + 1) & 1], unused);
           rs = row_sum_bf16(ph[(st + 1) & 1], rs);
@@ -483,13 +484,14 @@ void sel_sweep_kernel(SelectParams p) {
         __builtin_amdgcn_sched_barrier(0);
       }
       // P V over key steps 0 and 1, next to the weights and packs of key tile 1
-      bf16x8 va[2];
+      bf16x8 va[3];  // V fragments read two MFMAs ahead of their use
       va[0] = St::v_frag(vt, 0, 0, lane);
+      va[1] = St::v_frag(vt, 1 % NDT, 1 / NDT, lane);
 #pragma unroll
       for (int i = 0; i < 2 * NDT; ++i) {
         const int dt = i % NDT, st = i / NDT;
-        va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st],
+        va[(i + 2) % 3] = St::v_frag(vt, (i + 2) % NDT, (i + 2) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i % 3]), ph[st],
                                                        (FIRST && st == 0) ? f32x16{} : O[dt], 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < 16 / (2 * NDT); ++u) {
@@ -507,8 +509,8 @@ void sel_sweep_kernel(SelectParams p) {
 #pragma unroll
       for (int i = 2 * NDT; i < 4 * NDT; ++i) {  // key steps 2 and 3
         const int dt = i % NDT, st = i / NDT;
-        if (i + 1 < 4 * NDT) va[(i + 1) & 1] = St::v_frag(vt, (i + 1) % NDT, (i + 1) / NDT, lane);
-        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i & 1]), ph[st], O[dt], 0, 0, 0);
+        if (i + 2 < 4 * NDT) va[(i + 2) % 3] = St::v_frag(vt, (i + 2) % NDT, (i + 2) / NDT, lane);
+        O[dt] = __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, va[i % 3]), ph[st], O[dt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
